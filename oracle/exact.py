@@ -1,0 +1,91 @@
+"""Exact rational brute force for tiny shapes (pins the fp64 oracle).
+
+Evaluates the closed-form equation of Lesson 13, Fig. 13-1 with Python
+Fractions -- no floating point anywhere between the stored inputs and the final
+rounding -- and rounds the exact rational result to bf16 with
+round-to-nearest-even.  It decodes e4m3 bytes and rounds to bf16 with its own
+rational arithmetic, independent of ``e4m3.py`` and ``bf16.py``, so agreement
+with ``gemm.py`` checks those modules too.  Pure-Python loops: tiny inputs only.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+
+def e4m3_fraction(code: int):
+    """Exact value of an e4m3 (OCP E4M3FN) byte as a Fraction, or None for NaN."""
+    s = -1 if code & 0x80 else 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 15 and m == 7:
+        return None
+    if e == 0:
+        return s * Fraction(m, 8) * Fraction(1, 2 ** 6)
+    mag = Fraction(8 + m, 8)
+    return s * (mag * 2 ** (e - 7) if e >= 7 else mag / 2 ** (7 - e))
+
+
+def f32_fraction(v) -> Fraction:
+    """Exact value of a finite fp32 number."""
+    return Fraction(float(np.float32(v)))
+
+
+def bf16_bits_from_fraction(x: Fraction) -> int:
+    """Round an exact rational to bf16 (ties to even) and return the 16-bit pattern."""
+    if x == 0:
+        return 0  # exact zero: +0 (sign of zero is not observable from a rational)
+    sign = 0x8000 if x < 0 else 0
+    v = abs(x)
+    # find e with 2^e <= v < 2^(e+1)
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    e = max(e, -126)  # below the smallest normal the spacing stays 2^-133
+    q = Fraction(2) ** (e - 7)
+    t = v / q
+    n = t.numerator // t.denominator
+    rem = t - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * q
+    if r >= Fraction(2) ** 128:
+        return sign | 0x7F80  # overflow to infinity
+    # encode r = n * 2^(e-7) as bf16 fields
+    if r < Fraction(2) ** -126:
+        # subnormal: mantissa = r / 2^-133
+        return sign | int(r / Fraction(2) ** -133)
+    ee = r.numerator.bit_length() - r.denominator.bit_length()
+    while Fraction(2) ** ee > r:
+        ee -= 1
+    while Fraction(2) ** (ee + 1) <= r:
+        ee += 1
+    mant = r / Fraction(2) ** ee - 1  # in [0, 1)
+    m7 = mant * 128
+    assert m7.denominator == 1
+    return sign | ((ee + 127) << 7) | int(m7)
+
+
+def gemm_nt_exact(a_codes, sfa, b_codes, sfb):
+    """Exact closed form; returns (Fraction matrix as nested lists, uint16 bf16 bits)."""
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    b_codes = np.asarray(b_codes, dtype=np.uint8)
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    A = [[e4m3_fraction(int(c)) for c in row] for row in a_codes]
+    B = [[e4m3_fraction(int(c)) for c in row] for row in b_codes]
+    out = np.zeros((M, N), dtype=np.uint16)
+    exact = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            total = Fraction(0)
+            for g in range(K // 128):
+                part = sum(A[i][128 * g + k] * B[j][128 * g + k] for k in range(128))
+                total += f32_fraction(sfa[g][i]) * f32_fraction(sfb[j // 128][g]) * part
+            row.append(total)
+            out[i, j] = bf16_bits_from_fraction(total)
+        exact.append(row)
+    return exact, out
