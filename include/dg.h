@@ -1,0 +1,171 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) block-scaled FP8 GEMM library.
+ *
+ * Computes D = A . B^T in bf16 from e4m3 operands with fine-grained fp32
+ * scales, and its two MoE grouped forms.  The operation is the one defined by
+ * Lesson 13 "DeepSeek DeepGEMM core architecture and Hopper FP8 operator
+ * breakdown" (hpc.payai.win), Fig. 13-1 and its closed-form equation:
+ *
+ *   D[i,j] = sum_g alpha[i,g] * beta[j/128, g] * sum_{k<128} A[i,128g+k] * B[j,128g+k]
+ *
+ * where each 128-wide K block's partial product is scaled by alpha*beta and
+ * added into an fp32 accumulator inside the main loop, and the epilogue only
+ * converts to bf16 (round to nearest even).  Layout is NT: A is [M,K] and B is
+ * [N,K], both K-contiguous (DeepGEMM architecture deep dive, blog.123qwe.co.kr,
+ * section 3, "D = A @ B.T").
+ *
+ * Conventions shared by every entry point
+ *   - e4m3 means OCP FP8 E4M3FN (bias 7, max 448, 0x7F/0xFF NaN), passed as
+ *     uint8_t bytes; bf16 is passed as uint16_t bit patterns.
+ *   - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or synchronises on these calls.  Pointers must be
+ *     16-byte aligned (DG_ERR_ALIGN otherwise) except the scale, index and
+ *     workspace arrays, which need 4-byte alignment.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and returns; the calls
+ *     allocate nothing and never read device data on the host, so they may be
+ *     captured into a hipGraph.  Kernel faults surface through the usual HIP
+ *     stream error reporting.
+ *   - Shapes are int64_t.  K must be a positive multiple of 128, N a positive
+ *     multiple of 16, row counts >= 0 (0 rows = nothing to do, DG_OK).
+ *   - Return value: DG_OK or one of the DG_ERR_* codes below; on error nothing
+ *     is enqueued and dg_get_last_error() returns a message (thread-local).
+ *   - Scale layouts: activation scales alpha are MN-major, [K/128][rows] fp32
+ *     (per expert for the masked form); weight scales beta are
+ *     [ceil(N/128)][K/128] fp32 per expert.  alpha = amax/448 over each 1x128
+ *     row group; beta = amax/448 over each 128x128 block (Lesson 13,
+ *     Fig. 13-1).
+ *   - D rows that the operation does not define (padding rows of the
+ *     contiguous form, rows past masked_m of the masked form) are never
+ *     written.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1, /* null pointer, bad enum value */
+  DG_ERR_SHAPE = 2,       /* K % 128, N % 16, negative sizes, G out of range */
+  DG_ERR_ALIGN = 3,       /* pointer alignment */
+  DG_ERR_WORKSPACE = 4,   /* workspace pointer given with a size that is not a multiple of 4 */
+  DG_ERR_DEVICE = 5,      /* no HIP device, or the current device is not gfx950 */
+  DG_ERR_LAUNCH = 6       /* the kernel launch itself failed */
+};
+
+/* Operation ids for dg_get_workspace_size. */
+enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2 };
+
+/*
+ * Dense GEMM.  Lesson 13, Fig. 13-1; DeepGEMM's "normal" GEMM (the Feb-2025
+ * release article on dakule.com, usage section).
+ *   A   [M,K]  e4m3, row-major          sfa [K/128][M] fp32
+ *   B   [N,K]  e4m3, row-major          sfb [ceil(N/128)][K/128] fp32
+ *   D   [M,N]  bf16, row-major (written)
+ * workspace: optional fp32 scratch for splitting K across workgroups when the
+ *   output has too few tiles to fill the GPU (small M).  Pass NULL/0 to run
+ *   without it (same result, possibly slower).  Required size for the full
+ *   split is dg_get_workspace_size(DG_OP_GEMM_NT, M, N, K, 1); a smaller
+ *   buffer limits the split.  Calls that share one workspace must be ordered
+ *   on one stream.
+ */
+int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
+                   uint16_t* D, int64_t M, int64_t N, int64_t K, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * M-grouped contiguous GEMM (MoE training forward / prefill).  Lesson 13,
+ * Fig. 13-3 (contiguous layout); deep-dive blog section 3 (grouped API table,
+ * per-expert segments aligned to the M block).
+ *   A         [M_total,K] e4m3, rows of all experts concatenated
+ *   sfa       [K/128][M_total] fp32
+ *   B         [G,N,K] e4m3 (one weight per expert, same N and K for all)
+ *   sfb       [G][ceil(N/128)][K/128] fp32
+ *   m_indices [M_total] int32, device: expert of each row; a value outside
+ *             [0,G) marks a padding row, whose D row is not written
+ *   D         [M_total,N] bf16
+ * Each aligned block of dg_get_m_alignment_for_contiguous_layout() rows must
+ * hold rows of at most one expert (segments padded to that alignment); rows
+ * of a block whose index differs from the block's expert are not written.
+ * workspace: unused, pass NULL/0.
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B,
+                                        const float* sfb, uint16_t* D, const int32_t* m_indices,
+                                        int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * M-grouped masked GEMM (MoE decode under graph capture).  Lesson 13,
+ * Fig. 13-3 (masked layout) and the answer to Q3: fixed-capacity buffers per
+ * expert and a device array of valid row counts read by the kernel, so the
+ * launch never depends on host knowledge of the counts.
+ *   A        [G,max_m,K] e4m3             sfa [G][K/128][max_m] fp32
+ *   B        [G,N,K] e4m3                 sfb [G][ceil(N/128)][K/128] fp32
+ *   masked_m [G] int32, device: expert g's rows [0, clamp(masked_m[g],0,max_m))
+ *            are computed; all other rows of D are not written
+ *   D        [G,max_m,N] bf16
+ * expected_m: host hint of the typical masked_m (0 = unknown); it may only
+ *   change speed, never results.  workspace: unused, pass NULL/0.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const uint8_t* B,
+                                    const float* sfb, uint16_t* D, const int32_t* masked_m,
+                                    int64_t G, int64_t max_m, int64_t N, int64_t K,
+                                    int64_t expected_m, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * 1x128 activation quantiser.  Lesson 13, Fig. 13-1 (one scale per token per
+ * 128 K elements, scale = amax/448).
+ *   x   [G,M,K] fp32 (G=1 for a plain [M,K] matrix)
+ *   q   [G,M,K] e4m3 (written)
+ *   sfa [G][K/128][M] fp32 (written)
+ * alpha = fl32(amax / 448) by IEEE division; q = e4m3_RNE(fl32(x / alpha)),
+ * ties to even, sign of zero kept, saturating at +-448; a group with amax = 0
+ * (or amax/448 underflowing to 0) gets alpha = 1.  Non-finite inputs give
+ * unspecified codes.  Bit-exact and deterministic.
+ */
+int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K,
+                   void* stream);
+
+/*
+ * 128x128 weight quantiser.  Lesson 13, Fig. 13-1 (one scale per 128x128
+ * block of the weight, stored fp32).
+ *   x   [G,N,K] fp32       q [G,N,K] e4m3 (written)
+ *   sfb [G][ceil(N/128)][K/128] fp32 (written)
+ * Same rounding rules as dg_quant_1x128; when N is not a multiple of 128 the
+ * last block's amax covers only its existing rows.
+ */
+int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t N, int64_t K,
+                     void* stream);
+
+/* Workspace bytes that let `op` use its full K split for this shape (0 = none used). */
+size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
+
+/* Row alignment of expert segments in the contiguous layout (deep-dive blog,
+ * section 3: contiguous segments aligned to the M block).  Always 128. */
+int dg_get_m_alignment_for_contiguous_layout(void);
+
+/* Cap on the number of compute units the kernels plan for (analog of the
+ * "set max SM count" utility in the Feb-2025 release article).  n <= 0 resets
+ * to the device's count.  Process-wide; returns DG_OK. */
+int dg_set_num_cus(int n);
+/* Current cap (the device's CU count when no cap is set; 0 if no device). */
+int dg_get_num_cus(void);
+
+/* Message of the last error on this thread ("" if none). */
+const char* dg_get_last_error(void);
+/* Library version string. */
+const char* dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,72 @@
+"""Ahead-of-time build of the gfx950 library ``libdg_mi355x.so`` (in-tree).
+
+Compiles every HIP source under ``csrc/`` with hipcc for gfx950 and links one
+shared library next to this file.  Kernel register/scratch usage reported by
+the compiler is kept in ``_build/resource_usage.txt`` (read by a test that
+requires zero scratch, i.e. no register spills).
+
+Usage: python -m moe_grouped_matmul_amd.build   (or build() from Python)
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB_NAME = "libdg_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+COMMON = [
+    "-O3",
+    "--offload-arch=gfx950",
+    "-fPIC",
+    "-std=c++17",
+    "-Wall",
+    # packed fp32 VALU forms are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    return obj, r.stderr
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    report = []
+    for (obj, log), src in zip(results, SOURCES):
+        lines = [l for l in log.splitlines() if "remark" in l or "Function Name" in l or ":" in l]
+        report.append(f"== {src}\n" + "\n".join(l for l in log.splitlines() if "remark:" in l))
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        f.write("\n".join(report) + "\n")
+    tmp = LIB_PATH + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *[o for o, _ in results], "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

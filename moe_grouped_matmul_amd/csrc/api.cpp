@@ -1,0 +1,328 @@
+// C ABI of the library: argument validation, tile-configuration choice and
+// launch on the caller's stream.  No allocation, no synchronisation, no host
+// reads of device data, so every call can be captured into a hipGraph.
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "dg.h"
+#include "dg_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_cu_cap{0};
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other; CU count cached alongside
+std::atomic<int> g_dev_kind[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks that a HIP device is current and is gfx950; returns its CU count (>0) or fails.
+int check_device(int* cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(DG_ERR_DEVICE, "no HIP device available");
+  }
+  if (dev < kMaxDevices) {
+    const int kind = g_dev_kind[dev].load(std::memory_order_acquire);
+    if (kind == 1) {
+      *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+      return DG_OK;
+    }
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DG_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+  }
+  const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) {
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_dev_kind[dev].store(is950 ? 1 : 2, std::memory_order_release);
+  }
+  if (!is950) return fail(DG_ERR_DEVICE, "device %d is %s, this library is built for gfx950 only", dev, prop.gcnArchName);
+  *cus = prop.multiProcessorCount;
+  return DG_OK;
+}
+
+int effective_cus(int device_cus) {
+  const int cap = g_cu_cap.load(std::memory_order_relaxed);
+  return (cap > 0 && cap < device_cus) ? cap : device_cus;
+}
+
+int check_nk(int64_t N, int64_t K) {
+  if (K <= 0 || K % 128 != 0) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (N <= 0 || N % 16 != 0) return fail(DG_ERR_SHAPE, "N must be a positive multiple of 16 (got %lld)", (long long)N);
+  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30) return fail(DG_ERR_SHAPE, "N or K too large");
+  return DG_OK;
+}
+
+int check_operands(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, const uint16_t* D) {
+  if (!A || !sfa || !B || !sfb || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16))
+    return fail(DG_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+  if (!aligned(sfa, 4) || !aligned(sfb, 4)) return fail(DG_ERR_ALIGN, "scale arrays must be 4-byte aligned");
+  return DG_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Dense split-K plan: enough work items to cover the CUs twice when the
+// output alone has too few tiles.  Splits never exceed the K blocks.
+struct DensePlan {
+  int cfg;
+  int m_tiles;
+  int n_tiles;
+  int splits;
+  int kb_per_split;
+};
+
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+  DensePlan pl;
+  pl.cfg = M <= 64 ? dg::kTile64x64 : dg::kTile128x128;
+  const dg::TileShape ts = dg::tile_shape(pl.cfg);
+  pl.m_tiles = (int)ceil_div(M, ts.bm);
+  pl.n_tiles = (int)ceil_div(N, ts.bn);
+  const int KB = (int)(K / 128);
+  const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
+  int splits = 1;
+  if (tiles < cus) {
+    splits = (int)ceil_div(2 * (int64_t)cus, tiles);
+    if (splits > KB) splits = KB;
+    if (splits > 16) splits = 16;
+    const size_t per_split = (size_t)M * (size_t)N * sizeof(float);
+    const size_t fit = per_split ? ws_bytes / per_split : 0;
+    if ((size_t)splits > fit) splits = (int)fit;
+    if (splits < 2) splits = 1;
+  }
+  pl.kb_per_split = (int)ceil_div(KB, splits);
+  pl.splits = (int)ceil_div(KB, pl.kb_per_split);
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, uint16_t* D, int64_t M,
+                   int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if (M == 0) return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
+    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = sfa;
+  p.B = B;
+  p.sfb = sfb;
+  p.D = D;
+  p.ws = static_cast<float*>(workspace);
+  p.index = nullptr;
+  p.rows = M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = 1;
+  p.m_tiles = pl.m_tiles;
+  p.n_tiles = pl.n_tiles;
+  p.splits = pl.splits;
+  p.kb_per_split = pl.kb_per_split;
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld tile=%dx%d splits=%d grid=%lld\n", (long long)M,
+                 (long long)N, (long long)K, dg::tile_shape(pl.cfg).bm, dg::tile_shape(pl.cfg).bn, pl.splits,
+                 (long long)pl.m_tiles * pl.n_tiles * pl.splits);
+  const hipError_t e = dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
+                                        uint16_t* D, const int32_t* m_indices, int64_t M_total, int64_t N,
+                                        int64_t K, int64_t G, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (M_total < 0) return fail(DG_ERR_SHAPE, "M_total must be >= 0");
+  if (M_total > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M_total too large");
+  if (G < 1 || G > 65536) return fail(DG_ERR_SHAPE, "G must be in [1, 65536] (got %lld)", (long long)G);
+  if (M_total == 0) return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if (!m_indices) return fail(DG_ERR_INVALID_ARG, "null m_indices");
+  if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  const int cfg = dg::kTile128x128;
+  const dg::TileShape ts = dg::tile_shape(cfg);
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = sfa;
+  p.B = B;
+  p.sfb = sfb;
+  p.D = D;
+  p.index = m_indices;
+  p.rows = M_total;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = (int)G;
+  p.m_tiles = (int)ceil_div(M_total, ts.bm);
+  p.n_tiles = (int)ceil_div(N, ts.bn);
+  p.splits = 1;
+  p.kb_per_split = (int)(K / 128);
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d\n", (long long)M_total,
+                 (long long)N, (long long)K, (long long)G, ts.bm, ts.bn);
+  const hipError_t e = dg::launch_gemm(dg::kContiguous, cfg, p, 1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
+                                    uint16_t* D, const int32_t* masked_m, int64_t G, int64_t max_m, int64_t N,
+                                    int64_t K, int64_t expected_m, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (G < 1 || G > 65536) return fail(DG_ERR_SHAPE, "G must be in [1, 65536] (got %lld)", (long long)G);
+  if (max_m < 0) return fail(DG_ERR_SHAPE, "max_m must be >= 0");
+  if (G * max_m > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "G * max_m too large");
+  if (max_m == 0) return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if (!masked_m) return fail(DG_ERR_INVALID_ARG, "null masked_m");
+  if (!aligned(masked_m, 4)) return fail(DG_ERR_ALIGN, "masked_m must be 4-byte aligned");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  (void)expected_m;
+  const int cfg = max_m <= 64 ? dg::kTile64x128 : dg::kTile128x128;
+  const dg::TileShape ts = dg::tile_shape(cfg);
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = sfa;
+  p.B = B;
+  p.sfb = sfb;
+  p.D = D;
+  p.index = masked_m;
+  p.rows = max_m;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = (int)G;
+  p.m_tiles = (int)ceil_div(max_m, ts.bm);
+  p.n_tiles = (int)ceil_div(N, ts.bn);
+  p.splits = 1;
+  p.kb_per_split = (int)(K / 128);
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=%dx%d\n", (long long)G,
+                 (long long)max_m, (long long)N, (long long)K, ts.bm, ts.bn);
+  const hipError_t e = dg::launch_gemm(dg::kMasked, cfg, p, (int)G, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K, void* stream) {
+  if (K <= 0 || K % 128) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (G < 0 || M < 0) return fail(DG_ERR_SHAPE, "G and M must be >= 0");
+  if (G > ((int64_t)1 << 31) || M > ((int64_t)1 << 31) || G * M * (K / 128) > ((int64_t)1 << 35))
+    return fail(DG_ERR_SHAPE, "problem too large");
+  if (G == 0 || M == 0) return ok();
+  if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(DG_ERR_ALIGN, "x and q must be 16-byte aligned");
+  if (!aligned(sfa, 4)) return fail(DG_ERR_ALIGN, "sfa must be 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc) return rc;
+  const hipError_t e = dg::launch_quant_1x128(x, q, sfa, G, M, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t N, int64_t K, void* stream) {
+  if (K <= 0 || K % 128) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (G < 0 || N < 0) return fail(DG_ERR_SHAPE, "G and N must be >= 0");
+  if (G > ((int64_t)1 << 31) || N > ((int64_t)1 << 31) || G * ceil_div(N, 128) * (K / 128) > ((int64_t)1 << 31) - 1)
+    return fail(DG_ERR_SHAPE, "problem too large");
+  if (G == 0 || N == 0) return ok();
+  if (!x || !q || !sfb) return fail(DG_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(DG_ERR_ALIGN, "x and q must be 16-byte aligned");
+  if (!aligned(sfb, 4)) return fail(DG_ERR_ALIGN, "sfb must be 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc) return rc;
+  const hipError_t e = dg::launch_quant_128x128(x, q, sfb, G, N, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G) {
+  (void)G;
+  if (op != DG_OP_GEMM_NT) return 0;
+  if (rows <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+  int cus = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  }
+  (void)hipGetLastError();
+  if (cus <= 0) cus = 256;
+  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1);
+  if (pl.splits <= 1) return 0;
+  return (size_t)pl.splits * (size_t)rows * (size_t)N * sizeof(float);
+}
+
+int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }
+
+int dg_set_num_cus(int n) {
+  g_cu_cap.store(n > 0 ? n : 0, std::memory_order_relaxed);
+  return ok();
+}
+
+int dg_get_num_cus(void) {
+  int dev = -1;
+  int cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  }
+  (void)hipGetLastError();
+  if (cus <= 0) return 0;
+  return effective_cus(cus);
+}
+
+const char* dg_get_last_error(void) { return g_last_error.c_str(); }
+
+const char* dg_version(void) { return "dg-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal declarations shared by the host layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Parameters of one GEMM launch (dense, contiguous or masked form).
+struct GemmParams {
+  const uint8_t* A;      // e4m3 activations
+  const float* sfa;      // activation scales, MN-major [K/128][rows] (per group when masked)
+  const uint8_t* B;      // e4m3 weights [G][N][K]
+  const float* sfb;      // weight scales [G][ceil(N/128)][K/128]
+  uint16_t* D;           // bf16 output
+  float* ws;             // split-K partials [splits][rows][N] (dense only)
+  const int32_t* index;  // m_indices (contiguous) or masked_m (masked); unused when dense
+  int64_t rows;          // dense: M; contiguous: M_total; masked: max_m (rows per group)
+  int N;
+  int K;
+  int G;
+  int m_tiles;
+  int n_tiles;
+  int splits;
+  int kb_per_split;
+};
+
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// Tile configurations compiled for gfx950 (workgroup tile BM x BN, K step 128).
+enum TileCfg { kTile128x128 = 0, kTile64x128 = 1, kTile64x64 = 2, kNumTileCfgs = 3 };
+
+struct TileShape {
+  int bm;
+  int bn;
+};
+TileShape tile_shape(int cfg);
+
+// Enqueue the GEMM kernel (and the split-K reduction when p.splits > 1).
+hipError_t launch_gemm(int mode, int cfg, const GemmParams& p, int groups, hipStream_t stream);
+
+hipError_t launch_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K,
+                              hipStream_t stream);
+hipError_t launch_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t N, int64_t K,
+                                hipStream_t stream);
+
+}  // namespace dg

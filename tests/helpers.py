@@ -1,0 +1,43 @@
+"""Shared helpers for the parity tests: tolerance rule, sentinels, device upload."""
+
+import numpy as np
+
+import oracle
+
+SENTINEL = 0xFFFF  # bf16 NaN pattern prefilled into D
+
+
+def tol_violations(got_bits, ref_bits):
+    """Elements outside |got - ref| <= 2^-7 |ref| + 1e-3 rms(ref); NaN positions must coincide.
+
+    rms is taken over the finite reference elements of the call, in fp64.
+    Returns the number of violating elements.
+    """
+    got = oracle.bf16_bits_to_f64(np.asarray(got_bits, dtype=np.uint16))
+    ref = oracle.bf16_bits_to_f64(np.asarray(ref_bits, dtype=np.uint16))
+    gn, rn = np.isnan(got), np.isnan(ref)
+    bad = int(np.count_nonzero(gn != rn))
+    fin = ~rn & ~gn
+    r = ref[fin]
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    bad += int(np.count_nonzero(np.abs(got[fin] - r) > 2.0 ** -7 * np.abs(r) + 1e-3 * rms))
+    return bad
+
+
+def assert_close(got_bits, ref_bits, what=""):
+    n = tol_violations(got_bits, ref_bits)
+    if n:
+        got = oracle.bf16_bits_to_f64(np.asarray(got_bits, dtype=np.uint16))
+        ref = oracle.bf16_bits_to_f64(np.asarray(ref_bits, dtype=np.uint16))
+        idx = np.argwhere(~np.isclose(got, ref, rtol=2.0 ** -7, atol=0, equal_nan=True))[:5]
+        detail = [(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {n} elements outside tolerance, e.g. {detail}")
+
+
+def masked_layout(codes, scales, rows, G, max_m):
+    """Place valid rows (expert-major) into [G, max_m, K] / [G, K/128, max_m] with traps elsewhere."""
+    from moe_grouped_matmul_amd.workloads import place_rows
+
+    K = codes.shape[1]
+    q, s = place_rows(codes, scales, rows, G * max_m)
+    return q.reshape(G, max_m, K), np.ascontiguousarray(s.reshape(K // 128, G, max_m).transpose(1, 0, 2))

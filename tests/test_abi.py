@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every symbol the header declares, the header compiles as C and C++, every
+argument-validation status code is reachable, the kernels build without
+register spills, and the product path does not touch the oracle."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+PKG = os.path.join(ROOT, "moe_grouped_matmul_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from moe_grouped_matmul_amd import dg
+
+    if not os.path.exists(dg.LIB_PATH):
+        from moe_grouped_matmul_amd import build
+
+        build.build()
+    return dg.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
+              "dg_quant_1x128", "dg_quant_128x128"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dg_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+@pytest.mark.parametrize("compiler,lang", [("gcc", "c"), ("g++", "c++")])
+def test_header_compiles(compiler, lang, tmp_path):
+    src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
+    src.write_text('#include "dg.h"\nint main(void){ return dg_get_m_alignment_for_contiguous_layout() == 128 ? 0 : 1; }\n')
+    r = subprocess.run([compiler, "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+# fake, never-dereferenced device addresses: every call below fails validation
+# before any device work is attempted
+P16 = 0x10000
+P4 = 0x10004
+
+
+def _err(lib):
+    return lib.dg_get_last_error().decode()
+
+
+def test_status_codes_from_host(lib):
+    from moe_grouped_matmul_amd import dg
+
+    s = ctypes.c_void_p(0)
+    gemm = lib.dg_fp8_gemm_nt
+    # shape errors
+    assert gemm(P16, P16, P16, P16, P16, 64, 2112, 7000, None, 0, s) == dg.DG_ERR_SHAPE and "K" in _err(lib)
+    assert gemm(P16, P16, P16, P16, P16, 64, 2110, 7168, None, 0, s) == dg.DG_ERR_SHAPE and "N" in _err(lib)
+    assert gemm(P16, P16, P16, P16, P16, -1, 2112, 7168, None, 0, s) == dg.DG_ERR_SHAPE
+    # zero rows: nothing to do
+    assert gemm(None, None, None, None, None, 0, 2112, 7168, None, 0, s) == dg.DG_OK and _err(lib) == ""
+    # null / alignment / workspace
+    assert gemm(None, P16, P16, P16, P16, 64, 2112, 7168, None, 0, s) == dg.DG_ERR_INVALID_ARG
+    assert gemm(P16 + 8, P16, P16, P16, P16, 64, 2112, 7168, None, 0, s) == dg.DG_ERR_ALIGN
+    assert gemm(P16, P16 + 2, P16, P16, P16, 64, 2112, 7168, None, 0, s) == dg.DG_ERR_ALIGN
+    assert gemm(P16, P16, P16, P16, P16, 64, 2112, 7168, P4, 64, s) == dg.DG_ERR_WORKSPACE
+    assert gemm(P16, P16, P16, P16, P16, 64, 2112, 7168, P16, 6, s) == dg.DG_ERR_WORKSPACE
+    contig = lib.dg_m_grouped_fp8_gemm_nt_contiguous
+    assert contig(P16, P16, P16, P16, P16, P16, 256, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
+    assert contig(P16, P16, P16, P16, P16, None, 256, 128, 256, 2, None, 0, s) == dg.DG_ERR_INVALID_ARG
+    assert contig(P16, P16, P16, P16, P16, P16 + 2, 256, 128, 256, 2, None, 0, s) == dg.DG_ERR_ALIGN
+    masked = lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert masked(P16, P16, P16, P16, P16, P16, 0, 256, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
+    assert masked(P16, P16, P16, P16, P16, P16, 4, -1, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
+    assert masked(None, None, None, None, None, None, 4, 0, 128, 256, 0, None, 0, s) == dg.DG_OK
+    assert masked(P16, P16, P16, P16, P16, None, 4, 8, 128, 256, 0, None, 0, s) == dg.DG_ERR_INVALID_ARG
+    q1 = lib.dg_quant_1x128
+    assert q1(P16, P16, P16, 1, 4, 100, s) == dg.DG_ERR_SHAPE
+    assert q1(None, P16, P16, 1, 4, 128, s) == dg.DG_ERR_INVALID_ARG
+    assert q1(P16, P16 + 4, P16, 1, 4, 128, s) == dg.DG_ERR_ALIGN
+    assert q1(P16, P16, P16, 1, 0, 128, s) == dg.DG_OK
+    q2 = lib.dg_quant_128x128
+    assert q2(P16, P16, P16, 1, 4, 130, s) == dg.DG_ERR_SHAPE
+    assert q2(P16, P16, P16 + 1, 1, 4, 128, s) == dg.DG_ERR_ALIGN
+
+
+def test_no_device_status_on_cpu_host(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path only")
+    from moe_grouped_matmul_amd import dg
+
+    rc = lib.dg_fp8_gemm_nt(P16, P16, P16, P16, P16, 64, 2112, 7168, None, 0, ctypes.c_void_p(0))
+    assert rc == dg.DG_ERR_DEVICE and _err(lib)
+    assert lib.dg_get_num_cus() == 0
+
+
+def test_utilities(lib):
+    assert lib.dg_get_m_alignment_for_contiguous_layout() == 128
+    assert lib.dg_version().decode().startswith("dg-mi355x")
+    assert lib.dg_set_num_cus(64) == 0
+    assert lib.dg_set_num_cus(0) == 0
+    # dense small-M shapes ask for split-K scratch, large ones do not
+    assert lib.dg_get_workspace_size(0, 64, 2112, 7168, 1) > 0
+    assert lib.dg_get_workspace_size(0, 4096, 7168, 16384, 1) == 0
+    assert lib.dg_get_workspace_size(2, 256, 4096, 7168, 32) == 0
+
+
+def test_kernels_have_no_register_spills(lib):
+    report = os.path.join(PKG, "_build", "resource_usage.txt")
+    if not os.path.exists(report):
+        from moe_grouped_matmul_amd import build
+
+        build.build()
+    text = open(report).read()
+    sizes = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", text)]
+    assert sizes, "no resource-usage remarks recorded"
+    assert all(s == 0 for s in sizes), text
+
+
+def test_product_path_never_imports_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), f
+                assert "import_module(\"oracle" not in src and "/oracle/" not in src, f

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars: quantiser bytes and scales bit-exact; untouched rows bit-exact; GEMM
+elements within |d - ref| <= 2^-7 |ref| + 1e-3 rms(ref) with NaN positions
+equal; integer inputs with unit scales bit-exact.  Small cases compare every
+element; full-size cases run in the benchmark's launch configuration (GPU
+quantisers feeding the GEMM) and compare sampled rows/columns that the oracle
+computes from its own quantisation of the same fp32 sources, after checking
+that the GPU bytes of those rows/blocks equal the oracle's.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_grouped_matmul_amd import dg, workloads
+from tests.helpers import SENTINEL, assert_close, masked_layout
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _t(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    x = t.cpu().numpy()
+    return x.view(np.uint16) if x.dtype == np.int16 else x
+
+
+def _sentinel(*shape):
+    return torch.full(shape, -1, dtype=torch.int16, device=DEV)
+
+
+def _ws(M, N, K):
+    n = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
+    return torch.empty(max(n // 4, 1), dtype=torch.float32, device=DEV) if n else None
+
+
+def _gpu_dense(qa, sa, qb, sb, M, N, K, workspace=True):
+    D = _sentinel(M, N)
+    dg.dg_fp8_gemm_nt(_t(qa), _t(sa), _t(qb), _t(sb), D, _ws(M, N, K) if workspace else None)
+    return _np(D)
+
+
+# ---------------------------------------------------------------- quantisers
+
+@pytest.mark.parametrize("G,M,K", [(1, 1, 128), (1, 70, 512), (3, 33, 384), (1, 64, 7168)])
+def test_quant_1x128_bit_exact(G, M, K):
+    rng = np.random.default_rng(G * 100 + M)
+    x = rng.standard_normal((G, M, K), dtype=np.float32) * np.exp2(rng.integers(-30, 30, (G, M, 1))).astype(np.float32)
+    x[0, 0, :128] = 0.0  # all-zero group
+    x[0, 0, 5] = -0.0
+    if K > 128:
+        x[0, 0, 128:256] *= np.float32(1e-3)  # codes in the e4m3 subnormal range too
+    q = torch.empty((G, M, K), dtype=torch.uint8, device=DEV)
+    s = torch.empty((G, K // 128, M), dtype=torch.float32, device=DEV)
+    dg.dg_quant_1x128(_t(x), q, s)
+    qr, sr = oracle.quant_1x128(x)
+    assert np.array_equal(_np(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(_np(q), qr)
+
+
+def test_quant_1x128_rounding_ties_and_subnormals():
+    # each row: amax 448 so alpha = 1 and x/alpha = x exactly; the rest are
+    # e4m3 ties, subnormals, signed zeros and values near the saturation edge
+    vals = np.array([448, 432, 17, 19, 2.0 ** -10, 3 * 2.0 ** -10, 1.5 * 2.0 ** -9, -1e-4, -0.0, 447.9, 0.0,
+                     2.0 ** -6 - 2.0 ** -11, 240, 232, 1.0625, 1.1875], np.float32)
+    x = np.zeros((2, 128), np.float32)
+    x[0, :vals.size] = vals
+    x[1, :vals.size] = -vals
+    x[1, 0] = -448
+    q = torch.empty((2, 128), dtype=torch.uint8, device=DEV)
+    s = torch.empty((1, 2), dtype=torch.float32, device=DEV)
+    dg.dg_quant_1x128(_t(x), q, s)
+    qr, sr = oracle.quant_1x128(x)
+    assert np.all(sr == 1.0) and np.array_equal(_np(s), sr)
+    assert np.array_equal(_np(q), qr)
+
+
+@pytest.mark.parametrize("G,N,K", [(1, 16, 128), (1, 200, 384), (2, 136, 256), (1, 2112, 1024)])
+def test_quant_128x128_bit_exact(G, N, K):
+    rng = np.random.default_rng(N + K)
+    x = rng.standard_normal((G, N, K), dtype=np.float32) / np.float32(np.sqrt(K))
+    x[0, :, :128] = 0.0  # all-zero blocks in the first column block
+    q = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    s = torch.empty((G, (N + 127) // 128, K // 128), dtype=torch.float32, device=DEV)
+    dg.dg_quant_128x128(_t(x), q, s)
+    qr, sr = oracle.quant_128x128(x)
+    assert np.array_equal(_np(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(_np(q), qr)
+
+
+# ---------------------------------------------------------------- dense GEMM
+
+DENSE_SMALL = [(1, 16, 128), (64, 2112, 512), (70, 272, 512), (128, 384, 256), (130, 144, 640), (257, 400, 384),
+               (64, 128, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", DENSE_SMALL)
+@pytest.mark.parametrize("workspace", [True, False])
+def test_dense_matches_oracle(M, N, K, workspace):
+    a32, b32 = workloads.dense(M, N, K, seed=M * 7 + N + K)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    got = _gpu_dense(qa, sa, qb, sb, M, N, K, workspace)
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"dense {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 272, 512), (128, 256, 384), (200, 144, 1024), (1, 16, 256)])
+def test_dense_integer_inputs_bit_exact(M, N, K):
+    # integers in [-10, 9] with unit scales: every partial and every fp32 sum is
+    # an exact integer below 2^24, so the bf16 result must equal the oracle's bits
+    rng = np.random.default_rng(M + N)
+    qa = oracle.encode_e4m3(rng.integers(-10, 10, (M, K)).astype(np.float32))
+    qb = oracle.encode_e4m3(rng.integers(-10, 10, (N, K)).astype(np.float32))
+    sa = np.ones((K // 128, M), np.float32)
+    sb = np.ones(((N + 127) // 128, K // 128), np.float32)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    for ws in (True, False):
+        assert np.array_equal(_gpu_dense(qa, sa, qb, sb, M, N, K, ws), ref)
+
+
+def test_dense_power_of_two_scaling_bit_exact():
+    M, N, K = 96, 256, 512
+    a32, b32 = workloads.dense(M, N, K, seed=5)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    base = _gpu_dense(qa, sa, qb, sb, M, N, K)
+    scaled = _gpu_dense(qa, sa * np.float32(4.0), qb, sb * np.float32(0.5), M, N, K)
+    assert np.array_equal(oracle.bf16_bits_to_f64(scaled), oracle.bf16_bits_to_f64(base) * 2.0)
+
+
+def test_dense_deterministic_and_nan_rows_contained():
+    M, N, K = 64, 2112, 1024
+    a32, b32 = workloads.dense(M, N, K, seed=6)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    qa[5, 300] = 0x7F  # NaN code: poisons row 5 only
+    d1 = _gpu_dense(qa, sa, qb, sb, M, N, K)
+    d2 = _gpu_dense(qa, sa, qb, sb, M, N, K)
+    assert np.array_equal(d1, d2)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    assert_close(d1, ref, "dense with a NaN row")
+
+
+# ---------------------------------------------------------------- contiguous
+
+def _contig_small(counts, G, N, K, seed):
+    w = workloads.contiguous(G, N, K, seed, counts=counts)
+    qa, sa = oracle.quant_1x128(w["a"])
+    qa, sa = workloads.place_rows(qa, sa, w["rows"], w["m_total"])
+    qb, sb = oracle.quant_128x128(w["b"])
+    return w, qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("counts,N,K", [([5, 130, 1], 144, 256), ([128, 256, 1, 300], 272, 512), ([1], 16, 128),
+                                        ([129, 0, 7], 128, 384)])
+def test_contiguous_matches_oracle(counts, N, K):
+    G = len(counts)
+    w, qa, sa, qb, sb = _contig_small(counts, G, N, K, seed=sum(counts))
+    D = _sentinel(w["m_total"], N)
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(_t(qa), _t(sa), _t(qb), _t(sb), D, _t(w["m_indices"]))
+    got = _np(D)
+    ref = oracle.grouped_contiguous(qa, sa, qb, sb, w["m_indices"], np.full((w["m_total"], N), SENTINEL, np.uint16))
+    pad = w["m_indices"] < 0
+    assert np.array_equal(got[pad], ref[pad])
+    assert_close(got[~pad], ref[~pad], "contiguous")
+
+
+def test_contiguous_out_of_range_indices_untouched():
+    w, qa, sa, qb, sb = _contig_small([100, 60], 2, 128, 256, seed=3)
+    idx = w["m_indices"].copy()
+    idx[3] = 2  # == G
+    idx[140] = -5
+    idx[150] = 999
+    D = _sentinel(w["m_total"], 128)
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(_t(qa), _t(sa), _t(qb), _t(sb), D, _t(idx))
+    got = _np(D)
+    ref = oracle.grouped_contiguous(qa, sa, qb, sb, idx, np.full((w["m_total"], 128), SENTINEL, np.uint16))
+    bad = (idx < 0) | (idx >= 2)
+    assert np.all(got[bad] == SENTINEL)
+    assert_close(got[~bad], ref[~bad], "contiguous with out-of-range indices")
+
+
+# ---------------------------------------------------------------- masked
+
+@pytest.mark.parametrize("mm,max_m,N,K", [([64, 0, 17, 40], 64, 128, 256), ([256, 1, 129, 0, 200, 255], 256, 272, 512),
+                                          ([3, 99, -4], 8, 16, 128), ([0, 0], 128, 128, 128)])
+def test_masked_matches_oracle(mm, max_m, N, K):
+    G = len(mm)
+    w = workloads.masked(G, max_m, N, K, seed=G + max_m, masked_m=mm)
+    qa, sa = oracle.quant_1x128(w["a"]) if w["rows"].size else (np.zeros((0, K), np.uint8),
+                                                                  np.zeros((K // 128, 0), np.float32))
+    qa, sa = masked_layout(qa, sa, w["rows"], G, max_m)
+    qb, sb = oracle.quant_128x128(w["b"])
+    D = _sentinel(G, max_m, N)
+    dg.dg_m_grouped_fp8_gemm_nt_masked(_t(qa), _t(sa), _t(qb), _t(sb), D, _t(w["masked_m"]))
+    got = _np(D)
+    ref = oracle.grouped_masked(qa, sa, qb, sb, w["masked_m"], np.full((G, max_m, N), SENTINEL, np.uint16))
+    valid = np.zeros((G, max_m), bool)
+    for g, m in enumerate(w["masked_m"]):
+        valid[g, :min(max(int(m), 0), max_m)] = True
+    assert np.array_equal(got[~valid], ref[~valid])
+    if valid.any():
+        assert_close(got[valid], ref[valid], "masked")
+
+
+def test_masked_graph_replay_with_device_side_counts():
+    """Capture one masked call in a HIP graph, then change masked_m on the device
+    between replays: each replay must follow the new counts with no re-capture."""
+    G, max_m, N, K = 4, 128, 256, 512
+    w = workloads.masked(G, max_m, N, K, seed=77, masked_m=[max_m] * G)
+    qa, sa = oracle.quant_1x128(w["a"])
+    qa, sa = masked_layout(qa, sa, w["rows"], G, max_m)
+    qb, sb = oracle.quant_128x128(w["b"])
+    A, SA, B, SB = _t(qa), _t(sa), _t(qb), _t(sb)
+    mm_dev = torch.zeros(G, dtype=torch.int32, device=DEV)
+    D = _sentinel(G, max_m, N)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside capture
+        dg.dg_m_grouped_fp8_gemm_nt_masked(A, SA, B, SB, D, mm_dev)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dg.dg_m_grouped_fp8_gemm_nt_masked(A, SA, B, SB, D, mm_dev)
+    for counts in ([128, 0, 5, 64], [1, 127, 0, 128], [0, 0, 0, 3]):
+        D.fill_(-1)  # eager work between replays
+        mm_dev.copy_(torch.tensor(counts, dtype=torch.int32))
+        graph.replay()
+        got = _np(D)
+        ref = oracle.grouped_masked(qa, sa, qb, sb, np.array(counts), np.full((G, max_m, N), SENTINEL, np.uint16))
+        valid = np.zeros((G, max_m), bool)
+        for g, m in enumerate(counts):
+            valid[g, :m] = True
+        assert np.array_equal(got[~valid], ref[~valid]), counts
+        assert_close(got[valid], ref[valid], f"graph replay {counts}")
