@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Throughput of the block-scaled FP8 GEMM path on one MI355X.
+
+Default workload: the dense FP8 NT sweep, M in {64, 128, 4096} x (N, K) in
+{(2112,7168), (24576,1536), (32768,512), (7168,16384), (4096,7168), (7168,2048)}
+with 1x128 activation / 128x128 weight scales and bf16 output, synthetic
+seeded inputs (moe_grouped_matmul_amd.workloads).  One step = for each of the
+18 shapes: quantise the fp32 activations (dg_quant_1x128) and run the GEMM
+(dg_fp8_gemm_nt).  Weights are quantised once beforehand (offline, as in
+inference).  Every shape rotates over enough copies of its buffers that each
+call reads cold HBM (> 2x the 256 MB Infinity Cache per shape).
+
+Output: one JSON line with the whole-step FP8 TFLOPS, per-shape GEMM TFLOPS,
+GB/s and fraction of the MI355X roofline, the dominant kernel's roofline
+(HIP events on the launch stream), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+Other workloads for profiling: --workload large | contiguous | masked | small.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published, no sparsity)
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+ROTATE_BYTES = 768 << 20  # per-shape rotation footprint (3x the 256 MB MALL)
+
+
+def dense_work(M, N, K):
+    """Algorithmic FLOPs and HBM bytes of one dense call (valid rows only)."""
+    flops = 2.0 * M * N * K
+    nbytes = M * K + 4 * M * (K // 128) + N * K + 4 * ((N + 127) // 128) * (K // 128) + 2 * M * N
+    return flops, float(nbytes)
+
+
+def grouped_work(rows_per_group, N, K, index_bytes):
+    flops = 0.0
+    nbytes = float(index_bytes)
+    for r in rows_per_group:
+        if r <= 0:
+            continue
+        flops += 2.0 * r * N * K
+        nbytes += r * K + 4 * r * (K // 128) + N * K + 4 * ((N + 127) // 128) * (K // 128) + 2 * r * N
+    return flops, nbytes
+
+
+def roof_time_us(flops, nbytes):
+    return max(flops / (PEAK_FP8_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.torch.cuda.current_stream())
+        return e
+
+
+def run_dense(args, torch, dg, workloads):
+    dev = torch.device("cuda:0")
+    shapes = workloads.CONFIGS["dense_sweep"] if args.workload == "sweep" else \
+        workloads.CONFIGS["dense_large"] if args.workload == "large" else workloads.CONFIGS["dense_small"]
+    if args.shapes:
+        shapes = [shapes[int(i)] for i in args.shapes.split(",")]
+    prepared = []
+    for s in shapes:
+        M, N, K = s["M"], s["N"], s["K"]
+        a32, b32 = workloads.dense(M, N, K, s["seed"])
+        A32 = torch.from_numpy(a32).to(dev)
+        B32 = torch.from_numpy(b32).to(dev)
+        B8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        SB = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=dev)
+        dg.dg_quant_128x128(B32, B8, SB)  # offline weight quantisation
+        del B32
+        per_set = A32.numel() * 4 + M * K + 4 * M * (K // 128) + N * K + SB.numel() * 4 + 2 * M * N
+        nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        sets = []
+        for i in range(nsets):
+            sets.append(dict(
+                a32=A32 if i == 0 else A32.clone(),
+                a8=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                sa=torch.empty((K // 128, M), dtype=torch.float32, device=dev),
+                b8=B8 if i == 0 else B8.clone(),
+                sb=SB if i == 0 else SB.clone(),
+                d=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+        wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
+        ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
+        flops, nbytes = dense_work(M, N, K)
+        prepared.append(dict(M=M, N=N, K=K, sets=sets, ws=ws, flops=flops, bytes=nbytes,
+                             kernel="fp8_gemm_kernel<128,128,64,64,dense>" if M > 128 else
+                             "fp8_gemm_kernel<64,64,32,32,dense>+splitk_reduce"))
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+
+    def step(i, record):
+        evs = []
+        for p in prepared:
+            st = p["sets"][i % len(p["sets"])]
+            e0 = timer.ev() if record else None
+            dg.dg_quant_1x128(st["a32"], st["a8"], st["sa"])
+            e1 = timer.ev() if record else None
+            dg.dg_fp8_gemm_nt(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["ws"])
+            e2 = timer.ev() if record else None
+            evs.append((e0, e1, e2))
+        return evs
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = timer.ev()
+    w0 = time.perf_counter()
+    all_evs = [step(args.warmup + i, True) for i in range(args.steps)]
+    t_end = timer.ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    per_shape = []
+    for j, p in enumerate(prepared):
+        q_ms = sum(all_evs[i][j][0].elapsed_time(all_evs[i][j][1]) for i in range(args.steps)) / args.steps
+        g_ms = sum(all_evs[i][j][1].elapsed_time(all_evs[i][j][2]) for i in range(args.steps)) / args.steps
+        t_us = g_ms * 1e3
+        rt = roof_time_us(p["flops"], p["bytes"])
+        per_shape.append(dict(M=p["M"], N=p["N"], K=p["K"], gemm_us=round(t_us, 2), quant_us=round(q_ms * 1e3, 2),
+                              tflops=round(p["flops"] / t_us / 1e6, 1), gbs=round(p["bytes"] / t_us / 1e3, 1),
+                              bound="mfma" if p["flops"] / (PEAK_FP8_TFLOPS * 1e12) >= p["bytes"] / (PEAK_HBM_GBS * 1e9)
+                              else "hbm", roof_frac=round(rt / t_us, 4), kernel=p["kernel"]))
+    step_flops = sum(p["flops"] for p in prepared)
+    # dominant kernel: the one with the largest share of GEMM time
+    by_kernel = {}
+    for p, r in zip(prepared, per_shape):
+        k = by_kernel.setdefault(p["kernel"], dict(us=0.0, flops=0.0, bytes=0.0, n=0))
+        k["us"] += r["gemm_us"]
+        k["flops"] += p["flops"]
+        k["bytes"] += p["bytes"]
+        k["n"] += 1
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["us"])
+    avg_us = dom["us"] / dom["n"]
+    mfma_bound = dom["flops"] / (PEAK_FP8_TFLOPS * 1e12) >= dom["bytes"] / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved = dom["flops"] / dom["n"] / avg_us / 1e6
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_FP8_TFLOPS, 4))
+    else:
+        achieved = dom["bytes"] / dom["n"] / avg_us / 1e3
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    roof.update(traffic=None, kernel=dom_name, launches_per_step=dom["n"], avg_launch_us=round(avg_us, 2))
+    return dict(ms_per_step=ms_per_step, wall_s=wall, step_flops=step_flops, per_shape=per_shape, roofline=roof,
+                shapes=[(p["M"], p["N"], p["K"]) for p in prepared])
+
+
+def run_grouped(args, torch, dg, workloads):
+    """M-grouped contiguous (8 experts, tokens per expert uniform in [1, 8192],
+    segments padded to 128) or masked (32 experts x 256 capacity, masked_m
+    uniform in [0, 256]) GEMMs for both (N, K) pairs.  Activations arrive
+    already in e4m3 (as from an expert-parallel dispatch), so a step is the two
+    grouped GEMM calls."""
+    dev = torch.device("cuda:0")
+    cfgs = workloads.CONFIGS[args.workload]
+    prepared = []
+    for c in cfgs:
+        G, N, K = c["G"], c["N"], c["K"]
+        if args.workload == "contiguous":
+            w = workloads.contiguous(G, N, K, c["seed"])
+            rows_total = w["m_total"]
+            A32 = torch.from_numpy(w["a"]).to(dev)
+            q = torch.empty((A32.shape[0], K), dtype=torch.uint8, device=dev)
+            s = torch.empty((K // 128, A32.shape[0]), dtype=torch.float32, device=dev)
+            dg.dg_quant_1x128(A32, q, s)
+            del A32
+            rows_idx = torch.from_numpy(w["rows"]).to(dev)
+            A8 = torch.full((rows_total, K), workloads.TRAP_CODE, dtype=torch.uint8, device=dev)
+            SA = torch.full((K // 128, rows_total), float("nan"), dtype=torch.float32, device=dev)
+            A8[rows_idx] = q
+            SA[:, rows_idx] = s
+            index = torch.from_numpy(w["m_indices"]).to(dev)
+            flops, nbytes = grouped_work(w["counts"], N, K, 4 * rows_total)
+            d_shape = (rows_total, N)
+            counts = [int(x) for x in w["counts"]]
+        else:
+            max_m = c["max_m"]
+            w = workloads.masked(G, max_m, N, K, c["seed"])
+            A32 = torch.from_numpy(w["a"]).to(dev)
+            q = torch.empty((A32.shape[0], K), dtype=torch.uint8, device=dev)
+            s = torch.empty((K // 128, A32.shape[0]), dtype=torch.float32, device=dev)
+            dg.dg_quant_1x128(A32, q, s)
+            del A32
+            rows_idx = torch.from_numpy(w["rows"]).to(dev)
+            A8 = torch.full((G * max_m, K), workloads.TRAP_CODE, dtype=torch.uint8, device=dev)
+            SAf = torch.full((K // 128, G * max_m), float("nan"), dtype=torch.float32, device=dev)
+            A8[rows_idx] = q
+            SAf[:, rows_idx] = s
+            A8 = A8.view(G, max_m, K)
+            SA = SAf.view(K // 128, G, max_m).permute(1, 0, 2).contiguous()
+            index = torch.from_numpy(w["masked_m"]).to(dev)
+            counts = [int(x) for x in w["masked_m"]]
+            flops, nbytes = grouped_work(counts, N, K, 4 * G)
+            d_shape = (G, max_m, N)
+        B32 = torch.from_numpy(w["b"]).to(dev)
+        B8 = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+        SB = torch.empty((G, (N + 127) // 128, K // 128), dtype=torch.float32, device=dev)
+        dg.dg_quant_128x128(B32, B8, SB)
+        del B32
+        per_set = A8.numel() + SA.numel() * 4 + B8.numel() + SB.numel() * 4 + 2 * int(np.prod(d_shape))
+        nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        sets = [dict(a8=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(),
+                     b8=B8 if i == 0 else B8.clone(), sb=SB if i == 0 else SB.clone(),
+                     d=torch.empty(d_shape, dtype=torch.bfloat16, device=dev)) for i in range(nsets)]
+        prepared.append(dict(G=G, N=N, K=K, sets=sets, index=index, flops=flops, bytes=nbytes, counts=counts,
+                             rows=rows_total if args.workload == "contiguous" else G * c["max_m"]))
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+
+    def step(i, record):
+        evs = []
+        for p in prepared:
+            st = p["sets"][i % len(p["sets"])]
+            e0 = timer.ev() if record else None
+            if args.workload == "contiguous":
+                dg.dg_m_grouped_fp8_gemm_nt_contiguous(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"])
+            else:
+                dg.dg_m_grouped_fp8_gemm_nt_masked(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"],
+                                                   expected_m=128)
+            e1 = timer.ev() if record else None
+            evs.append((e0, e1))
+        return evs
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = timer.ev()
+    w0 = time.perf_counter()
+    all_evs = [step(args.warmup + i, True) for i in range(args.steps)]
+    t_end = timer.ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per_shape = []
+    for j, p in enumerate(prepared):
+        t_us = sum(all_evs[i][j][0].elapsed_time(all_evs[i][j][1]) for i in range(args.steps)) / args.steps * 1e3
+        rt = roof_time_us(p["flops"], p["bytes"])
+        mf = p["flops"] / (PEAK_FP8_TFLOPS * 1e12) >= p["bytes"] / (PEAK_HBM_GBS * 1e9)
+        per_shape.append(dict(G=p["G"], N=p["N"], K=p["K"], rows=p["rows"], valid_rows=int(sum(max(c, 0) for c in p["counts"])),
+                              gemm_us=round(t_us, 2), tflops=round(p["flops"] / t_us / 1e6, 1),
+                              gbs=round(p["bytes"] / t_us / 1e3, 1), bound="mfma" if mf else "hbm",
+                              roof_frac=round(rt / t_us, 4)))
+    big = max(per_shape, key=lambda r: r["gemm_us"])
+    if big["bound"] == "mfma":
+        roof = dict(bound="mfma", achieved=big["tflops"], peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                    frac=round(big["tflops"] / PEAK_FP8_TFLOPS, 4))
+    else:
+        roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
+    kname = "contiguous" if args.workload == "contiguous" else "masked"
+    roof.update(traffic=None, kernel=f"fp8_gemm_kernel<{kname}> ({big['N']}x{big['K']})",
+                avg_launch_us=big["gemm_us"])
+    name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
+    config = dict(workload=name, shapes=[f"G={p['G']} N={p['N']} K={p['K']}" for p in prepared],
+                  step="grouped GEMM per (N,K) pair", cold_hbm=True)
+    return dict(ms_per_step=ms_per_step, wall_s=wall, step_flops=sum(p["flops"] for p in prepared),
+                per_shape=per_shape, roofline=roof, name=name, config=config)
+
+
+def cpu_baseline(shapes, workloads):
+    """The CPU oracle as it stands, on the first min(M, 128) rows of each shape:
+    activation quantisation + GEMM timed (weights quantised beforehand, untimed)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    t_total = 0.0
+    flops = 0.0
+    for (M, N, K), s in shapes:
+        rows = min(M, 128)
+        a32, b32 = workloads.dense(rows, N, K, s["seed"])
+        qb, sb = oracle.quant_128x128(b32)
+        t0 = time.perf_counter()
+        qa, sa = oracle.quant_1x128(a32)
+        oracle.gemm_nt(qa, sa, qb, sb)
+        t_total += time.perf_counter() - t0
+        flops += 2.0 * rows * N * K
+    return dict(value=round(flops / t_total / 1e12, 5), unit="TFLOPS", cores=int(threads), kind="oracle",
+                sample=f"first min(M,128) rows of each of the {len(shapes)} shapes: fp64 oracle 1x128 quantisation "
+                       f"+ promoted GEMM + bf16 rounding ({flops / 1e9:.1f} GFLOP in {t_total:.1f} s); "
+                       "weights pre-quantised untimed")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the FP8 GEMM path is a per-GPU kernel and multi-GPU runs are not part of it", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from moe_grouped_matmul_amd import dg, workloads
+
+    if not os.path.exists(dg.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+
+    if args.workload in ("sweep", "large", "small"):
+        r = run_dense(args, torch, dg, workloads)
+        name = {"sweep": "dense_fp8_nt_sweep_18_shapes", "large": "dense_fp8_nt_4096x7168x16384",
+                "small": "dense_fp8_nt_64x2112x7168"}[args.workload]
+        config = dict(workload=name, shapes=[f"{m}x{n}x{k}" for m, n, k in r["shapes"]],
+                      scales="1x128 activations, 128x128 weights, fp32", out="bf16",
+                      step="dg_quant_1x128 + dg_fp8_gemm_nt per shape", cold_hbm=True)
+    else:
+        r = run_grouped(args, torch, dg, workloads)
+        name = r["name"]
+        config = r["config"]
+
+    value = r["step_flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+    line = {
+        "metric": "FP8 TFLOPS + GB/s per shape (dense/contig/masked), % of MI355X roofline",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded DeepSeek-V3-shaped fp32 sources, quantised on device)",
+        "config": config,
+        "per_shape": r["per_shape"],
+        "roofline": r["roofline"],
+    }
+    if not args.no_cpu_baseline and args.workload in ("sweep", "large", "small"):
+        shp = workloads.CONFIGS["dense_sweep"] if args.workload == "sweep" else \
+            workloads.CONFIGS["dense_large"] if args.workload == "large" else workloads.CONFIGS["dense_small"]
+        if args.shapes:
+            shp = [shp[int(i)] for i in args.shapes.split(",")]
+        line["cpu_baseline"] = cpu_baseline([((s["M"], s["N"], s["K"]), s) for s in shp], workloads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

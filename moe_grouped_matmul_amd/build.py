@@ -30,14 +30,17 @@ COMMON = [
     "-Wall",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the promotion FMAs read them without
+    # v_accvgpr_read copies and consecutive MFMAs get distinct destinations
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, build_dir, extra):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,25 +49,29 @@ def _compile(src):
     return obj, r.stderr
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, out_path=None, extra_flags=()):
+    """Compile and link; out_path/extra_flags serve experiments with compile-time
+    tuning macros (the default build is what the package loads)."""
+    lib_path = out_path or LIB_PATH
+    build_dir = BUILD if out_path is None else os.path.join(os.path.dirname(out_path), "_build")
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, build_dir, list(extra_flags)), SOURCES))
     report = []
     for (obj, log), src in zip(results, SOURCES):
         lines = [l for l in log.splitlines() if "remark" in l or "Function Name" in l or ":" in l]
         report.append(f"== {src}\n" + "\n".join(l for l in log.splitlines() if "remark:" in l))
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+    with open(os.path.join(build_dir, "resource_usage.txt"), "w") as f:
         f.write("\n".join(report) + "\n")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *[o for o, _ in results], "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":

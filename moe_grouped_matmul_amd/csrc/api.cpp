@@ -103,7 +103,7 @@ struct DensePlan {
 
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   DensePlan pl;
-  pl.cfg = M <= 64 ? dg::kTile64x64 : dg::kTile128x128;
+  pl.cfg = M <= 128 ? dg::kTile64x64 : dg::kTile128x128;
   const dg::TileShape ts = dg::tile_shape(pl.cfg);
   pl.m_tiles = (int)ceil_div(M, ts.bm);
   pl.n_tiles = (int)ceil_div(N, ts.bn);
@@ -158,9 +158,9 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   p.splits = pl.splits;
   p.kb_per_split = pl.kb_per_split;
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld tile=%dx%d splits=%d grid=%lld\n", (long long)M,
-                 (long long)N, (long long)K, dg::tile_shape(pl.cfg).bm, dg::tile_shape(pl.cfg).bn, pl.splits,
-                 (long long)pl.m_tiles * pl.n_tiles * pl.splits);
+    std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
+                 (long long)M, (long long)N, (long long)K, dg::tile_shape(pl.cfg).bm, dg::tile_shape(pl.cfg).bn,
+                 pl.m_tiles, pl.n_tiles, pl.splits);
   const hipError_t e = dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -183,8 +183,9 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  const int cfg = dg::kTile128x128;
-  const dg::TileShape ts = dg::tile_shape(cfg);
+  // 128-row tiles: each tile lies inside one 128-row aligned expert segment
+  const int bm = 128;
+  const int bn = 128;
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
@@ -196,14 +197,14 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.N = (int)N;
   p.K = (int)K;
   p.G = (int)G;
-  p.m_tiles = (int)ceil_div(M_total, ts.bm);
-  p.n_tiles = (int)ceil_div(N, ts.bn);
+  p.m_tiles = (int)ceil_div(M_total, bm);
+  p.n_tiles = (int)ceil_div(N, bn);
   p.splits = 1;
   p.kb_per_split = (int)(K / 128);
   if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d\n", (long long)M_total,
-                 (long long)N, (long long)K, (long long)G, ts.bm, ts.bn);
-  const hipError_t e = dg::launch_gemm(dg::kContiguous, cfg, p, 1, static_cast<hipStream_t>(stream));
+                 (long long)N, (long long)K, (long long)G, bm, bn);
+  const hipError_t e = dg::launch_gemm(dg::kContiguous, dg::kTile128x128, p, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

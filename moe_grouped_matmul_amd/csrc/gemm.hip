@@ -26,23 +26,10 @@
 // second kernel sums in a fixed order (deterministic).
 
 #include "dg_internal.hpp"
+#include "gemm_common.hpp"
 
 namespace dg {
 namespace {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte chunk swizzle inside a 128-byte LDS row: 16 consecutive rows that
-// read the same logical chunk land on 16 distinct bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ void __launch_bounds__(256) fp8_gemm_kernel(GemmParams p) {

@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdg_mi355x.so")
+# DG_LIBRARY may point at another build of the same library (tuning experiments)
+LIB_PATH = os.environ.get("DG_LIBRARY", os.path.join(_HERE, "libdg_mi355x.so"))
 
 DG_OK = 0
 DG_ERR_INVALID_ARG = 1

@@ -98,7 +98,9 @@ def test_quant_128x128_bit_exact(G, N, K):
 # ---------------------------------------------------------------- dense GEMM
 
 DENSE_SMALL = [(1, 16, 128), (64, 2112, 512), (70, 272, 512), (128, 384, 256), (130, 144, 640), (257, 400, 384),
-               (64, 128, 2048)]
+               (64, 128, 2048),
+               # large-tile kernel: K blocks 1..5 exercise every ring-slot tail, ragged M and N
+               (256, 128, 128), (300, 272, 256), (512, 384, 384), (1000, 528, 512), (777, 2112, 640), (2048, 256, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_SMALL)
@@ -111,7 +113,7 @@ def test_dense_matches_oracle(M, N, K, workspace):
     assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"dense {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 272, 512), (128, 256, 384), (200, 144, 1024), (1, 16, 256)])
+@pytest.mark.parametrize("M,N,K", [(64, 272, 512), (128, 256, 384), (200, 144, 1024), (1, 16, 256), (512, 400, 640)])
 def test_dense_integer_inputs_bit_exact(M, N, K):
     # integers in [-10, 9] with unit scales: every partial and every fp32 sum is
     # an exact integer below 2^24, so the bf16 result must equal the oracle's bits
@@ -159,7 +161,7 @@ def _contig_small(counts, G, N, K, seed):
 
 
 @pytest.mark.parametrize("counts,N,K", [([5, 130, 1], 144, 256), ([128, 256, 1, 300], 272, 512), ([1], 16, 128),
-                                        ([129, 0, 7], 128, 384)])
+                                        ([129, 0, 7], 128, 384), ([700, 33, 256, 1], 400, 640)])
 def test_contiguous_matches_oracle(counts, N, K):
     G = len(counts)
     w, qa, sa, qb, sb = _contig_small(counts, G, N, K, seed=sum(counts))
