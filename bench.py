@@ -34,6 +34,8 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published, no sparsity)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 ROTATE_BYTES = 768 << 20  # per-shape rotation footprint (3x the 256 MB MALL)
+CPU_SAMPLE_ROWS = 2048  # rows per shape in the CPU-oracle baseline sample
+COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
 
 
 def dense_work(M, N, K):
@@ -66,6 +68,8 @@ def parse():
     ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -289,7 +293,7 @@ def run_grouped(args, torch, dg, workloads):
 
 
 def cpu_baseline(shapes, workloads):
-    """The CPU oracle as it stands, on the first min(M, 128) rows of each shape:
+    """The CPU oracle as it stands, on the first min(M, 1024) rows of each shape:
     activation quantisation + GEMM timed (weights quantised beforehand, untimed)."""
     import oracle
 
@@ -302,7 +306,7 @@ def cpu_baseline(shapes, workloads):
     t_total = 0.0
     flops = 0.0
     for (M, N, K), s in shapes:
-        rows = min(M, 128)
+        rows = min(M, CPU_SAMPLE_ROWS)
         a32, b32 = workloads.dense(rows, N, K, s["seed"])
         qb, sb = oracle.quant_128x128(b32)
         t0 = time.perf_counter()
@@ -311,7 +315,7 @@ def cpu_baseline(shapes, workloads):
         t_total += time.perf_counter() - t0
         flops += 2.0 * rows * N * K
     return dict(value=round(flops / t_total / 1e12, 5), unit="TFLOPS", cores=int(threads), kind="oracle",
-                sample=f"first min(M,128) rows of each of the {len(shapes)} shapes: fp64 oracle 1x128 quantisation "
+                sample=f"first min(M,{CPU_SAMPLE_ROWS}) rows of each of the {len(shapes)} shapes: fp64 oracle 1x128 quantisation "
                        f"+ promoted GEMM + bf16 rounding ({flops / 1e9:.1f} GFLOP in {t_total:.1f} s); "
                        "weights pre-quantised untimed")
 
@@ -332,6 +336,12 @@ def main():
 
         __graft_entry__.build()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.workload in ("sweep", "large", "small"):
         r = run_dense(args, torch, dg, workloads)
