@@ -116,7 +116,7 @@ def run_dense(args, torch, dg, workloads):
         ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
         flops, nbytes = dense_work(M, N, K)
         prepared.append(dict(M=M, N=N, K=K, sets=sets, ws=ws, flops=flops, bytes=nbytes,
-                             kernel="fp8_gemm_kernel<128,128,64,64,dense>" if M > 128 else
+                             kernel="fp8_gemm_lds_kernel<4,2,dense>" if M > 128 else
                              "fp8_gemm_kernel<64,64,32,32,dense>+splitk_reduce"))
     torch.cuda.synchronize()
     timer = Timer(torch)
@@ -282,8 +282,8 @@ def run_grouped(args, torch, dg, workloads):
     else:
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
-    kname = "contiguous" if args.workload == "contiguous" else "masked"
-    roof.update(traffic=None, kernel=f"fp8_gemm_kernel<{kname}> ({big['N']}x{big['K']})",
+    kname = "fp8_gemm_lds_kernel<2,4,contiguous>" if args.workload == "contiguous" else "fp8_gemm_kernel<masked>"
+    roof.update(traffic=None, kernel=f"{kname} ({big['N']}x{big['K']})",
                 avg_launch_us=big["gemm_us"])
     name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
     config = dict(workload=name, shapes=[f"G={p['G']} N={p['N']} K={p['K']}" for p in prepared],

@@ -21,7 +21,10 @@ LIB_NAME = "libdg_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_lds.hip", "api.cpp"]
+# per-source flags: the LDS-ring kernel needs the iterative ILP scheduler to
+# stay within 256 VGPRs (two waves per SIMD) without spilling
+SOURCE_FLAGS = {"gemm_lds.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 COMMON = [
     "-O3",
     "--offload-arch=gfx950",
@@ -40,7 +43,7 @@ COMMON = [
 
 def _compile(src, build_dir, extra):
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *SOURCE_FLAGS.get(src, []), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

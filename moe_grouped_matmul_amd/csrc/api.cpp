@@ -94,6 +94,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Dense split-K plan: enough work items to cover the CUs twice when the
 // output alone has too few tiles.  Splits never exceed the K blocks.
 struct DensePlan {
+  bool lds;  // LDS-ring kernel (gemm_lds.hip)
   int cfg;
   int m_tiles;
   int n_tiles;
@@ -101,8 +102,24 @@ struct DensePlan {
   int kb_per_split;
 };
 
+// The LDS-ring kernel addresses operands with 32-bit buffer offsets.
+bool fits_32bit(int64_t rows, int64_t N, int64_t K) {
+  const int64_t lim = ((int64_t)1 << 32) - 1;
+  return (rows + 256) * K < lim && (N + 256) * K < lim && rows * (K / 128) * 4 < lim;
+}
+
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   DensePlan pl;
+  pl.lds = false;
+  if (M > 128 && fits_32bit(M, N, K)) {
+    pl.lds = true;
+    pl.cfg = dg::kLds256x128;
+    pl.m_tiles = (int)ceil_div(M, 256);
+    pl.n_tiles = (int)ceil_div(N, 128);
+    pl.splits = 1;
+    pl.kb_per_split = (int)(K / 128);
+    return pl;
+  }
   pl.cfg = M <= 128 ? dg::kTile64x64 : dg::kTile128x128;
   const dg::TileShape ts = dg::tile_shape(pl.cfg);
   pl.m_tiles = (int)ceil_div(M, ts.bm);
@@ -159,9 +176,12 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   p.kb_per_split = pl.kb_per_split;
   if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
-                 (long long)M, (long long)N, (long long)K, dg::tile_shape(pl.cfg).bm, dg::tile_shape(pl.cfg).bn,
+                 (long long)M, (long long)N, (long long)K,
+                 pl.lds ? dg::lds_tile_shape(pl.cfg).bm : dg::tile_shape(pl.cfg).bm,
+                 pl.lds ? dg::lds_tile_shape(pl.cfg).bn : dg::tile_shape(pl.cfg).bn,
                  pl.m_tiles, pl.n_tiles, pl.splits);
-  const hipError_t e = dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
+  const hipError_t e = pl.lds ? dg::launch_gemm_lds(dg::kDense, pl.cfg, p, static_cast<hipStream_t>(stream))
+                              : dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -184,8 +204,9 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
   // 128-row tiles: each tile lies inside one 128-row aligned expert segment
+  const bool lds = fits_32bit(M_total, N, K);
   const int bm = 128;
-  const int bn = 128;
+  const int bn = lds ? 256 : 128;
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
@@ -204,7 +225,8 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d\n", (long long)M_total,
                  (long long)N, (long long)K, (long long)G, bm, bn);
-  const hipError_t e = dg::launch_gemm(dg::kContiguous, dg::kTile128x128, p, 1, static_cast<hipStream_t>(stream));
+  const hipError_t e = lds ? dg::launch_gemm_lds(dg::kContiguous, dg::kLds128x256, p, static_cast<hipStream_t>(stream))
+                           : dg::launch_gemm(dg::kContiguous, dg::kTile128x128, p, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,0 +1,281 @@
+// Block-scaled FP8 GEMM for gfx950 with a 3-slot LDS ring fed by
+// buffer-to-LDS loads: the kernel for MFMA-bound dense and M-grouped
+// contiguous problems.
+//
+// The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
+// closed-form equation: for every 128-wide K block the fp8 partial product of
+// a tile is formed by the matrix cores and promoted into an fp32 accumulator
+// with alpha[row, k] * beta[k]; the epilogue rounds to bf16.
+//
+// Organisation:
+//   * 512 threads = 8 wave64s (two per SIMD), arranged WGM x WGN, each wave a
+//     64 x 64 sub-tile of 4 x 4 v_mfma_f32_16x16x128_f8f6f4 tiles; one MFMA
+//     covers a whole 128-deep K block;
+//   * A, B and the row scales alpha of K block k travel HBM -> LDS with
+//     gfx950 buffer-to-LDS loads (no staging registers) into ring slot k % 3,
+//     issued two K blocks ahead; each wave waits for its own loads with an
+//     explicit vmcnt and one s_barrier per K block publishes the slot and
+//     frees the slot of block k-1 for block k+2.  The three slots are
+//     separate LDS arrays so the compiler can tell in-flight DMA targets
+//     from the slot being read;
+//   * LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk
+//     c ^ (r % 8), so 8 consecutive rows read at one logical chunk hit 8
+//     distinct 16-byte bank groups (conflict-free at 128 B/clk);
+//   * a lane's MFMA operand is row (lane % 16), K chunks q and q + 4
+//     (q = lane / 16) of the 128-byte block -- the same K permutation for A
+//     and B, so every dot product is unchanged;
+//   * promotion with a rescaled accumulator: the kernel keeps u = acc / s_k,
+//     s_k = alpha[row, k] * beta[k] for the current block.  Entering block k
+//     it multiplies u by s_{k-1} / s_k (one fp32 multiply per element, the
+//     same VALU count as a promotion FMA) and the MFMA then adds the block's
+//     fp8 partial straight into u (C = D = u).  Every 128-K partial enters
+//     the fp32 sum exactly once with its own alpha * beta; the epilogue
+//     returns u * s_last.  This needs no partial-product registers and no
+//     MFMA -> VALU round trip.  It differs from one FMA per partial only in
+//     rounding (a few fp32 ulps per block) and assumes the running sum
+//     divided by the current block's scale stays inside the fp32 range
+//     (true unless a 128-K group's amax is below ~1e-30 after large ones);
+//   * tiles are mapped so each XCD runs a contiguous, m-grouped range
+//     (operand reuse in that XCD's L2).
+
+#include "dg_internal.hpp"
+#include "gemm_common.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
+}
+
+template <int WGM, int WGN, int MODE>
+__global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
+  // The body uses device-only builtins (buffer resources); the host pass only
+  // needs the kernel's signature to emit its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int TM = 4;
+  constexpr int TN = 4;
+  constexpr int BM = WGM * 64;
+  constexpr int BN = WGN * 64;
+  constexpr int NWAVES = 8;
+  constexpr int A_INS = BM / 8 / NWAVES;  // 1 KB (8-row) loads per wave per K block
+  constexpr int B_INS = BN / 8 / NWAVES;
+  constexpr int L_BLOCK = A_INS + B_INS + 1;  // + one alpha load per wave
+  constexpr int GM = 4;                      // m-tiles per tile group
+  static_assert(WGM * WGN == NWAVES, "eight waves");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && A_INS >= 1 && B_INS >= 1, "tile");
+  static_assert(BM <= 256, "alpha slots");
+  static_assert(L_BLOCK < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[BN * 128];
+  // alpha: 64 rows per wave; waves past BM/64 load clamped rows nobody reads
+  __shared__ __attribute__((aligned(256))) float sS0[NWAVES * 64];
+  __shared__ __attribute__((aligned(256))) float sS1[NWAVES * 64];
+  __shared__ __attribute__((aligned(256))) float sS2[NWAVES * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN;
+  const int wn = wave % WGN;
+
+  int mt, nt;
+  grouped_mn(xcd_tile(blockIdx.x, p.m_tiles * p.n_tiles), p.m_tiles, p.n_tiles, GM, &mt, &nt);
+
+  const int K = p.K;
+  const int N = p.N;
+  const int KB = K >> 7;
+  const int NB = (N + 127) >> 7;
+  const int rows = (int)p.rows;
+  const int m0 = mt * BM;
+  const int n0 = nt * BN;
+  const uint8_t* Bp = p.B;
+  const float* sfb = p.sfb;
+  const int row_limit = rows - m0 < BM ? rows - m0 : BM;
+  int expert = 0;
+
+  if (MODE == kContiguous) {
+    // expert of this tile = largest valid index among its rows (computed by
+    // every wave; rows of an aligned block belong to one expert)
+    int e = -1;
+    for (int r = lane; r < row_limit; r += 64) {
+      const int v = p.index[m0 + r];
+      if (v >= 0 && v < p.G) e = v > e ? v : e;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const int o = __shfl_xor(e, off);
+      e = o > e ? o : e;
+    }
+    expert = __builtin_amdgcn_readfirstlane(e);
+    if (expert < 0) return;  // padding-only tile (uniform over the workgroup)
+    Bp += (int64_t)expert * N * K;
+    sfb += (int64_t)expert * NB * KB;
+  }
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)rows * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp, (uint32_t)N * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (uint32_t)rows * (uint32_t)KB * 4u);
+
+  // DMA sources: instruction i of this wave fills LDS rows 8*(i*8 + wave) + lane/8;
+  // lane chunk (lane % 8) of row r holds K chunk (lane % 8) ^ (r % 8).  The
+  // offsets are linear in i (stride 64 rows); rows past the end of a buffer
+  // fall outside its buffer range and read as zeros -- they only feed
+  // accumulator rows / columns that are never stored.
+  const int dma_chunk = ((lane & 7) ^ ((lane >> 3) & 7)) << 4;
+  const uint32_t a_src = (uint32_t)(m0 + 8 * wave + (lane >> 3)) * (uint32_t)K + (uint32_t)dma_chunk;
+  const uint32_t b_src = (uint32_t)(n0 + 8 * wave + (lane >> 3)) * (uint32_t)K + (uint32_t)dma_chunk;
+  const uint32_t dma_stride = 64u * (uint32_t)K;
+  const uint32_t s_src = (uint32_t)(m0 + wave * 64 + lane) * 4u;
+
+  // fragment reads: row base + 16 t + (lane % 16), K chunks q and q + 4
+  const int q = lane >> 4;
+  const uint32_t fr_lo = (uint32_t)((lane & 15) * 128 + ((q ^ (lane & 7)) << 4));
+  const uint32_t fr_hi = (uint32_t)((lane & 15) * 128 + (((q + 4) ^ (lane & 7)) << 4));
+  const uint32_t a_row0 = (uint32_t)(wm * 64 * 128);
+  const uint32_t b_row0 = (uint32_t)(wn * 64 * 128);
+
+  // this wave's weight-scale row (its 64 columns lie in one 128-column block);
+  // made explicitly uniform so the per-block read is a scalar load
+  int nblk = (n0 + wn * 64) >> 7;
+  nblk = nblk < NB ? nblk : NB - 1;
+  const DG_CONST float* sfb_w;
+  {
+    const uint64_t a = reinterpret_cast<uint64_t>(sfb + nblk * KB);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
+  }
+
+  f32x4 u[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) u[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 s_prev[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) s_prev[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#define DG_SA(st) ((st) == 0 ? sA0 : ((st) == 1 ? sA1 : sA2))
+#define DG_SB(st) ((st) == 0 ? sB0 : ((st) == 1 ? sB1 : sB2))
+#define DG_SS(st) ((st) == 0 ? sS0 : ((st) == 1 ? sS1 : sS2))
+
+  // all loads of K block kb_ into ring slot st_
+#define DG_ISSUE(st_, kb_)                                                                                 \
+  do {                                                                                                     \
+    const int ks_ = (kb_) << 7;                                                                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_INS; ++i_)                                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (DG_LDS void*)(DG_SA(st_) + (i_ * NWAVES + wave) * 1024), \
+                                                 16, a_src + i_ * dma_stride, ks_, 0, 0);                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_INS; ++i_)                                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (DG_LDS void*)(DG_SB(st_) + (i_ * NWAVES + wave) * 1024), \
+                                                 16, b_src + i_ * dma_stride, ks_, 0, 0);                  \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (DG_LDS void*)(DG_SS(st_) + wave * 64), 4, s_src,         \
+                                             (kb_) * rows * 4, 0, 0);                                      \
+  } while (0)
+
+#define DG_FRAG(dst_, base_, off_)                                                                         \
+  do {                                                                                                     \
+    const uint4 lo_ = *reinterpret_cast<const uint4*>((base_) + fr_lo + (off_));                          \
+    const uint4 hi_ = *reinterpret_cast<const uint4*>((base_) + fr_hi + (off_));                          \
+    dst_ = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
+  } while (0)
+
+  // One K block.  When block k starts, only block k+1's L_BLOCK loads (issued
+  // with block k-1) may still be in flight.  Past the last block the issue
+  // repeats the last block into a slot nobody reads again, which keeps the
+  // wait count the same in every block.
+#define DG_STEP(st_, k_)                                                                                   \
+  do {                                                                                                     \
+    wait_vmcnt<L_BLOCK>();                                                                                 \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    DG_ISSUE(((st_) + 2) % 3, (k_) + 2 < KB ? (k_) + 2 : KB - 1);                                         \
+    const float beta_ = sfb_w[(k_)];                                                                       \
+    const uint8_t* as_ = DG_SA(st_) + a_row0;                                                              \
+    const uint8_t* bs_ = DG_SB(st_) + b_row0;                                                              \
+    i32x8 af_[TM];                                                                                         \
+    f32x4 r_[TM];                                                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
+      DG_FRAG(af_[i_], as_, i_ * 2048);                                                                    \
+      const f32x4 al_ = *reinterpret_cast<const f32x4*>(DG_SS(st_) + wm * 64 + i_ * 16 + q * 4);          \
+      const f32x4 sc_ = al_ * beta_;                                                                       \
+      _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) r_[i_][v_] = s_prev[i_][v_] * __builtin_amdgcn_rcpf(sc_[v_]); \
+      s_prev[i_] = sc_;                                                                                    \
+    }                                                                                                      \
+    _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                    \
+      i32x8 bf_;                                                                                           \
+      DG_FRAG(bf_, bs_, j_ * 2048);                                                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
+        u[i_][j_] *= r_[i_];                                                                               \
+        u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_[i_], bf_, u[i_][j_], 0, 0, 0, 0, 0, 0); \
+      }                                                                                                    \
+    }                                                                                                      \
+  } while (0)
+
+  DG_ISSUE(0, 0);
+  DG_ISSUE(1, 1 < KB ? 1 : 0);
+  int k = 0;
+  for (; k + 3 <= KB; k += 3) {
+    DG_STEP(0, k);
+    DG_STEP(1, k + 1);
+    DG_STEP(2, k + 2);
+  }
+  if (k < KB) DG_STEP(0, k);
+  if (k + 1 < KB) DG_STEP(1, k + 1);
+  wait_vmcnt<0>();  // no LDS writes may be in flight when the workgroup ends
+
+#undef DG_STEP
+#undef DG_FRAG
+#undef DG_ISSUE
+#undef DG_SA
+#undef DG_SB
+#undef DG_SS
+
+  // epilogue: lane holds column (lane & 15) and rows 4 * (lane >> 4) + v of each 16x16 tile
+  uint16_t* D = p.D;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = wm * 64 + i * 16 + q * 4 + v;
+      if (r >= row_limit) continue;
+      const int64_t gr = (int64_t)m0 + r;
+      if (MODE == kContiguous && p.index[gr] != expert) continue;
+      uint16_t* drow = D + gr * N;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int gc = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (gc < N) drow[gc] = f32_to_bf16_rne(u[i][j][v] * s_prev[i][v]);
+      }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int WGM, int WGN>
+hipError_t launch_lds_cfg(int mode, const GemmParams& p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.m_tiles * p.n_tiles;
+  if (grid <= 0) return hipSuccess;
+  if (mode == kContiguous)
+    hipLaunchKernelGGL((fp8_gemm_lds_kernel<WGM, WGN, kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8_gemm_lds_kernel<WGM, WGN, kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+TileShape lds_tile_shape(int cfg) { return cfg == kLds256x128 ? TileShape{256, 128} : TileShape{128, 256}; }
+
+hipError_t launch_gemm_lds(int mode, int cfg, const GemmParams& p, hipStream_t stream) {
+  return cfg == kLds256x128 ? launch_lds_cfg<4, 2>(mode, p, stream) : launch_lds_cfg<2, 4>(mode, p, stream);
+}
+
+}  // namespace dg
