@@ -32,6 +32,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned (used
+// before a barrier after which other waves overwrite the slot it read).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
 // Map a workgroup id to a linear tile id so that the tiles one XCD runs are a
 // contiguous range: workgroups are dealt to the 8 XCDs round-robin, and XCD x
 // is given tiles [start_x, start_x + count_x).

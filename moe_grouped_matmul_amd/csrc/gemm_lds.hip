@@ -13,11 +13,12 @@
 //     covers a whole 128-deep K block;
 //   * A, B and the row scales alpha of K block k travel HBM -> LDS with
 //     gfx950 buffer-to-LDS loads (no staging registers) into ring slot k % 3,
-//     issued two K blocks ahead; each wave waits for its own loads with an
-//     explicit vmcnt and one s_barrier per K block publishes the slot and
-//     frees the slot of block k-1 for block k+2.  The three slots are
-//     separate LDS arrays so the compiler can tell in-flight DMA targets
-//     from the slot being read;
+//     issued three K blocks ahead: a wave first copies all its operands of
+//     block k from LDS into registers, so after one s_barrier per K block
+//     slot k % 3 is free again and receives block k+3 while the MFMAs run
+//     from registers.  Each wave waits for its own loads with an explicit
+//     vmcnt; the three slots are separate LDS arrays so the compiler can tell
+//     in-flight DMA targets from the slot being read;
 //   * LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk
 //     c ^ (r % 8), so 8 consecutive rows read at one logical chunk hit 8
 //     distinct 16-byte bank groups (conflict-free at 128 B/clk);
@@ -188,39 +189,53 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     dst_ = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
   } while (0)
 
-  // One K block.  When block k starts, only block k+1's L_BLOCK loads (issued
-  // with block k-1) may still be in flight.  Past the last block the issue
-  // repeats the last block into a slot nobody reads again, which keeps the
-  // wait count the same in every block.
+  // One K block k, its data already in ring slot k % 3:
+  //   1. read all of this wave's fragments and row scales of block k into
+  //      registers;
+  //   2. wait until this wave's loads of block k+1 have landed (only block
+  //      k+2's L_BLOCK loads may remain in flight) and its LDS reads of
+  //      block k have returned, then one s_barrier: after it block k+1 is
+  //      complete in LDS and no wave reads slot k % 3 again;
+  //   3. issue block k+3 into slot k % 3 (three blocks of load latency cover);
+  //   4. MFMAs and promotion from registers, overlapping the loads in flight.
+  // Past the last block the issue repeats the last block into a slot nobody
+  // reads again, which keeps the wait count the same in every block.
 #define DG_STEP(st_, k_)                                                                                   \
   do {                                                                                                     \
-    wait_vmcnt<L_BLOCK>();                                                                                 \
-    __builtin_amdgcn_s_barrier();                                                                          \
-    DG_ISSUE(((st_) + 2) % 3, (k_) + 2 < KB ? (k_) + 2 : KB - 1);                                         \
     const float beta_ = sfb_w[(k_)];                                                                       \
     const uint8_t* as_ = DG_SA(st_) + a_row0;                                                              \
     const uint8_t* bs_ = DG_SB(st_) + b_row0;                                                              \
     i32x8 af_[TM];                                                                                         \
-    f32x4 r_[TM];                                                                                          \
+    i32x8 bf_[TN];                                                                                         \
+    f32x4 al_[TM];                                                                                         \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
       DG_FRAG(af_[i_], as_, i_ * 2048);                                                                    \
-      const f32x4 al_ = *reinterpret_cast<const f32x4*>(DG_SS(st_) + wm * 64 + i_ * 16 + q * 4);          \
-      const f32x4 sc_ = al_ * beta_;                                                                       \
+      al_[i_] = *reinterpret_cast<const f32x4*>(DG_SS(st_) + wm * 64 + i_ * 16 + q * 4);                  \
+    }                                                                                                      \
+    _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) DG_FRAG(bf_[j_], bs_, j_ * 2048);                   \
+    wait_vmcnt<L_BLOCK>();                                                                                 \
+    wait_lgkmcnt0(); /* own reads of slot k done before anyone may refill it */                           \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    DG_ISSUE((st_), (k_) + 3 < KB ? (k_) + 3 : KB - 1);                                                   \
+    f32x4 r_[TM];                                                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
+      const f32x4 sc_ = al_[i_] * beta_;                                                                   \
       _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) r_[i_][v_] = s_prev[i_][v_] * __builtin_amdgcn_rcpf(sc_[v_]); \
       s_prev[i_] = sc_;                                                                                    \
     }                                                                                                      \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                    \
-      i32x8 bf_;                                                                                           \
-      DG_FRAG(bf_, bs_, j_ * 2048);                                                                        \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         u[i_][j_] *= r_[i_];                                                                               \
-        u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_[i_], bf_, u[i_][j_], 0, 0, 0, 0, 0, 0); \
+        u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_[i_], bf_[j_], u[i_][j_], 0, 0, 0, 0, 0, 0); \
       }                                                                                                    \
     }                                                                                                      \
   } while (0)
 
   DG_ISSUE(0, 0);
-  DG_ISSUE(1, 1 < KB ? 1 : 0);
+  DG_ISSUE(1, 1 < KB ? 1 : KB - 1);
+  DG_ISSUE(2, 2 < KB ? 2 : KB - 1);
+  wait_vmcnt<2 * L_BLOCK>();  // block 0 landed (this wave's part)
+  __builtin_amdgcn_s_barrier();
   int k = 0;
   for (; k + 3 <= KB; k += 3) {
     DG_STEP(0, k);
