@@ -249,8 +249,9 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
   (void)expected_m;
-  const int cfg = max_m <= 64 ? dg::kTile64x128 : dg::kTile128x128;
-  const dg::TileShape ts = dg::tile_shape(cfg);
+  const bool lds = fits_32bit(max_m, N, K);
+  const int cfg = lds ? (int)dg::kLds256x128 : (max_m <= 64 ? dg::kTile64x128 : dg::kTile128x128);
+  const dg::TileShape ts = lds ? dg::lds_tile_shape(cfg) : dg::tile_shape(cfg);
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
@@ -269,7 +270,8 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=%dx%d\n", (long long)G,
                  (long long)max_m, (long long)N, (long long)K, ts.bm, ts.bn);
-  const hipError_t e = dg::launch_gemm(dg::kMasked, cfg, p, (int)G, static_cast<hipStream_t>(stream));
+  const hipError_t e = lds ? dg::launch_gemm_lds(dg::kMasked, cfg, p, static_cast<hipStream_t>(stream))
+                           : dg::launch_gemm(dg::kMasked, cfg, p, (int)G, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -40,7 +40,7 @@ TileShape tile_shape(int cfg);
 enum LdsCfg { kLds256x128 = 0, kLds128x256 = 1 };
 TileShape lds_tile_shape(int cfg);
 
-// Enqueue the LDS-ring kernel (dense or contiguous, no split-K); operands are
+// Enqueue the LDS-ring kernel (dense, contiguous or masked; no split-K); operands are
 // addressed with 32-bit offsets, so (rows + 256) * K, (N + 256) * K and
 // rows * K / 32 must stay below 2^32.
 hipError_t launch_gemm_lds(int mode, int cfg, const GemmParams& p, hipStream_t stream);

@@ -1,6 +1,8 @@
 // Block-scaled FP8 GEMM for gfx950 with a 3-slot LDS ring fed by
-// buffer-to-LDS loads: the kernel for MFMA-bound dense and M-grouped
-// contiguous problems.
+// buffer-to-LDS loads: the kernel for large dense problems, the M-grouped
+// contiguous form, and the M-grouped masked form (one 256-row tile covers
+// an expert's whole capacity, so each expert's weights stream once; 16-row
+// MFMA tiles past masked_m are skipped).
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: for every 128-wide K block the fp8 partial product of
@@ -87,8 +89,18 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
   const int wm = wave / WGN;
   const int wn = wave % WGN;
 
-  int mt, nt;
-  grouped_mn(xcd_tile(blockIdx.x, p.m_tiles * p.n_tiles), p.m_tiles, p.n_tiles, GM, &mt, &nt);
+  int mt, nt, grp = 0;
+  if (MODE == kMasked) {
+    // (expert, m-tile, n-tile), n fastest: an expert's tiles are adjacent, so
+    // each XCD streams a few experts' weights and reuses their activations
+    const int t = xcd_tile(blockIdx.x, p.G * p.m_tiles * p.n_tiles);
+    const int per = p.m_tiles * p.n_tiles;
+    grp = t / per;
+    mt = (t - grp * per) / p.n_tiles;
+    nt = t - grp * per - mt * p.n_tiles;
+  } else {
+    grouped_mn(xcd_tile(blockIdx.x, p.m_tiles * p.n_tiles), p.m_tiles, p.n_tiles, GM, &mt, &nt);
+  }
 
   const int K = p.K;
   const int N = p.N;
@@ -97,10 +109,25 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
   const int rows = (int)p.rows;
   const int m0 = mt * BM;
   const int n0 = nt * BN;
+  const uint8_t* Ap = p.A;
+  const float* sfa = p.sfa;
   const uint8_t* Bp = p.B;
   const float* sfb = p.sfb;
-  const int row_limit = rows - m0 < BM ? rows - m0 : BM;
+  uint16_t* D = p.D;
+  int row_limit = rows - m0 < BM ? rows - m0 : BM;
   int expert = 0;
+
+  if (MODE == kMasked) {
+    int mm = p.index[grp];
+    mm = mm < 0 ? 0 : (mm > rows ? rows : mm);
+    if (m0 >= mm) return;  // whole tile past this expert's valid rows (uniform)
+    row_limit = mm - m0 < BM ? mm - m0 : BM;
+    Ap += (int64_t)grp * rows * K;
+    sfa += (int64_t)grp * KB * rows;
+    Bp += (int64_t)grp * N * K;
+    sfb += (int64_t)grp * NB * KB;
+    D += (int64_t)grp * rows * N;
+  }
 
   if (MODE == kContiguous) {
     // expert of this tile = largest valid index among its rows (computed by
@@ -121,9 +148,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     sfb += (int64_t)expert * NB * KB;
   }
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)rows * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ap, (uint32_t)rows * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp, (uint32_t)N * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (uint32_t)rows * (uint32_t)KB * 4u);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(sfa, (uint32_t)rows * (uint32_t)KB * 4u);
 
   // DMA sources: instruction i of this wave fills LDS rows 8*(i*8 + wave) + lane/8;
   // lane chunk (lane % 8) of row r holds K chunk (lane % 8) ^ (r % 8).  The
@@ -154,6 +181,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
   }
+
+  // 16-row MFMA tiles of this wave that hold rows to be stored (all four
+  // except in the last rows of a grouped problem); the others skip their MFMAs
+  int act = (row_limit - wm * 64 + 15) >> 4;
+  act = act < 0 ? 0 : (act > TM ? TM : act);
+  act = __builtin_amdgcn_readfirstlane(act);
 
   f32x4 u[TM][TN];
 #pragma unroll
@@ -225,8 +258,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     }                                                                                                      \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
-        u[i_][j_] *= r_[i_];                                                                               \
-        u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_[i_], bf_[j_], u[i_][j_], 0, 0, 0, 0, 0, 0); \
+        if (MODE != kMasked || i_ < act) {                                                                 \
+          u[i_][j_] *= r_[i_];                                                                             \
+          u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_[i_], bf_[j_], u[i_][j_], 0, 0, 0, 0, 0, 0); \
+        }                                                                                                  \
       }                                                                                                    \
     }                                                                                                      \
   } while (0)
@@ -254,7 +289,6 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
 #undef DG_SS
 
   // epilogue: lane holds column (lane & 15) and rows 4 * (lane >> 4) + v of each 16x16 tile
-  uint16_t* D = p.D;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -276,10 +310,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
 
 template <int WGM, int WGN>
 hipError_t launch_lds_cfg(int mode, const GemmParams& p, hipStream_t stream) {
-  const int64_t grid = (int64_t)p.m_tiles * p.n_tiles;
+  const int64_t grid = (int64_t)p.m_tiles * p.n_tiles * (mode == kMasked ? p.G : 1);
   if (grid <= 0) return hipSuccess;
   if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_lds_kernel<WGM, WGN, kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kMasked)
+    hipLaunchKernelGGL((fp8_gemm_lds_kernel<WGM, WGN, kMasked>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((fp8_gemm_lds_kernel<WGM, WGN, kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();
