@@ -36,6 +36,40 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 ROTATE_BYTES = 768 << 20  # per-shape rotation footprint (3x the 256 MB MALL)
 CPU_SAMPLE_ROWS = 2048  # rows per shape in the CPU-oracle baseline sample
 COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE /
+# WRITE_SIZE counters (calibrated against a plain copy) and recorded together with
+# a hash of the kernel's sources: reported only while those sources are unchanged.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_lds_kernel_dense_sweep.md")
+KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_lds.hip", "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
+                  "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/build.py")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter record, or None when the
+    record is missing, is for another kernel/workload, or predates the sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            fields = dict(l.strip()[2:].split(": ", 1) for l in f if l.startswith("- ") and ": " in l)
+    except OSError:
+        return None
+    if fields.get("kernel") != kernel or fields.get("workload") != workload:
+        return None
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def dense_work(M, N, K):
@@ -175,7 +209,10 @@ def run_dense(args, torch, dg, workloads):
         achieved = dom["bytes"] / dom["n"] / avg_us / 1e3
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4))
-    roof.update(traffic=None, kernel=dom_name, launches_per_step=dom["n"], avg_launch_us=round(avg_us, 2))
+    traffic = recorded_traffic(dom_name, args.workload) if not args.shapes else None
+    roof.update(traffic=traffic, kernel=dom_name, launches_per_step=dom["n"], avg_launch_us=round(avg_us, 2),
+                algorithmic_bytes_per_launch=round(dom["bytes"] / dom["n"]),
+                algorithmic_flops_per_launch=round(dom["flops"] / dom["n"]))
     return dict(ms_per_step=ms_per_step, wall_s=wall, step_flops=step_flops, per_shape=per_shape, roofline=roof,
                 shapes=[(p["M"], p["N"], p["K"]) for p in prepared])
 
@@ -282,7 +319,7 @@ def run_grouped(args, torch, dg, workloads):
     else:
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
-    kname = "fp8_gemm_lds_kernel<2,4,contiguous>" if args.workload == "contiguous" else "fp8_gemm_kernel<masked>"
+    kname = "fp8_gemm_lds_kernel<2,4,contiguous>" if args.workload == "contiguous" else "fp8_gemm_lds_kernel<4,2,masked>"
     roof.update(traffic=None, kernel=f"{kname} ({big['N']}x{big['K']})",
                 avg_launch_us=big["gemm_us"])
     name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
@@ -367,7 +404,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "dtype": "fp8_e4m3",
         "data": "synthetic (seeded DeepSeek-V3-shaped fp32 sources, quantised on device)",
         "config": config,
         "per_shape": r["per_shape"],

@@ -25,6 +25,8 @@ def _mutant(a_codes, sfa, b_codes, sfb, mistake):
     b = decode_e4m3(b_codes)
     M, K = a.shape
     N = b.shape[0]
+    if mistake == "b_transposed":  # B's bytes read as if stored [K, N]
+        b = b.reshape(K, N).T
     nb = sfb.shape[0]
     acc = np.zeros((M, N))
     blocks = range(K // 128 - 1) if mistake == "drop_block" else range(K // 128)
@@ -40,6 +42,8 @@ def _mutant(a_codes, sfa, b_codes, sfb, mistake):
         if mistake == "sign":
             p = -p if g == 1 else p
         acc += s * p
+    if mistake == "bf16_truncate":  # round toward zero through fp32 instead of RNE from fp64
+        return (acc.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     return bf16_rne_bits(acc)
 
 
@@ -64,3 +68,11 @@ def test_pin_rejects_wrong_alpha_group():
 
 def test_pin_rejects_sign_error():
     assert _brute_force_rejects("sign")
+
+
+def test_pin_rejects_transposed_operand():
+    assert _brute_force_rejects("b_transposed")
+
+
+def test_pin_rejects_truncating_epilogue():
+    assert _brute_force_rejects("bf16_truncate")
