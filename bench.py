@@ -10,10 +10,14 @@ seeded inputs (moe_grouped_matmul_amd.workloads).  One step = for each of the
 inference).  Every shape rotates over enough copies of its buffers that each
 call reads cold HBM (> 2x the 256 MB Infinity Cache per shape).
 
+Timing: every step is captured into a HIP graph (one per rotation index) and
+the timed region replays them back to back, so no host launch gaps enter the
+measurement; per-shape kernel times come from graphs of back-to-back launches
+over all rotating buffer sets, timed with HIP events on the launch stream.
+
 Output: one JSON line with the whole-step FP8 TFLOPS, per-shape GEMM TFLOPS,
-GB/s and fraction of the MI355X roofline, the dominant kernel's roofline
-(HIP events on the launch stream), and the CPU oracle timed on a bounded
-sample of the same workload.
+GB/s and fraction of the MI355X roofline, the dominant kernel's roofline, and
+the CPU oracle timed on a bounded sample of the same workload.
 
 Other workloads for profiling: --workload large | contiguous | masked | small.
 """
@@ -119,6 +123,31 @@ class Timer:
         return e
 
 
+def capture(torch, fn):
+    """Capture fn's launches into a HIP graph (replayed back to back on the GPU,
+    so the timed region holds no host launch gaps)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def time_graph(torch, timer, g, reps):
+    """Average milliseconds of one replay of g over reps replays (after one untimed)."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = timer.ev()
+    for _ in range(reps):
+        g.replay()
+    e1 = timer.ev()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+PER_SHAPE_LAUNCHES = 16  # minimum launches per per-shape timing graph (cycling over the rotating buffer sets)
+PER_SHAPE_REPS = 5       # timed replays of each per-shape graph
+
+
 def run_dense(args, torch, dg, workloads):
     dev = torch.device("cuda:0")
     shapes = workloads.CONFIGS["dense_sweep"] if args.workload == "sweep" else \
@@ -147,42 +176,54 @@ def run_dense(args, torch, dg, workloads):
                 sb=SB if i == 0 else SB.clone(),
                 d=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
         wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
-        ws = torch.empty(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
+        ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
         flops, nbytes = dense_work(M, N, K)
         prepared.append(dict(M=M, N=N, K=K, sets=sets, ws=ws, flops=flops, bytes=nbytes,
-                             kernel="fp8_gemm_lds_kernel<4,2,dense>" if M > 128 else
-                             "fp8_gemm_kernel<64,64,32,32,dense>+splitk_reduce"))
+                             kernel="fp8_gemm_lds_kernel<4,2,dense>" if M > 128 else "fp8_gemm_skinny_kernel"))
     torch.cuda.synchronize()
     timer = Timer(torch)
 
-    def step(i, record):
-        evs = []
+    def quant(p, i):
+        st = p["sets"][i % len(p["sets"])]
+        dg.dg_quant_1x128(st["a32"], st["a8"], st["sa"])
+
+    def gemm(p, i):
+        st = p["sets"][i % len(p["sets"])]
+        dg.dg_fp8_gemm_nt(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["ws"])
+
+    def step(i):
         for p in prepared:
-            st = p["sets"][i % len(p["sets"])]
-            e0 = timer.ev() if record else None
-            dg.dg_quant_1x128(st["a32"], st["a8"], st["sa"])
-            e1 = timer.ev() if record else None
-            dg.dg_fp8_gemm_nt(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["ws"])
-            e2 = timer.ev() if record else None
-            evs.append((e0, e1, e2))
-        return evs
+            quant(p, i)
+            gemm(p, i)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
+    torch.cuda.synchronize()
+    # one graph per rotation index: replay i runs the whole step on buffer set i of every shape
+    n_graphs = max(len(p["sets"]) for p in prepared)
+    graphs = [capture(torch, lambda i=i: step(i)) for i in range(n_graphs)]
+    graphs[0].replay()
     torch.cuda.synchronize()
     t_start = timer.ev()
     w0 = time.perf_counter()
-    all_evs = [step(args.warmup + i, True) for i in range(args.steps)]
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % n_graphs].replay()
     t_end = timer.ev()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    del graphs
 
+    # per-shape kernel times: graphs of back-to-back launches over the rotating sets
     per_shape = []
-    for j, p in enumerate(prepared):
-        q_ms = sum(all_evs[i][j][0].elapsed_time(all_evs[i][j][1]) for i in range(args.steps)) / args.steps
-        g_ms = sum(all_evs[i][j][1].elapsed_time(all_evs[i][j][2]) for i in range(args.steps)) / args.steps
+    for p in prepared:
+        launches = max(PER_SHAPE_LAUNCHES, len(p["sets"]))  # every set once per replay: cold HBM
+        gq = capture(torch, lambda p=p: [quant(p, i) for i in range(launches)])
+        gg = capture(torch, lambda p=p: [gemm(p, i) for i in range(launches)])
+        q_ms = time_graph(torch, timer, gq, PER_SHAPE_REPS) / launches
+        g_ms = time_graph(torch, timer, gg, PER_SHAPE_REPS) / launches
+        del gq, gg
         t_us = g_ms * 1e3
         rt = roof_time_us(p["flops"], p["bytes"])
         per_shape.append(dict(M=p["M"], N=p["N"], K=p["K"], gemm_us=round(t_us, 2), quant_us=round(q_ms * 1e3, 2),
@@ -279,33 +320,40 @@ def run_grouped(args, torch, dg, workloads):
     torch.cuda.synchronize()
     timer = Timer(torch)
 
-    def step(i, record):
-        evs = []
+    def gemm(p, i):
+        st = p["sets"][i % len(p["sets"])]
+        if args.workload == "contiguous":
+            dg.dg_m_grouped_fp8_gemm_nt_contiguous(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"])
+        else:
+            dg.dg_m_grouped_fp8_gemm_nt_masked(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"],
+                                               expected_m=128)
+
+    def step(i):
         for p in prepared:
-            st = p["sets"][i % len(p["sets"])]
-            e0 = timer.ev() if record else None
-            if args.workload == "contiguous":
-                dg.dg_m_grouped_fp8_gemm_nt_contiguous(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"])
-            else:
-                dg.dg_m_grouped_fp8_gemm_nt_masked(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"],
-                                                   expected_m=128)
-            e1 = timer.ev() if record else None
-            evs.append((e0, e1))
-        return evs
+            gemm(p, i)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
+    torch.cuda.synchronize()
+    n_graphs = max(len(p["sets"]) for p in prepared)
+    graphs = [capture(torch, lambda i=i: step(i)) for i in range(n_graphs)]
+    graphs[0].replay()
     torch.cuda.synchronize()
     t_start = timer.ev()
     w0 = time.perf_counter()
-    all_evs = [step(args.warmup + i, True) for i in range(args.steps)]
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % n_graphs].replay()
     t_end = timer.ev()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    del graphs
     per_shape = []
-    for j, p in enumerate(prepared):
-        t_us = sum(all_evs[i][j][0].elapsed_time(all_evs[i][j][1]) for i in range(args.steps)) / args.steps * 1e3
+    for p in prepared:
+        launches = max(len(p["sets"]), 4)  # every set once per replay: cold HBM
+        gg = capture(torch, lambda p=p: [gemm(p, i) for i in range(launches)])
+        t_us = time_graph(torch, timer, gg, PER_SHAPE_REPS) / launches * 1e3
+        del gg
         rt = roof_time_us(p["flops"], p["bytes"])
         mf = p["flops"] / (PEAK_FP8_TFLOPS * 1e12) >= p["bytes"] / (PEAK_HBM_GBS * 1e9)
         per_shape.append(dict(G=p["G"], N=p["N"], K=p["K"], rows=p["rows"], valid_rows=int(sum(max(c, 0) for c in p["counts"])),

@@ -69,12 +69,17 @@ enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2 };
  *   A   [M,K]  e4m3, row-major          sfa [K/128][M] fp32
  *   B   [N,K]  e4m3, row-major          sfb [ceil(N/128)][K/128] fp32
  *   D   [M,N]  bf16, row-major (written)
- * workspace: optional fp32 scratch for splitting K across workgroups when the
+ * workspace: optional scratch for splitting K across workgroups when the
  *   output has too few tiles to fill the GPU (small M).  Pass NULL/0 to run
- *   without it (same result, possibly slower).  Required size for the full
- *   split is dg_get_workspace_size(DG_OP_GEMM_NT, M, N, K, 1); a smaller
- *   buffer limits the split.  Calls that share one workspace must be ordered
- *   on one stream.
+ *   without it (possibly slower; the split changes only the fp32 summation
+ *   order, so results agree within rounding, and each configuration is
+ *   deterministic).  Required size for the full split is
+ *   dg_get_workspace_size(DG_OP_GEMM_NT, M, N, K, 1); a smaller buffer limits
+ *   the split.  The workspace MUST be zero-filled before its first use (e.g.
+ *   hipMemset once after allocation): for M <= 128 it holds per-tile
+ *   completion counters besides the fp32 partials, and every call leaves
+ *   those counters at zero again, so a workspace stays reusable without
+ *   clearing.  Calls that share one workspace must be ordered on one stream.
  */
 int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                    uint16_t* D, int64_t M, int64_t N, int64_t K, void* workspace,

@@ -94,8 +94,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Dense split-K plan: enough work items to cover the CUs twice when the
 // output alone has too few tiles.  Splits never exceed the K blocks.
 struct DensePlan {
-  bool lds;  // LDS-ring kernel (gemm_lds.hip)
-  int cfg;
+  bool lds;     // LDS-ring kernel (gemm_lds.hip)
+  bool skinny;  // skinny kernel (gemm_skinny.hip), M <= 128
+  int cfg;      // lds / v1 tile configuration, or skinny rows per tile (64 | 128)
+  int wn;       // skinny: columns per wave (16 | 32)
   int m_tiles;
   int n_tiles;
   int splits;
@@ -108,9 +110,51 @@ bool fits_32bit(int64_t rows, int64_t N, int64_t K) {
   return (rows + 256) * K < lim && (N + 256) * K < lim && rows * (K / 128) * 4 < lim;
 }
 
+// Skinny kernel (one workgroup per CU): column width and K split chosen so
+// the workgroups fill the CUs in whole rounds.  Without a split the wider
+// tile wins ties; with one, 16-column waves give the most tiles, and the split
+// is at most K / (16 bm) (the fp32 partials then stay below a quarter of the
+// weight bytes), at most 16, and only as large as the workspace holds.
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   DensePlan pl;
   pl.lds = false;
+  pl.skinny = false;
+  pl.wn = 0;
+  const int KB = (int)(K / 128);
+  if (M <= 128 && fits_32bit(M, N, K)) {
+    pl.skinny = true;
+    // 64 < M <= 128: one 128-row tile (weights read once) when the columns
+    // alone nearly fill the CUs; otherwise two 64-row tiles, whose split-K
+    // partials are half as large per tile
+    pl.cfg = (M <= 64 || ceil_div(N, 64) < cus / 2) ? 64 : 128;
+    pl.m_tiles = (int)ceil_div(M, pl.cfg);
+    const int64_t t16 = pl.m_tiles * ceil_div(N, 64);
+    const int64_t t32 = pl.m_tiles * ceil_div(N, 128);
+    auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
+    pl.wn = (t16 >= cus && fill(t32) >= fill(t16)) ? 32 : 16;
+    pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
+    const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
+    int splits = 1;
+    if (tiles < cus) {
+      splits = (int)(cus / tiles);
+      const int cap = (int)(K / (16 * pl.cfg));  // partials (splits * bm * 4 B per column) <= K / 4
+      if (splits > cap) splits = cap;
+      if (splits > 16) splits = 16;
+      while (splits > 1 && (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes ||
+                            dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) >
+                                ((size_t)1 << 31)))
+        --splits;
+      if (splits < 2) splits = 1;
+    }
+    // whole ring cycles per split where that does not cost a split
+    const int depth = dg::skinny_depth(pl.cfg, pl.wn);
+    int kbs = (int)ceil_div(KB, splits);
+    const int kbs_r = (int)ceil_div(kbs, depth) * depth;
+    if (ceil_div(KB, kbs_r) == splits || kbs_r - kbs < depth / 2) kbs = kbs_r;
+    pl.kb_per_split = kbs;
+    pl.splits = (int)ceil_div(KB, pl.kb_per_split);
+    return pl;
+  }
   if (M > 128 && fits_32bit(M, N, K)) {
     pl.lds = true;
     pl.cfg = dg::kLds256x128;
@@ -124,7 +168,6 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) 
   const dg::TileShape ts = dg::tile_shape(pl.cfg);
   pl.m_tiles = (int)ceil_div(M, ts.bm);
   pl.n_tiles = (int)ceil_div(N, ts.bn);
-  const int KB = (int)(K / 128);
   const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
   int splits = 1;
   if (tiles < cus) {
@@ -175,13 +218,18 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   p.splits = pl.splits;
   p.kb_per_split = pl.kb_per_split;
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
-                 (long long)M, (long long)N, (long long)K,
-                 pl.lds ? dg::lds_tile_shape(pl.cfg).bm : dg::tile_shape(pl.cfg).bm,
-                 pl.lds ? dg::lds_tile_shape(pl.cfg).bn : dg::tile_shape(pl.cfg).bn,
+    std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=%s tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
+                 (long long)M, (long long)N, (long long)K, pl.skinny ? "skinny" : (pl.lds ? "lds" : "v1"),
+                 pl.skinny ? pl.cfg : (pl.lds ? dg::lds_tile_shape(pl.cfg).bm : dg::tile_shape(pl.cfg).bm),
+                 pl.skinny ? 4 * pl.wn : (pl.lds ? dg::lds_tile_shape(pl.cfg).bn : dg::tile_shape(pl.cfg).bn),
                  pl.m_tiles, pl.n_tiles, pl.splits);
-  const hipError_t e = pl.lds ? dg::launch_gemm_lds(dg::kDense, pl.cfg, p, static_cast<hipStream_t>(stream))
-                              : dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
+  hipError_t e;
+  if (pl.skinny)
+    e = dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream));
+  else if (pl.lds)
+    e = dg::launch_gemm_lds(dg::kDense, pl.cfg, p, static_cast<hipStream_t>(stream));
+  else
+    e = dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -324,6 +372,8 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   if (cus <= 0) cus = 256;
   const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1);
   if (pl.splits <= 1) return 0;
+  if (pl.skinny)
+    return (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, pl.splits) + 15) / 16 * 16;
   return (size_t)pl.splits * (size_t)rows * (size_t)N * sizeof(float);
 }
 

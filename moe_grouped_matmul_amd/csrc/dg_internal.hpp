@@ -45,6 +45,19 @@ TileShape lds_tile_shape(int cfg);
 // rows * K / 32 must stay below 2^32.
 hipError_t launch_gemm_lds(int mode, int cfg, const GemmParams& p, hipStream_t stream);
 
+// Enqueue the skinny dense kernel (gemm_skinny.hip, M <= 128, bm-row tiles
+// with bm in {64, 128}, wn in {16, 32} columns per wave, 4 waves):
+// p.m_tiles = ceil(M / bm), p.n_tiles = ceil(N / (4 wn)), p.splits K splits of
+// p.kb_per_split blocks.  With p.splits > 1, p.ws must hold
+// skinny_workspace_bytes(...) bytes: fp32 partials followed by one uint32
+// counter per tile that must be zero on entry (each call leaves them zero).
+size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int splits);
+hipError_t launch_gemm_skinny(int bm, int wn, const GemmParams& p, hipStream_t stream);
+// K blocks in flight per wave (ring depth; LDS per slot is (bm + 4 wn) * 128 B
+// plus 1 KB, one workgroup per CU); a split's block count is padded to a
+// multiple of it (padding blocks read as zeros), so splits should be multiples
+constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? (wn == 16 ? 8 : 4) : (wn == 16 ? 6 : 4); }
+
 // Enqueue the GEMM kernel (and the split-K reduction when p.splits > 1).
 hipError_t launch_gemm(int mode, int cfg, const GemmParams& p, int groups, hipStream_t stream);
 

@@ -148,7 +148,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     sfb += (int64_t)expert * NB * KB;
   }
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ap, (uint32_t)rows * (uint32_t)K);
+  // masked: A rows past masked_m lie outside the buffer range, so their loads
+  // return zeros without touching memory
+  const uint32_t a_rows = MODE == kMasked ? (uint32_t)(m0 + row_limit) : (uint32_t)rows;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ap, a_rows * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp, (uint32_t)N * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(sfa, (uint32_t)rows * (uint32_t)KB * 4u);
 

@@ -85,7 +85,7 @@ def test_dense_full_size(shape):
     qb, sb = _gpu_quant_b(b32)
     D = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
     n = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
-    ws = torch.empty(max(n // 4, 1), dtype=torch.float32, device=DEV) if n else None
+    ws = torch.zeros(max(n // 4, 1), dtype=torch.float32, device=DEV) if n else None
     dg.dg_fp8_gemm_nt(qa, sa, qb, sb, D, ws)
     torch.cuda.synchronize()
     rows = _sample_rows(M, 24, np.random.default_rng(seed))

@@ -38,7 +38,7 @@ def _sentinel(*shape):
 
 def _ws(M, N, K):
     n = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
-    return torch.empty(max(n // 4, 1), dtype=torch.float32, device=DEV) if n else None
+    return torch.zeros(max(n // 4, 1), dtype=torch.float32, device=DEV) if n else None
 
 
 def _gpu_dense(qa, sa, qb, sb, M, N, K, workspace=True):
@@ -148,6 +148,33 @@ def test_dense_deterministic_and_nan_rows_contained():
     assert np.array_equal(d1, d2)
     ref = oracle.gemm_nt(qa, sa, qb, sb)
     assert_close(d1, ref, "dense with a NaN row")
+
+
+# skinny kernel (M <= 128): one or many K splits, ragged M and N, splits whose
+# block count is not a multiple of the ring depth, and one workspace reused
+# across calls (its split counters must come back to zero after every call)
+SKINNY = [(1, 2112, 7168), (17, 144, 1024), (64, 2112, 7168), (100, 272, 4096), (128, 2112, 7168),
+          (64, 4096, 640), (128, 32768, 512), (33, 24576, 1536), (64, 7168, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY)
+def test_dense_skinny_matches_oracle_with_reused_workspace(M, N, K):
+    a32, b32 = workloads.dense(M, N, K, seed=M + 3 * N + K)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    ws = _ws(M, N, K)
+    outs = []
+    for _ in range(3):
+        D = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
+        dg.dg_fp8_gemm_nt(_t(qa), _t(sa), _t(qb), _t(sb), D, ws)
+        outs.append(D)
+    torch.cuda.synchronize()
+    got = _np(outs[0]).view(np.uint16)
+    for o in outs[1:]:
+        assert np.array_equal(_np(o).view(np.uint16), got), "results differ between calls on one workspace"
+    # a counter left non-zero by one call would leave tiles of the next call
+    # unreduced (still -1), so equal results across calls show they were reset
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"dense {M}x{N}x{K}")
 
 
 # ---------------------------------------------------------------- contiguous
