@@ -26,7 +26,10 @@
 //     distinct 16-byte bank groups (conflict-free at 128 B/clk);
 //   * a lane's MFMA operand is row (lane % 16), K chunks q and q + 4
 //     (q = lane / 16) of the 128-byte block -- the same K permutation for A
-//     and B, so every dot product is unchanged;
+//     and B, so every dot product is unchanged.  B is the row operand and A
+//     the column operand; B rows enter LDS in a permuted order so that each
+//     lane ends with 16 consecutive output columns of one row (32-byte
+//     stores) and one row scale per row tile;
 //   * promotion with a rescaled accumulator: the kernel keeps u = acc / s_k,
 //     s_k = alpha[row, k] * beta[k] for the current block.  Entering block k
 //     it multiplies u by s_{k-1} / s_k (one fp32 multiply per element, the
@@ -162,7 +165,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
   // accumulator rows / columns that are never stored.
   const int dma_chunk = ((lane & 7) ^ ((lane >> 3) & 7)) << 4;
   const uint32_t a_src = (uint32_t)(m0 + 8 * wave + (lane >> 3)) * (uint32_t)K + (uint32_t)dma_chunk;
-  const uint32_t b_src = (uint32_t)(n0 + 8 * wave + (lane >> 3)) * (uint32_t)K + (uint32_t)dma_chunk;
+  // B rows enter LDS permuted: row 16 j + i of a wave's 64-row block holds
+  // weight row (i / 4) * 16 + 4 j + i % 4 of it, so that in the MFMA output
+  // (B as row operand) lane l holds 16 consecutive columns q * 16 + [0, 16)
+  // of one output row.  Instruction i of this wave fills LDS rows
+  // 64 i + 8 wave + lane / 8, i.e. local row 8 wave + lane / 8 of block i.
+  const int b_loc = 8 * wave + (lane >> 3);
+  const int b_perm = ((b_loc & 15) >> 2) * 16 + 4 * (b_loc >> 4) + (b_loc & 3);
+  const uint32_t b_src = (uint32_t)(n0 + b_perm) * (uint32_t)K + (uint32_t)dma_chunk;
   const uint32_t dma_stride = 64u * (uint32_t)K;
   const uint32_t s_src = (uint32_t)(m0 + wave * 64 + lane) * 4u;
 
@@ -196,9 +206,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) u[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 s_prev[TM];
+  // scale of the current block for this lane's output row of each row tile
+  float s_prev[TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) s_prev[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < TM; ++i) s_prev[i] = 0.f;
 
 #define DG_SA(st) ((st) == 0 ? sA0 : ((st) == 1 ? sA1 : sA2))
 #define DG_SB(st) ((st) == 0 ? sB0 : ((st) == 1 ? sB1 : sB2))
@@ -243,27 +254,27 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     const uint8_t* bs_ = DG_SB(st_) + b_row0;                                                              \
     i32x8 af_[TM];                                                                                         \
     i32x8 bf_[TN];                                                                                         \
-    f32x4 al_[TM];                                                                                         \
+    float al_[TM];                                                                                         \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
       DG_FRAG(af_[i_], as_, i_ * 2048);                                                                    \
-      al_[i_] = *reinterpret_cast<const f32x4*>(DG_SS(st_) + wm * 64 + i_ * 16 + q * 4);                  \
+      al_[i_] = DG_SS(st_)[wm * 64 + i_ * 16 + (lane & 15)];                                               \
     }                                                                                                      \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) DG_FRAG(bf_[j_], bs_, j_ * 2048);                   \
     wait_vmcnt<L_BLOCK>();                                                                                 \
     wait_lgkmcnt0(); /* own reads of slot k done before anyone may refill it */                           \
     __builtin_amdgcn_s_barrier();                                                                          \
     DG_ISSUE((st_), (k_) + 3 < KB ? (k_) + 3 : KB - 1);                                                   \
-    f32x4 r_[TM];                                                                                          \
+    float r_[TM];                                                                                          \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
-      const f32x4 sc_ = al_[i_] * beta_;                                                                   \
-      _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) r_[i_][v_] = s_prev[i_][v_] * __builtin_amdgcn_rcpf(sc_[v_]); \
+      const float sc_ = al_[i_] * beta_;                                                                   \
+      r_[i_] = s_prev[i_] * __builtin_amdgcn_rcpf(sc_);                                                    \
       s_prev[i_] = sc_;                                                                                    \
     }                                                                                                      \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         if (MODE != kMasked || i_ < act) {                                                                 \
           u[i_][j_] *= r_[i_];                                                                             \
-          u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af_[i_], bf_[j_], u[i_][j_], 0, 0, 0, 0, 0, 0); \
+          u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_], af_[i_], u[i_][j_], 0, 0, 0, 0, 0, 0); \
         }                                                                                                  \
       }                                                                                                    \
     }                                                                                                      \
@@ -291,22 +302,28 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
 #undef DG_SB
 #undef DG_SS
 
-  // epilogue: lane holds column (lane & 15) and rows 4 * (lane >> 4) + v of each 16x16 tile
+  // epilogue: for row tile i, lane l holds output row wm*64 + 16 i + l % 16
+  // and its 16 consecutive columns wn*64 + q*16 + 4 j + v: two 16-byte
+  // stores.  N is a multiple of 16, so a lane's columns are all inside N or
+  // all outside.
+  const int gc0 = n0 + wn * 64 + q * 16;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int r = wm * 64 + i * 16 + (lane & 15);
+    if (r >= row_limit || gc0 >= N) continue;
+    const int64_t gr = (int64_t)m0 + r;
+    if (MODE == kContiguous && p.index[gr] != expert) continue;
+    uint32_t w[8];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = wm * 64 + i * 16 + q * 4 + v;
-      if (r >= row_limit) continue;
-      const int64_t gr = (int64_t)m0 + r;
-      if (MODE == kContiguous && p.index[gr] != expert) continue;
-      uint16_t* drow = D + gr * N;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int gc = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (gc < N) drow[gc] = f32_to_bf16_rne(u[i][j][v] * s_prev[i][v]);
-      }
+    for (int j = 0; j < TN; ++j) {
+      w[2 * j] = (uint32_t)f32_to_bf16_rne(u[i][j][0] * s_prev[i]) |
+                 ((uint32_t)f32_to_bf16_rne(u[i][j][1] * s_prev[i]) << 16);
+      w[2 * j + 1] = (uint32_t)f32_to_bf16_rne(u[i][j][2] * s_prev[i]) |
+                     ((uint32_t)f32_to_bf16_rne(u[i][j][3] * s_prev[i]) << 16);
     }
+    uint4* dst = reinterpret_cast<uint4*>(D + gr * N + gc0);
+    dst[0] = uint4{w[0], w[1], w[2], w[3]};
+    dst[1] = uint4{w[4], w[5], w[6], w[7]};
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
