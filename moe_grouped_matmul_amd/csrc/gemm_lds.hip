@@ -30,17 +30,12 @@
 //     the column operand; B rows enter LDS in a permuted order so that each
 //     lane ends with 16 consecutive output columns of one row (32-byte
 //     stores) and one row scale per row tile;
-//   * promotion with a rescaled accumulator: the kernel keeps u = acc / s_k,
-//     s_k = alpha[row, k] * beta[k] for the current block.  Entering block k
-//     it multiplies u by s_{k-1} / s_k (one fp32 multiply per element, the
-//     same VALU count as a promotion FMA) and the MFMA then adds the block's
-//     fp8 partial straight into u (C = D = u).  Every 128-K partial enters
-//     the fp32 sum exactly once with its own alpha * beta; the epilogue
-//     returns u * s_last.  This needs no partial-product registers and no
-//     MFMA -> VALU round trip.  It differs from one FMA per partial only in
-//     rounding (a few fp32 ulps per block) and assumes the running sum
-//     divided by the current block's scale stays inside the fp32 range
-//     (true unless a 128-K group's amax is below ~1e-30 after large ones);
+//   * promotion: each 16x16x128 MFMA writes a fresh fp32 partial of one
+//     128-K block, and one FMA per element adds it into the fp32
+//     accumulator with that block's alpha[row] * beta (exact for any scale,
+//     zero included; measured as fast here as folding the scales into a
+//     rescaled accumulator, since the other wave of the SIMD fills the
+//     MFMA -> FMA latency);
 //   * tiles are mapped so each XCD runs a contiguous, m-grouped range
 //     (operand reuse in that XCD's L2).
 
@@ -201,15 +196,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
   act = act < 0 ? 0 : (act > TM ? TM : act);
   act = __builtin_amdgcn_readfirstlane(act);
 
-  f32x4 u[TM][TN];
+  f32x4 u[TM][TN];  // fp32 accumulators
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) u[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // scale of the current block for this lane's output row of each row tile
-  float s_prev[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) s_prev[i] = 0.f;
 
 #define DG_SA(st) ((st) == 0 ? sA0 : ((st) == 1 ? sA1 : sA2))
 #define DG_SB(st) ((st) == 0 ? sB0 : ((st) == 1 ? sB1 : sB2))
@@ -264,17 +255,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     wait_lgkmcnt0(); /* own reads of slot k done before anyone may refill it */                           \
     __builtin_amdgcn_s_barrier();                                                                          \
     DG_ISSUE((st_), (k_) + 3 < KB ? (k_) + 3 : KB - 1);                                                   \
-    float r_[TM];                                                                                          \
-    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
-      const float sc_ = al_[i_] * beta_;                                                                   \
-      r_[i_] = s_prev[i_] * __builtin_amdgcn_rcpf(sc_);                                                    \
-      s_prev[i_] = sc_;                                                                                    \
-    }                                                                                                      \
+    float sc_[TM];                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) sc_[i_] = al_[i_] * beta_;                           \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         if (MODE != kMasked || i_ < act) {                                                                 \
-          u[i_][j_] *= r_[i_];                                                                             \
-          u[i_][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_], af_[i_], u[i_][j_], 0, 0, 0, 0, 0, 0); \
+          const f32x4 t_ = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) u[i_][j_][v_] = __builtin_fmaf(t_[v_], sc_[i_], u[i_][j_][v_]); \
         }                                                                                                  \
       }                                                                                                    \
     }                                                                                                      \
@@ -316,10 +303,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     uint32_t w[8];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      w[2 * j] = (uint32_t)f32_to_bf16_rne(u[i][j][0] * s_prev[i]) |
-                 ((uint32_t)f32_to_bf16_rne(u[i][j][1] * s_prev[i]) << 16);
-      w[2 * j + 1] = (uint32_t)f32_to_bf16_rne(u[i][j][2] * s_prev[i]) |
-                     ((uint32_t)f32_to_bf16_rne(u[i][j][3] * s_prev[i]) << 16);
+      w[2 * j] = (uint32_t)f32_to_bf16_rne(u[i][j][0]) |
+                 ((uint32_t)f32_to_bf16_rne(u[i][j][1]) << 16);
+      w[2 * j + 1] = (uint32_t)f32_to_bf16_rne(u[i][j][2]) |
+                     ((uint32_t)f32_to_bf16_rne(u[i][j][3]) << 16);
     }
     uint4* dst = reinterpret_cast<uint4*>(D + gr * N + gc0);
     dst[0] = uint4{w[0], w[1], w[2], w[3]};

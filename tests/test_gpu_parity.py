@@ -177,6 +177,30 @@ def test_dense_skinny_matches_oracle_with_reused_workspace(M, N, K):
     assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"dense {M}x{N}x{K}")
 
 
+# zero scales (an all-zero group quantised as amax / 448 gives alpha = 0, a
+# zero weight block gives beta = 0): such blocks contribute exactly nothing,
+# on the skinny (M <= 128) and the LDS-ring (M > 128) paths, including a zero
+# scale in the first and in the last K block of a row
+@pytest.mark.parametrize("M,N,K", [(64, 272, 1024), (300, 272, 1024), (128, 2112, 7168), (512, 384, 640)])
+def test_dense_zero_scales_add_nothing(M, N, K):
+    a32, b32 = workloads.dense(M, N, K, seed=M + N)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    rng = np.random.default_rng(M)
+    KB = K // 128
+    sa[rng.random(sa.shape) < 0.05] = 0.0
+    sa[0, 1] = 0.0
+    sa[KB - 1, 2] = 0.0
+    sa[:, 3] = 0.0  # a row with every scale zero
+    sb[0, KB - 1] = 0.0
+    sb[-1, 0] = 0.0
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    for ws in (True, False):
+        got = _gpu_dense(qa, sa, qb, sb, M, N, K, ws)
+        assert not np.isnan(oracle.bf16_bits_to_f64(got)).any()
+        assert_close(got, ref, f"dense {M}x{N}x{K} with zero scales")
+
+
 # ---------------------------------------------------------------- contiguous
 
 def _contig_small(counts, G, N, K, seed):
