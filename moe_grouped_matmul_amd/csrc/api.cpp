@@ -94,6 +94,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Dense split-K plan: enough work items to cover the CUs twice when the
 // output alone has too few tiles.  Splits never exceed the K blocks.
 struct DensePlan {
+  bool persist;  // persistent kernel (gemm_persist.hip), M > 128
+  int grid;      // persistent: workgroups
+  int dp_tiles, sk_tiles, sk_pieces, sk_kb;
   bool lds;     // LDS-ring kernel (gemm_lds.hip)
   bool skinny;  // skinny kernel (gemm_skinny.hip), M <= 128
   int cfg;      // lds / v1 tile configuration, or skinny rows per tile (64 | 128)
@@ -110,6 +113,51 @@ bool fits_32bit(int64_t rows, int64_t N, int64_t K) {
   return (rows + 256) * K < lim && (N + 256) * K < lim && rows * (K / 128) * 4 < lim;
 }
 
+// The persistent kernel addresses A, B, alpha and D of all groups with 32-bit
+// buffer offsets and uses offsets from 0xFFFFFF00 up for lanes outside a tile.
+bool fits_persistent(int64_t groups, int64_t rows, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
+  return groups * (rows + 256) * K < lim && groups * (N + 256) * K < lim &&
+         groups * (rows + 256) * (K / 128) * 4 < lim && groups * rows * N * 2 < lim;
+}
+
+// Persistent dense schedule over 256x128 tiles, one workgroup per CU: whole
+// rounds of tiles; a partial last round is split along K into P <= 4 pieces
+// run by the workgroups it would leave idle (when the workspace holds the
+// partials), so every workgroup ends at about the same time.
+void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+  const int KB = (int)(K / 128);
+  const int64_t T = ceil_div(M, 256) * ceil_div(N, 128);
+  pl.persist = true;
+  pl.cfg = dg::kLds256x128;
+  pl.m_tiles = (int)ceil_div(M, 256);
+  pl.n_tiles = (int)ceil_div(N, 128);
+  pl.splits = 1;
+  pl.kb_per_split = KB;
+  pl.dp_tiles = (int)T;
+  pl.sk_tiles = 0;
+  pl.sk_pieces = 1;
+  pl.sk_kb = KB;
+  pl.grid = (int)(T < cus ? T : cus);
+  const int64_t rem = T < cus ? T : T % cus;
+  if (rem == 0) return;
+  int P = (int)(cus / rem);
+  if (P > 4) P = 4;
+  if (P > KB) P = KB;
+  if (P < 2) return;
+  const int kbs = (int)ceil_div(KB, P);
+  P = (int)ceil_div(KB, kbs);  // every piece non-empty
+  if (P < 2 || dg::persistent_workspace_bytes((int)rem, P) > ws_bytes ||
+      dg::persistent_workspace_bytes((int)rem, P) > (size_t)0xFFFFFF00 - 4096)
+    return;
+  pl.dp_tiles = (int)(T - rem);
+  pl.sk_tiles = (int)rem;
+  pl.sk_pieces = P;
+  pl.sk_kb = kbs;
+  const int64_t g = T < cus ? rem * P : cus;
+  pl.grid = (int)g;
+}
+
 // Skinny kernel (one workgroup per CU): column width and K split chosen so
 // the workgroups fill the CUs in whole rounds.  Without a split the wider
 // tile wins ties; with one, 16-column waves give the most tiles, and the split
@@ -117,6 +165,11 @@ bool fits_32bit(int64_t rows, int64_t N, int64_t K) {
 // weight bytes), at most 16, and only as large as the workspace holds.
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   DensePlan pl;
+  pl.persist = false;
+  pl.grid = 0;
+  pl.dp_tiles = pl.sk_tiles = 0;
+  pl.sk_pieces = 1;
+  pl.sk_kb = 0;
   pl.lds = false;
   pl.skinny = false;
   pl.wn = 0;
@@ -153,6 +206,10 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) 
     if (ceil_div(KB, kbs_r) == splits || kbs_r - kbs < depth / 2) kbs = kbs_r;
     pl.kb_per_split = kbs;
     pl.splits = (int)ceil_div(KB, pl.kb_per_split);
+    return pl;
+  }
+  if (M > 128 && fits_persistent(1, M, N, K)) {
+    plan_persistent(pl, M, N, K, cus, ws_bytes);
     return pl;
   }
   if (M > 128 && fits_32bit(M, N, K)) {
@@ -217,14 +274,25 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   p.n_tiles = pl.n_tiles;
   p.splits = pl.splits;
   p.kb_per_split = pl.kb_per_split;
-  if (std::getenv("DG_PRINT_CONFIGS"))
+  p.dp_tiles = pl.dp_tiles;
+  p.sk_tiles = pl.sk_tiles;
+  p.sk_pieces = pl.sk_pieces;
+  p.sk_kb = pl.sk_kb;
+  if (std::getenv("DG_PRINT_CONFIGS") && pl.persist)
+    std::fprintf(stderr,
+                 "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=persistent grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                 (long long)M, (long long)N, (long long)K, pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
+                 pl.sk_pieces, pl.sk_kb);
+  else if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=%s tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
                  (long long)M, (long long)N, (long long)K, pl.skinny ? "skinny" : (pl.lds ? "lds" : "v1"),
                  pl.skinny ? pl.cfg : (pl.lds ? dg::lds_tile_shape(pl.cfg).bm : dg::tile_shape(pl.cfg).bm),
                  pl.skinny ? 4 * pl.wn : (pl.lds ? dg::lds_tile_shape(pl.cfg).bn : dg::tile_shape(pl.cfg).bn),
                  pl.m_tiles, pl.n_tiles, pl.splits);
   hipError_t e;
-  if (pl.skinny)
+  if (pl.persist)
+    e = dg::launch_gemm_persistent(dg::kDense, pl.grid, p, static_cast<hipStream_t>(stream));
+  else if (pl.skinny)
     e = dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream));
   else if (pl.lds)
     e = dg::launch_gemm_lds(dg::kDense, pl.cfg, p, static_cast<hipStream_t>(stream));
@@ -297,7 +365,9 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
   (void)expected_m;
-  const bool lds = fits_32bit(max_m, N, K);
+  // persistent kernel with a device-side task list over the active tiles
+  const bool persist = G <= 1024 && fits_persistent(G, max_m, N, K);
+  const bool lds = persist || fits_32bit(max_m, N, K);
   const int cfg = lds ? (int)dg::kLds256x128 : (max_m <= 64 ? dg::kTile64x128 : dg::kTile128x128);
   const dg::TileShape ts = lds ? dg::lds_tile_shape(cfg) : dg::tile_shape(cfg);
   dg::GemmParams p{};
@@ -316,10 +386,18 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   p.splits = 1;
   p.kb_per_split = (int)(K / 128);
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=%dx%d\n", (long long)G,
-                 (long long)max_m, (long long)N, (long long)K, ts.bm, ts.bn);
-  const hipError_t e = lds ? dg::launch_gemm_lds(dg::kMasked, cfg, p, static_cast<hipStream_t>(stream))
-                           : dg::launch_gemm(dg::kMasked, cfg, p, (int)G, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=%dx%d kernel=%s\n", (long long)G,
+                 (long long)max_m, (long long)N, (long long)K, ts.bm, ts.bn, persist ? "persistent" : "grid");
+  hipError_t e;
+  if (persist) {
+    const int64_t tiles = G * p.m_tiles * p.n_tiles;
+    e = dg::launch_gemm_persistent(dg::kMasked, (int)(tiles < cus ? tiles : effective_cus(cus)), p,
+                                   static_cast<hipStream_t>(stream));
+  } else if (lds) {
+    e = dg::launch_gemm_lds(dg::kMasked, cfg, p, static_cast<hipStream_t>(stream));
+  } else {
+    e = dg::launch_gemm(dg::kMasked, cfg, p, (int)G, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -371,6 +449,7 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   (void)hipGetLastError();
   if (cus <= 0) cus = 256;
   const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1);
+  if (pl.persist) return (dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces) + 15) / 16 * 16;
   if (pl.splits <= 1) return 0;
   if (pl.skinny)
     return (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, pl.splits) + 15) / 16 * 16;

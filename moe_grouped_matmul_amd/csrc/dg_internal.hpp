@@ -23,6 +23,13 @@ struct GemmParams {
   int n_tiles;
   int splits;
   int kb_per_split;
+  // persistent kernel (gemm_persist.hip): tiles run whole (tile ids
+  // [0, dp_tiles)), and tail tiles [dp_tiles, dp_tiles + sk_tiles) each split
+  // into sk_pieces pieces of sk_kb K blocks (dense only)
+  int dp_tiles;
+  int sk_tiles;
+  int sk_pieces;
+  int sk_kb;
 };
 
 enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
@@ -57,6 +64,14 @@ hipError_t launch_gemm_skinny(int bm, int wn, const GemmParams& p, hipStream_t s
 // plus 1 KB, one workgroup per CU); a split's block count is padded to a
 // multiple of it (padding blocks read as zeros), so splits should be multiples
 constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? (wn == 16 ? 8 : 4) : (wn == 16 ? 6 : 4); }
+
+// Enqueue the persistent 256x128-tile kernel (gemm_persist.hip) with `grid`
+// workgroups (one per CU): mode kDense (tail tiles split along K when
+// p.sk_tiles > 0, p.ws then holds persistent_workspace_bytes(...) bytes whose
+// counters must be zero on entry and are left zero) or kMasked (G <= 1024).
+// A, B, sfa and D of all groups are addressed with 32-bit offsets.
+size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces);
+hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream);
 
 // Enqueue the GEMM kernel (and the split-K reduction when p.splits > 1).
 hipError_t launch_gemm(int mode, int cfg, const GemmParams& p, int groups, hipStream_t stream);

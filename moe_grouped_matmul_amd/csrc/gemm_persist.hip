@@ -1,0 +1,453 @@
+// Persistent block-scaled FP8 GEMM for gfx950: one 512-thread workgroup per
+// CU walks a list of 256 x 128 output tiles with one continuous LDS ring, so
+// the next tile's first K blocks load while the current tile finishes and
+// stores.  Used for the dense form with M > 128 and for the M-grouped masked
+// form.
+//
+// The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
+// closed-form equation: for every 128-wide K block the fp8 partial product of
+// a tile is formed by the matrix cores and promoted into an fp32 accumulator
+// with alpha[row, k] * beta[k]; the epilogue rounds to bf16.
+//
+// Tile scheduler:
+//   * dense: tile ids are walked round-robin over the workgroups (id b, b + G,
+//     ...), each id mapped so that the 8 XCDs run contiguous, m-grouped tile
+//     ranges (operand reuse in each XCD's L2).  When the tile count leaves a
+//     partial last round, those tail tiles are split along K into P pieces
+//     run by otherwise idle workgroups: each piece stores an fp32 partial tile
+//     (coherent across XCDs) and the last piece of a tile to finish (agent-
+//     scope counter) sums the partials in piece order and writes bf16, so the
+//     result does not depend on the order in which pieces finish;
+//   * masked (Lesson 13, Fig. 13-3, masked layout): every workgroup reads
+//     masked_m on the device and builds the prefix sums of the active tiles
+//     per group, sum_g ceil(masked_m[g] / 256) * ceil(N / 128); task ids are
+//     walked round-robin and located by binary search, so only the rows below
+//     masked_m are computed and the launch shape is fixed (graph-capturable).
+//
+// Main loop (one iteration = one K block of one tile): the three ring slots
+// are separate LDS arrays; iteration j's operands sit in slot j % 3.  A wave
+// reads all its fragments of iteration j, waits for its own loads of
+// iteration j + 1 and for its LDS reads, and after one s_barrier refills slot
+// j % 3 with iteration j + 3 -- which may belong to the next tile -- then runs
+// the MFMAs and promotions of iteration j.  A finished tile is written with
+// buffer stores (lanes outside the tile address past the buffer end) while
+// the next tile's blocks are already loading.  Operand layout, fragment order
+// and promotion are those of the non-persistent LDS-ring kernel
+// (gemm_lds.hip).
+
+#include "dg_internal.hpp"
+#include "gemm_common.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int kRsrcWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 family
+constexpr int kCoherent = 16;              // sc1: coherent across the XCDs' L2 caches
+constexpr uint32_t kOOB = 0xFFFFFF00u;     // an offset past every buffer range used here
+constexpr int kMaxMaskedGroups = 1024;     // groups the masked task list supports
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
+}
+
+// One segment of a workgroup's work: K blocks [kb_lo, kb_hi) of one tile.
+struct Seg {
+  int mt, nt, grp;   // row tile, column tile, group (masked)
+  int row_limit;     // rows of the tile that exist (masked: below masked_m)
+  int kb_lo, kb_hi;
+  int tail;          // -1: whole tile; else index of a K-split tail tile
+  int piece;         // piece of that tail tile
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int WGM = 4;
+  constexpr int WGN = 2;
+  constexpr int TM = 4;
+  constexpr int TN = 4;
+  constexpr int BM = WGM * 64;
+  constexpr int BN = WGN * 64;
+  constexpr int NWAVES = 8;
+  constexpr int A_INS = BM / 8 / NWAVES;  // 1 KB (8-row) loads per wave per K block
+  constexpr int B_INS = BN / 8 / NWAVES;
+  constexpr int L_BLOCK = A_INS + B_INS + 1;  // + one alpha load per wave
+  constexpr int GM = 4;                       // m-tiles per tile group
+  static_assert(2 * L_BLOCK < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[BN * 128];
+  __shared__ __attribute__((aligned(256))) float sS0[NWAVES * 64];
+  __shared__ __attribute__((aligned(256))) float sS1[NWAVES * 64];
+  __shared__ __attribute__((aligned(256))) float sS2[NWAVES * 64];
+  __shared__ int pref[MODE == kMasked ? kMaxMaskedGroups + 1 : 1];  // active tiles before each group
+  __shared__ int mmv[MODE == kMasked ? kMaxMaskedGroups : 1];       // masked_m clamped to [0, max_m]
+  __shared__ int last_piece;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN;
+  const int wn = wave % WGN;
+  const int q = lane >> 4;
+  const int b = (int)blockIdx.x;
+  const int G = (int)gridDim.x;
+
+  const int K = p.K;
+  const int N = p.N;
+  const int KB = K >> 7;
+  const int NB = (N + 127) >> 7;
+  const int rows = (int)p.rows;  // dense: M; masked: max_m
+  const int ngrp = MODE == kMasked ? p.G : 1;
+
+  // ---- task list
+  int T;  // tasks: dense tiles / active masked tiles
+  if (MODE == kMasked) {
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < ngrp; base += 64) {
+        const int g = base + lane;
+        int v = 0;
+        if (g < ngrp) {
+          int mm = p.index[g];
+          mm = mm < 0 ? 0 : (mm > rows ? rows : mm);
+          mmv[g] = mm;
+          v = ((mm + BM - 1) / BM) * p.n_tiles;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(v, off);
+          if (lane >= off) v += o;
+        }
+        if (g < ngrp) pref[g + 1] = carry + v;
+        carry += __shfl(v, 63);
+      }
+      if (lane == 0) pref[0] = 0;
+    }
+    __syncthreads();
+    T = __builtin_amdgcn_readfirstlane(pref[ngrp]);
+  } else {
+    T = p.m_tiles * p.n_tiles;
+  }
+  const int dp_tiles = MODE == kMasked ? T : p.dp_tiles;  // tasks run as whole tiles
+  const int P = p.sk_pieces;                               // pieces per tail tile (dense)
+  const int n_dp = b < dp_tiles ? (dp_tiles - b + G - 1) / G : 0;
+  const bool has_tail = MODE == kDense && b < p.sk_tiles * P;
+  const int nseg = n_dp + (has_tail ? 1 : 0);
+  if (nseg == 0) return;  // uniform over the workgroup
+
+  auto seg_of = [&](int s) -> Seg {
+    Seg r;
+    r.grp = 0;
+    r.tail = -1;
+    r.piece = 0;
+    r.kb_lo = 0;
+    r.kb_hi = KB;
+    int d;
+    if (s < n_dp) {
+      d = b + s * G;
+    } else {
+      r.tail = b / P;
+      r.piece = b - r.tail * P;
+      d = dp_tiles + r.tail;
+      r.kb_lo = r.piece * p.sk_kb;
+      r.kb_hi = r.kb_lo + p.sk_kb < KB ? r.kb_lo + p.sk_kb : KB;
+    }
+    if (MODE == kMasked) {
+      int lo = 0, hi = ngrp - 1;  // largest g with pref[g] <= d
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pref[mid] <= d) lo = mid;
+        else hi = mid - 1;
+      }
+      r.grp = __builtin_amdgcn_readfirstlane(lo);
+      const int local = d - __builtin_amdgcn_readfirstlane(pref[r.grp]);
+      r.mt = local / p.n_tiles;
+      r.nt = local - r.mt * p.n_tiles;
+      const int mm = __builtin_amdgcn_readfirstlane(mmv[r.grp]);
+      r.row_limit = mm - r.mt * BM < BM ? mm - r.mt * BM : BM;
+    } else {
+      grouped_mn(xcd_tile(d, T), p.m_tiles, p.n_tiles, GM, &r.mt, &r.nt);
+      r.row_limit = rows - r.mt * BM < BM ? rows - r.mt * BM : BM;
+    }
+    return r;
+  };
+
+  // ---- buffer resources over whole arrays (all groups); offsets are 32-bit
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)(ngrp * rows) * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (uint32_t)(ngrp * N) * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
+  const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(p.A, 0);
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(p.B, 0);
+  const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(p.sfa, 0);
+
+  // DMA lanes: instruction i of this wave fills LDS rows 64 i + 8 wave + lane / 8;
+  // lane chunk (lane % 8) of row r holds K chunk (lane % 8) ^ (r % 8).  B rows
+  // enter LDS permuted (row 16 j + i of a 64-row block holds weight row
+  // (i / 4) * 16 + 4 j + i % 4 of it) so each lane ends with 16 consecutive
+  // output columns of one row.
+  const int dma_chunk = ((lane & 7) ^ ((lane >> 3) & 7)) << 4;
+  const int a_loc = 8 * wave + (lane >> 3);
+  const int b_perm = ((a_loc & 15) >> 2) * 16 + 4 * (a_loc >> 4) + (a_loc & 3);
+
+  const int q16 = lane & 15;
+  const uint32_t fr_lo = (uint32_t)(q16 * 128 + ((q ^ (lane & 7)) << 4));
+  const uint32_t fr_hi = (uint32_t)(q16 * 128 + (((q + 4) ^ (lane & 7)) << 4));
+  const uint32_t a_row0 = (uint32_t)(wm * 64 * 128);
+  const uint32_t b_row0 = (uint32_t)(wn * 64 * 128);
+
+#define PS_SA(st) ((st) == 0 ? sA0 : ((st) == 1 ? sA1 : sA2))
+#define PS_SB(st) ((st) == 0 ? sB0 : ((st) == 1 ? sB1 : sB2))
+#define PS_SS(st) ((st) == 0 ? sS0 : ((st) == 1 ? sS1 : sS2))
+
+  // ---- issue pointer: iteration j + 3 of this workgroup's sequence.  Its
+  // per-lane source offsets change only with its tile (rows outside the tile
+  // get an offset past the buffer end); the K block enters through soffset.
+  int is_seg = 0;
+  Seg is_t = seg_of(0);
+  int is_kb = is_t.kb_lo;
+  uint32_t is_aoff[A_INS];
+  uint32_t is_boff[B_INS];
+  uint32_t is_soff;
+  auto is_setup = [&]() {
+    const int arow = is_t.grp * rows + is_t.mt * BM;
+    const int brow = is_t.grp * N + is_t.nt * BN;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = 64 * i + a_loc;
+      is_aoff[i] = r < is_t.row_limit ? (uint32_t)(arow + r) * (uint32_t)K + dma_chunk : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int c = 64 * i + b_perm;
+      is_boff[i] = is_t.nt * BN + c < N ? (uint32_t)(brow + c) * (uint32_t)K + dma_chunk : kOOB;
+    }
+    is_soff = (uint32_t)((is_t.grp * KB * rows + is_t.mt * BM + wave * 64 + lane) * 4);
+  };
+  is_setup();
+
+  // all loads of the issue pointer's block into slot st_, then advance it
+#define PS_ISSUE(st_)                                                                                      \
+  do {                                                                                                     \
+    const bool in_ = is_seg < nseg;                                                                        \
+    const __amdgpu_buffer_rsrc_t ra_ = in_ ? ra : ra0;                                                     \
+    const __amdgpu_buffer_rsrc_t rb_ = in_ ? rb : rb0;                                                     \
+    const __amdgpu_buffer_rsrc_t rs_ = in_ ? rs : rs0;                                                     \
+    const int ks_ = in_ ? is_kb << 7 : 0;                                                                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < A_INS; ++i_)                                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(PS_SA(st_) + (i_ * NWAVES + wave) * 1024), \
+                                                 16, is_aoff[i_], ks_, 0, 0);                              \
+    _Pragma("unroll") for (int i_ = 0; i_ < B_INS; ++i_)                                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_, (DG_LDS void*)(PS_SB(st_) + (i_ * NWAVES + wave) * 1024), \
+                                                 16, is_boff[i_], ks_, 0, 0);                              \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(PS_SS(st_) + wave * 64), 4, is_soff,      \
+                                             in_ ? is_kb * rows * 4 : 0, 0, 0);                            \
+    if (in_ && ++is_kb == is_t.kb_hi) {                                                                    \
+      if (++is_seg < nseg) {                                                                               \
+        is_t = seg_of(is_seg);                                                                             \
+        is_kb = is_t.kb_lo;                                                                                \
+        is_setup();                                                                                        \
+      }                                                                                                    \
+    }                                                                                                      \
+  } while (0)
+
+  int J = n_dp * KB;  // iterations of this workgroup
+  if (has_tail) {
+    const Seg t = seg_of(n_dp);
+    J += t.kb_hi - t.kb_lo;
+  }
+
+  // ---- compute pointer: iteration j
+  int cp_seg = 0;
+  Seg cp_t = seg_of(0);
+  int cp_kb = cp_t.kb_lo;
+  const DG_CONST float* sfb_w;
+  int act;
+  auto cp_setup = [&]() {
+    int nblk = (cp_t.nt * BN + wn * 64) >> 7;
+    nblk = nblk < NB ? nblk : NB - 1;
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_t.grp * NB + nblk) * KB);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
+    int a_ = (cp_t.row_limit - wm * 64 + 15) >> 4;  // 16-row MFMA tiles holding stored rows
+    a_ = a_ < 0 ? 0 : (a_ > TM ? TM : a_);
+    act = __builtin_amdgcn_readfirstlane(a_);
+  };
+  cp_setup();
+
+  f32x4 u[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) u[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // bf16 output of the compute tile: for row tile i, lane l holds output row
+  // wm*64 + 16 i + l % 16 and its 16 consecutive columns wn*64 + q*16 + [0, 16)
+  // (two 16-byte stores; lanes outside the tile store past the buffer end)
+#define PS_STORE_TILE()                                                                                    \
+  do {                                                                                                     \
+    const int gc0_ = cp_t.nt * BN + wn * 64 + q * 16;                                                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
+      const int r_ = wm * 64 + i_ * 16 + q16;                                                              \
+      const uint32_t off_ = (r_ < cp_t.row_limit && gc0_ < N)                                              \
+                                ? ((uint32_t)(cp_t.grp * rows + cp_t.mt * BM + r_) * (uint32_t)N + gc0_) * 2u \
+                                : kOOB;                                                                    \
+      uint32_t w_[8];                                                                                      \
+      _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                  \
+        w_[2 * j_] = (uint32_t)f32_to_bf16_rne(u[i_][j_][0]) | ((uint32_t)f32_to_bf16_rne(u[i_][j_][1]) << 16); \
+        w_[2 * j_ + 1] = (uint32_t)f32_to_bf16_rne(u[i_][j_][2]) | ((uint32_t)f32_to_bf16_rne(u[i_][j_][3]) << 16); \
+      }                                                                                                    \
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[0], w_[1], w_[2], w_[3]}, rd, off_, 0, 0);           \
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rd, off_ == kOOB ? kOOB : off_ + 16u, 0, 0); \
+    }                                                                                                      \
+  } while (0)
+
+#define PS_FRAG(dst_, base_, off_)                                                                         \
+  do {                                                                                                     \
+    const uint4 lo_ = *reinterpret_cast<const uint4*>((base_) + fr_lo + (off_));                          \
+    const uint4 hi_ = *reinterpret_cast<const uint4*>((base_) + fr_hi + (off_));                          \
+    dst_ = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
+  } while (0)
+
+  // One iteration jj_ (slot st_ = jj_ % 3), see the header.  The wait for
+  // iteration jj_ + 1 counts loads only: loads complete in issue order, so at
+  // most L_BLOCK outstanding operations means all loads up to iteration
+  // jj_ + 1 have landed, whatever output stores are also in flight (those only
+  // add to the count, which makes the wait longer, never shorter).
+#define PS_STEP(st_, jj_)                                                                                  \
+  do {                                                                                                     \
+    const bool live_ = (jj_) < J;                                                                          \
+    const float beta_ = live_ ? sfb_w[cp_kb] : 0.f;                                                        \
+    const uint8_t* as_ = PS_SA(st_) + a_row0;                                                              \
+    const uint8_t* bs_ = PS_SB(st_) + b_row0;                                                              \
+    i32x8 af_[TM];                                                                                         \
+    i32x8 bf_[TN];                                                                                         \
+    float al_[TM];                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
+      PS_FRAG(af_[i_], as_, i_ * 2048);                                                                    \
+      al_[i_] = PS_SS(st_)[wm * 64 + i_ * 16 + q16];                                                       \
+    }                                                                                                      \
+    _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) PS_FRAG(bf_[j_], bs_, j_ * 2048);                   \
+    wait_vmcnt<L_BLOCK>();                                                                                 \
+    wait_lgkmcnt0(); /* own reads of this slot done before anyone may refill it */                        \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    PS_ISSUE(st_);                                                                                         \
+    if (live_) {                                                                                           \
+      float sc_[TM];                                                                                       \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) sc_[i_] = al_[i_] * beta_;                         \
+      _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                  \
+        _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                \
+          if (MODE != kMasked || i_ < act) {                                                               \
+            const f32x4 t_ = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) u[i_][j_][v_] = __builtin_fmaf(t_[v_], sc_[i_], u[i_][j_][v_]); \
+          }                                                                                                \
+        }                                                                                                  \
+      }                                                                                                    \
+      if (++cp_kb == cp_t.kb_hi && cp_t.tail < 0) {  /* a whole tile is done: store it */                  \
+        PS_STORE_TILE();                                                                                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                  \
+          _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) u[i_][j_] = f32x4{0.f, 0.f, 0.f, 0.f};         \
+        if (++cp_seg < nseg) {                                                                             \
+          cp_t = seg_of(cp_seg);                                                                           \
+          cp_kb = cp_t.kb_lo;                                                                              \
+          cp_setup();                                                                                      \
+        }                                                                                                  \
+      }                                                                                                    \
+    }                                                                                                      \
+  } while (0)
+
+  // prologue: iterations 0, 1, 2 into slots 0, 1, 2
+  PS_ISSUE(0);
+  PS_ISSUE(1);
+  PS_ISSUE(2);
+  wait_vmcnt<2 * L_BLOCK>();  // iteration 0 landed (this wave's part)
+  __builtin_amdgcn_s_barrier();
+  // iterations, padded to whole ring cycles; a tail piece (always this
+  // workgroup's last segment) leaves the loop with its partial in u
+  for (int j = 0; j < J; j += 3) {
+    PS_STEP(0, j);
+    PS_STEP(1, j + 1);
+    PS_STEP(2, j + 2);
+  }
+  wait_vmcnt<0>();  // no LDS writes or stores in flight past this point
+
+#undef PS_STEP
+#undef PS_FRAG
+#undef PS_ISSUE
+#undef PS_SA
+#undef PS_SB
+#undef PS_SS
+
+  if (has_tail) {
+    // K-split tail tile: fp32 partial in fragment order (piece pc of tail
+    // tile s, wave w, fragment (i, j), lane l at byte
+    // (((s * P + pc) * 8 + w) * 16 + i * 4 + j) * 1024 + 16 l), coherent stores;
+    // the last piece sums all pieces' partials in piece order
+    const uint32_t frag_bytes = (uint32_t)TM * TN * 1024u;
+    const uint32_t tile_bytes = (uint32_t)NWAVES * frag_bytes;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws, (uint32_t)p.sk_tiles * (uint32_t)P * tile_bytes);
+    const uint32_t w_off = (uint32_t)(cp_t.tail * P) * tile_bytes + (uint32_t)wave * frag_bytes + (uint32_t)lane * 16u;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, u[i][j]), rw,
+                                               w_off + (uint32_t)(i * TN + j) * 1024u,
+                                               (uint32_t)cp_t.piece * tile_bytes, kCoherent);
+    wait_vmcnt<0>();
+    __syncthreads();
+    unsigned int* counters = reinterpret_cast<unsigned int*>(reinterpret_cast<uint8_t*>(p.ws) +
+                                                             (size_t)p.sk_tiles * P * tile_bytes);
+    if (tid == 0)
+      last_piece = __hip_atomic_fetch_add(&counters[cp_t.tail], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned int)(P - 1);
+    __syncthreads();
+    if (!last_piece) return;
+#define PS_LDP(pc_, i_, j_)                                                                                \
+  __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(                                         \
+                                rw, w_off + (uint32_t)((i_) * TN + (j_)) * 1024u, (uint32_t)(pc_) * tile_bytes, kCoherent))
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) u[i][j] = PS_LDP(0, i, j);
+    for (int pc = 1; pc < P; ++pc) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) u[i][j] += PS_LDP(pc, i, j);
+    }
+#undef PS_LDP
+    if (tid == 0)  // ready for the next call on this workspace
+      __hip_atomic_store(&counters[cp_t.tail], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    PS_STORE_TILE();
+  }
+#undef PS_STORE_TILE
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+}  // namespace
+
+size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces) {
+  if (sk_tiles <= 0 || sk_pieces <= 1) return 0;
+  // fp32 partials of 256 x 128 tiles, then one uint32 counter per tail tile
+  return (size_t)sk_tiles * sk_pieces * 256 * 128 * 4 + (size_t)sk_tiles * 4;
+}
+
+hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (mode == kMasked)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dg

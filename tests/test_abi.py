@@ -119,9 +119,15 @@ def test_utilities(lib):
     assert lib.dg_version().decode().startswith("dg-mi355x")
     assert lib.dg_set_num_cus(64) == 0
     assert lib.dg_set_num_cus(0) == 0
-    # dense small-M shapes ask for split-K scratch, large ones do not
+    # dense small-M shapes ask for split-K scratch; large ones only when the
+    # tile count leaves a partial last round on the (default 256) CUs, whose
+    # tail tiles are then split along K: 4096x7168 -> 16 x 56 = 896 tiles,
+    # 128 tail tiles in 2 pieces of 256x128 fp32 partials + one counter each
     assert lib.dg_get_workspace_size(0, 64, 2112, 7168, 1) > 0
-    assert lib.dg_get_workspace_size(0, 4096, 7168, 16384, 1) == 0
+    assert lib.dg_set_num_cus(256) == 0  # the MI355X count, also when no device is visible
+    assert lib.dg_get_workspace_size(0, 4096, 7168, 16384, 1) == 128 * 2 * 256 * 128 * 4 + 128 * 4
+    assert lib.dg_get_workspace_size(0, 4096, 4096, 7168, 1) == 0  # 512 tiles: whole rounds
+    assert lib.dg_set_num_cus(0) == 0
     assert lib.dg_get_workspace_size(2, 256, 4096, 7168, 32) == 0
 
 

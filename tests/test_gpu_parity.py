@@ -157,7 +157,14 @@ SKINNY = [(1, 2112, 7168), (17, 144, 1024), (64, 2112, 7168), (100, 272, 4096), 
           (64, 4096, 640), (128, 32768, 512), (33, 24576, 1536), (64, 7168, 2048)]
 
 
-@pytest.mark.parametrize("M,N,K", SKINNY)
+# persistent kernel (M > 128): tile counts that leave a partial last round, so
+# tail tiles are split along K into pieces (2 to 4, including a short last
+# piece), again with one workspace reused across calls
+PERSISTENT_TAIL = [(130, 144, 640), (257, 400, 384), (300, 272, 1024), (1000, 528, 512), (777, 2112, 640),
+                   (2048, 4096, 1536)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY + PERSISTENT_TAIL)
 def test_dense_skinny_matches_oracle_with_reused_workspace(M, N, K):
     a32, b32 = workloads.dense(M, N, K, seed=M + 3 * N + K)
     qa, sa = oracle.quant_1x128(a32)
