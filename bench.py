@@ -43,9 +43,10 @@ COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte cou
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE counters (calibrated against a plain copy) and recorded together with
 # a hash of the kernel's sources: reported only while those sources are unchanged.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_lds_kernel_dense_sweep.md")
-KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_lds.hip", "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
-                  "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/build.py")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_dense_sweep.md")
+KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
+                  "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/csrc/api.cpp",
+                  "moe_grouped_matmul_amd/build.py")
 
 
 def kernel_source_hash():
@@ -179,7 +180,7 @@ def run_dense(args, torch, dg, workloads):
         ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
         flops, nbytes = dense_work(M, N, K)
         prepared.append(dict(M=M, N=N, K=K, sets=sets, ws=ws, flops=flops, bytes=nbytes,
-                             kernel="fp8_gemm_lds_kernel<4,2,dense>" if M > 128 else "fp8_gemm_skinny_kernel"))
+                             kernel="fp8_gemm_persistent_kernel<dense>" if M > 128 else "fp8_gemm_skinny_kernel"))
     torch.cuda.synchronize()
     timer = Timer(torch)
 
@@ -367,7 +368,7 @@ def run_grouped(args, torch, dg, workloads):
     else:
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
-    kname = "fp8_gemm_lds_kernel<2,4,contiguous>" if args.workload == "contiguous" else "fp8_gemm_lds_kernel<4,2,masked>"
+    kname = "fp8_gemm_lds_kernel<2,4,contiguous>" if args.workload == "contiguous" else "fp8_gemm_persistent_kernel<masked>"
     roof.update(traffic=None, kernel=f"{kname} ({big['N']}x{big['K']})",
                 avg_launch_us=big["gemm_us"])
     name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
