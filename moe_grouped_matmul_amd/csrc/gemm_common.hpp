@@ -17,12 +17,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // operand read touches at the same logical chunk land on distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> a packed bf16 pair (a in the low half), rounded to nearest
+// even by the gfx950 conversion instruction (v_cvt_pk_bf16_f32, under the
+// default round-to-nearest-even mode); NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)pack_bf16x2(f, 0.f); }
 
 // s_waitcnt immediate that waits for vmcnt <= n and leaves the other counters alone
 // (gfx9 layout: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8]).

@@ -303,10 +303,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_lds_kernel(GemmParams p) {
     uint32_t w[8];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      w[2 * j] = (uint32_t)f32_to_bf16_rne(u[i][j][0]) |
-                 ((uint32_t)f32_to_bf16_rne(u[i][j][1]) << 16);
-      w[2 * j + 1] = (uint32_t)f32_to_bf16_rne(u[i][j][2]) |
-                     ((uint32_t)f32_to_bf16_rne(u[i][j][3]) << 16);
+      w[2 * j] = pack_bf16x2(u[i][j][0], u[i][j][1]);
+      w[2 * j + 1] = pack_bf16x2(u[i][j][2], u[i][j][3]);
     }
     uint4* dst = reinterpret_cast<uint4*>(D + gr * N + gc0);
     dst[0] = uint4{w[0], w[1], w[2], w[3]};

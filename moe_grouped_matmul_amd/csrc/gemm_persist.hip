@@ -77,15 +77,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   constexpr int GM = 4;                       // m-tiles per tile group
   static_assert(2 * L_BLOCK < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA2[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB2[BN * 128];
-  __shared__ __attribute__((aligned(256))) float sS0[NWAVES * 64];
-  __shared__ __attribute__((aligned(256))) float sS1[NWAVES * 64];
-  __shared__ __attribute__((aligned(256))) float sS2[NWAVES * 64];
+  // ring slots: A rows [0, BM * 128), B rows [BM * 128, SLOT_S), alpha of
+  // the tile's rows [SLOT_S, SLOT_BYTES); one array per slot keeps the
+  // compiler's tracking of the buffer-to-LDS loads exact
+  constexpr int SLOT_S = (BM + BN) * 128;
+  constexpr int SLOT_BYTES = SLOT_S + NWAVES * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[SLOT_BYTES];
   __shared__ int pref[MODE == kMasked ? kMaxMaskedGroups + 1 : 1];  // active tiles before each group
   __shared__ int mmv[MODE == kMasked ? kMaxMaskedGroups : 1];       // masked_m clamped to [0, max_m]
   __shared__ int last_piece;
@@ -180,13 +179,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   };
 
   // ---- buffer resources over whole arrays (all groups); offsets are 32-bit
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)(ngrp * rows) * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (uint32_t)(ngrp * N) * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa, (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u);
+  const uint32_t a_bytes = (uint32_t)(ngrp * rows) * (uint32_t)K;
+  const uint32_t b_bytes = (uint32_t)(ngrp * N) * (uint32_t)K;
+  const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u;
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
-  const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(p.A, 0);
-  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(p.B, 0);
-  const __amdgpu_buffer_rsrc_t rs0 = make_rsrc(p.sfa, 0);
 
   // DMA lanes: instruction i of this wave fills LDS rows 64 i + 8 wave + lane / 8;
   // lane chunk (lane % 8) of row r holds K chunk (lane % 8) ^ (r % 8).  B rows
@@ -203,9 +199,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const uint32_t a_row0 = (uint32_t)(wm * 64 * 128);
   const uint32_t b_row0 = (uint32_t)(wn * 64 * 128);
 
-#define PS_SA(st) ((st) == 0 ? sA0 : ((st) == 1 ? sA1 : sA2))
-#define PS_SB(st) ((st) == 0 ? sB0 : ((st) == 1 ? sB1 : sB2))
-#define PS_SS(st) ((st) == 0 ? sS0 : ((st) == 1 ? sS1 : sS2))
+#define PS_SLOT(st) ((st) == 0 ? slot0 : ((st) == 1 ? slot1 : slot2))
+#define PS_SA(st) (PS_SLOT(st))
+#define PS_SB(st) (PS_SLOT(st) + BM * 128)
+#define PS_SS(st) (reinterpret_cast<float*>(PS_SLOT(st) + SLOT_S))
 
   // ---- issue pointer: iteration j + 3 of this workgroup's sequence.  Its
   // per-lane source offsets change only with its tile (rows outside the tile
@@ -237,10 +234,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #define PS_ISSUE(st_)                                                                                      \
   do {                                                                                                     \
     const bool in_ = is_seg < nseg;                                                                        \
-    const __amdgpu_buffer_rsrc_t ra_ = in_ ? ra : ra0;                                                     \
-    const __amdgpu_buffer_rsrc_t rb_ = in_ ? rb : rb0;                                                     \
-    const __amdgpu_buffer_rsrc_t rs_ = in_ ? rs : rs0;                                                     \
-    const int ks_ = in_ ? is_kb << 7 : 0;                                                                  \
+    /* past the last iteration: zero-length ranges (loads return zeros), selected without a branch */    \
+    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(p.A, in_ ? a_bytes : 0u);                                 \
+    const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(p.B, in_ ? b_bytes : 0u);                                 \
+    const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(p.sfa, in_ ? s_bytes : 0u);                               \
+    const int ks_ = is_kb << 7;                                                                            \
     _Pragma("unroll") for (int i_ = 0; i_ < A_INS; ++i_)                                                   \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(PS_SA(st_) + (i_ * NWAVES + wave) * 1024), \
                                                  16, is_aoff[i_], ks_, 0, 0);                              \
@@ -248,7 +246,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_, (DG_LDS void*)(PS_SB(st_) + (i_ * NWAVES + wave) * 1024), \
                                                  16, is_boff[i_], ks_, 0, 0);                              \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(PS_SS(st_) + wave * 64), 4, is_soff,      \
-                                             in_ ? is_kb * rows * 4 : 0, 0, 0);                            \
+                                             is_kb * rows * 4, 0, 0);                                      \
     if (in_ && ++is_kb == is_t.kb_hi) {                                                                    \
       if (++is_seg < nseg) {                                                                               \
         is_t = seg_of(is_seg);                                                                             \
@@ -289,24 +287,37 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #pragma unroll
     for (int j = 0; j < TN; ++j) u[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // bf16 output of the compute tile: for row tile i, lane l holds output row
-  // wm*64 + 16 i + l % 16 and its 16 consecutive columns wn*64 + q*16 + [0, 16)
-  // (two 16-byte stores; lanes outside the tile store past the buffer end)
-#define PS_STORE_TILE()                                                                                    \
+  // bf16 output of a finished tile, from u: for row tile i, lane l holds
+  // output row wm*64 + 16 i + l % 16 and its 16 consecutive columns
+  // wn*64 + q*16 + [0, 16) (two 16-byte stores; lanes outside the tile store
+  // past the buffer end).  A tile that finishes in the main loop stays in u
+  // until the next iteration's barrier has passed; its stores are then issued
+  // ahead of that iteration's loads, so a whole iteration passes before a load
+  // wait can depend on their completion.  (st_row0, st_col0, st_rows) locate
+  // the tile.
+  bool pend = false;
+  int st_row0 = 0, st_col0 = 0, st_rows = 0;
+#define PS_MARK_TILE()                                                                                     \
   do {                                                                                                     \
-    const int gc0_ = cp_t.nt * BN + wn * 64 + q * 16;                                                      \
+    st_row0 = cp_t.grp * rows + cp_t.mt * BM;                                                              \
+    st_col0 = cp_t.nt * BN;                                                                                \
+    st_rows = cp_t.row_limit;                                                                              \
+  } while (0)
+#define PS_STORE_U()                                                                                       \
+  do {                                                                                                     \
+    const int gc0_ = st_col0 + wn * 64 + q * 16;                                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
       const int r_ = wm * 64 + i_ * 16 + q16;                                                              \
-      const uint32_t off_ = (r_ < cp_t.row_limit && gc0_ < N)                                              \
-                                ? ((uint32_t)(cp_t.grp * rows + cp_t.mt * BM + r_) * (uint32_t)N + gc0_) * 2u \
-                                : kOOB;                                                                    \
+      const uint32_t off_ =                                                                                \
+          (r_ < st_rows && gc0_ < N) ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u : kOOB;        \
       uint32_t w_[8];                                                                                      \
       _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                  \
-        w_[2 * j_] = (uint32_t)f32_to_bf16_rne(u[i_][j_][0]) | ((uint32_t)f32_to_bf16_rne(u[i_][j_][1]) << 16); \
-        w_[2 * j_ + 1] = (uint32_t)f32_to_bf16_rne(u[i_][j_][2]) | ((uint32_t)f32_to_bf16_rne(u[i_][j_][3]) << 16); \
+        w_[2 * j_] = pack_bf16x2(u[i_][j_][0], u[i_][j_][1]);                                              \
+        w_[2 * j_ + 1] = pack_bf16x2(u[i_][j_][2], u[i_][j_][3]);                                          \
       }                                                                                                    \
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[0], w_[1], w_[2], w_[3]}, rd, off_, 0, 0);           \
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rd, off_ == kOOB ? kOOB : off_ + 16u, 0, 0); \
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rd,                        \
+                                             off_ == kOOB ? kOOB : off_ + 16u, 0, 0);                      \
     }                                                                                                      \
   } while (0)
 
@@ -317,74 +328,158 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     dst_ = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
   } while (0)
 
-  // One iteration jj_ (slot st_ = jj_ % 3), see the header.  The wait for
-  // iteration jj_ + 1 counts loads only: loads complete in issue order, so at
-  // most L_BLOCK outstanding operations means all loads up to iteration
-  // jj_ + 1 have landed, whatever output stores are also in flight (those only
-  // add to the count, which makes the wait longer, never shorter).
-#define PS_STEP(st_, jj_)                                                                                  \
+  // this wave's fragments and row scales of the iteration held in slot st_
+#define PS_LOAD_FRAGS(st_, AF, BF, AL)                                                                     \
   do {                                                                                                     \
-    const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = live_ ? sfb_w[cp_kb] : 0.f;                                                        \
     const uint8_t* as_ = PS_SA(st_) + a_row0;                                                              \
     const uint8_t* bs_ = PS_SB(st_) + b_row0;                                                              \
-    i32x8 af_[TM];                                                                                         \
-    i32x8 bf_[TN];                                                                                         \
-    float al_[TM];                                                                                         \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
-      PS_FRAG(af_[i_], as_, i_ * 2048);                                                                    \
-      al_[i_] = PS_SS(st_)[wm * 64 + i_ * 16 + q16];                                                       \
+      PS_FRAG(AF[i_], as_, i_ * 2048);                                                                     \
+      AL[i_] = PS_SS(st_)[wm * 64 + i_ * 16 + q16];                                                        \
     }                                                                                                      \
-    _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) PS_FRAG(bf_[j_], bs_, j_ * 2048);                   \
-    wait_vmcnt<L_BLOCK>();                                                                                 \
-    wait_lgkmcnt0(); /* own reads of this slot done before anyone may refill it */                        \
-    __builtin_amdgcn_s_barrier();                                                                          \
-    PS_ISSUE(st_);                                                                                         \
-    if (live_) {                                                                                           \
-      float sc_[TM];                                                                                       \
-      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) sc_[i_] = al_[i_] * beta_;                         \
-      _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                  \
-        _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                \
-          if (MODE != kMasked || i_ < act) {                                                               \
-            const f32x4 t_ = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
-            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) u[i_][j_][v_] = __builtin_fmaf(t_[v_], sc_[i_], u[i_][j_][v_]); \
-          }                                                                                                \
+    _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) PS_FRAG(BF[j_], bs_, j_ * 2048);                    \
+  } while (0)
+
+  // The products and promotions of one iteration, with the next iteration's
+  // fragment reads from slot (st_ + 1) % 3 interleaved.  Dense: a fixed
+  // order of 16 steps, each one MFMA (B fragment j = k / 4, A fragment
+  // i = k % 4), one 16-byte LDS read of the next fragments and the four
+  // promotion FMAs of the MFMA two steps back, so the LDS reads and the FMAs
+  // overlap the matrix cores.  Masked: all reads first, then the MFMAs of the
+  // 16-row tiles holding rows below masked_m.
+#define PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN)                                                          \
+  do {                                                                                                     \
+    float sc_[TM];                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) sc_[i_] = AL[i_] * beta_;                            \
+    if constexpr (MODE == kMasked) {                                                                       \
+      const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
+      uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
+        _Pragma("unroll") for (int h_ = 0; h_ < 4; ++h_) {                                                 \
+          const int k_ = 4 * i_ + h_;                                                                      \
+          const int f_ = k_ >> 1;                                                                          \
+          const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +      \
+                              ((k_ & 1) ? fr_hi : fr_lo);                                                  \
+          if (k_ & 1) nhi_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                               \
+          else nlo_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                                      \
+        }                                                                                                  \
+        if (i_ < act) { /* 16-row tiles holding rows below masked_m */                                     \
+          f32x4 t_[TN];                                                                                    \
+          _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                \
+            t_[j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[j_], AF[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                \
+            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
+              u[i_][j_][v_] = __builtin_fmaf(t_[j_][v_], sc_[i_], u[i_][j_][v_]);                          \
         }                                                                                                  \
       }                                                                                                    \
-      if (++cp_kb == cp_t.kb_hi && cp_t.tail < 0) {  /* a whole tile is done: store it */                  \
-        PS_STORE_TILE();                                                                                   \
-        _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                  \
-          _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) u[i_][j_] = f32x4{0.f, 0.f, 0.f, 0.f};         \
-        if (++cp_seg < nseg) {                                                                             \
-          cp_t = seg_of(cp_seg);                                                                           \
-          cp_kb = cp_t.kb_lo;                                                                              \
-          cp_setup();                                                                                      \
+      _Pragma("unroll") for (int f_ = 0; f_ < TM + TN; ++f_) {                                             \
+        const i32x8 v8_ = i32x8{(int)nlo_[f_].x, (int)nlo_[f_].y, (int)nlo_[f_].z, (int)nlo_[f_].w,        \
+                                (int)nhi_[f_].x, (int)nhi_[f_].y, (int)nhi_[f_].z, (int)nhi_[f_].w};       \
+        if (f_ < TM) AN[f_] = v8_;                                                                         \
+        else BN_[f_ - TM] = v8_;                                                                           \
+      }                                                                                                    \
+    } else {                                                                                               \
+      const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
+      uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
+      f32x4 t_[TM * TN];                                                                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
+      _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 2; ++k_) {                                         \
+        if (k_ < TM * TN) {                                                                                \
+          t_[k_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[k_ / TM], AF[k_ % TM], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          const int f_ = k_ >> 1; /* fragment: A 0..TM-1, then B */                                        \
+          const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +      \
+                              ((k_ & 1) ? fr_hi : fr_lo);                                                  \
+          if (k_ & 1) nhi_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                               \
+          else nlo_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                                      \
         }                                                                                                  \
+        if (k_ >= 2) {                                                                                     \
+          const int kk_ = k_ - 2;                                                                          \
+          f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
+          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
+            uk_[v_] = __builtin_fmaf(t_[kk_][v_], sc_[kk_ % TM], uk_[v_]);                                 \
+          /* keeps these FMAs in this step: instruction selection would sink them to the block's end */    \
+          asm volatile("" : "+v"(uk_));                                                                    \
+        }                                                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                                 \
+      }                                                                                                    \
+      _Pragma("unroll") for (int f_ = 0; f_ < TM + TN; ++f_) {                                             \
+        const i32x8 v8_ = i32x8{(int)nlo_[f_].x, (int)nlo_[f_].y, (int)nlo_[f_].z, (int)nlo_[f_].w,        \
+                                (int)nhi_[f_].x, (int)nhi_[f_].y, (int)nhi_[f_].z, (int)nhi_[f_].w};       \
+        if (f_ < TM) AN[f_] = v8_;                                                                         \
+        else BN_[f_ - TM] = v8_;                                                                           \
       }                                                                                                    \
     }                                                                                                      \
   } while (0)
 
-  // prologue: iterations 0, 1, 2 into slots 0, 1, 2
+  // One iteration jj_ (slot st_ = jj_ % 3), see the header.  Fragments of
+  // iteration jj_ (AF, BF, AL) were read during iteration jj_ - 1; those of
+  // jj_ + 1 are read here (AN, BN_, ALN) while the matrix cores work.  The
+  // wait for iteration jj_ + 1 counts loads only: loads complete in issue
+  // order, so at most L_BLOCK outstanding operations means all loads up to
+  // iteration jj_ + 1 have landed, whatever output stores are also in flight
+  // (those only add to the count).  Iterations past this workgroup's last one
+  // read zero operands (their loads address zero-length ranges) and a zero
+  // scale, so their products add exactly nothing.
+#define PS_STEP(st_, jj_, AF, BF, AL, AN, BN_, ALN)                                                        \
+  do {                                                                                                     \
+    const bool live_ = (jj_) < J;                                                                          \
+    const float beta_ = live_ ? sfb_w[cp_kb] : 0.f;                                                        \
+    wait_vmcnt<L_BLOCK>();                                                                                 \
+    wait_lgkmcnt0(); /* own reads of this slot done before anyone may refill it */                        \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    if (pend) {                                                                                            \
+      PS_STORE_U();                                                                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                    \
+        _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) u[i_][j_] = f32x4{0.f, 0.f, 0.f, 0.f};           \
+      pend = false;                                                                                        \
+    }                                                                                                      \
+    PS_ISSUE(st_);                                                                                         \
+    PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN);                                                              \
+    if (live_ && ++cp_kb == cp_t.kb_hi && cp_t.tail < 0) { /* a whole tile is done */                     \
+      PS_MARK_TILE();                                                                                      \
+      pend = true;                                                                                         \
+      if (++cp_seg < nseg) {                                                                               \
+        cp_t = seg_of(cp_seg);                                                                             \
+        cp_kb = cp_t.kb_lo;                                                                                \
+        cp_setup();                                                                                        \
+      }                                                                                                    \
+    }                                                                                                      \
+  } while (0)
+
+  i32x8 afX[TM], bfX[TN], afY[TM], bfY[TN];
+  float alX[TM], alY[TM];
+  // prologue: iterations 0, 1, 2 into slots 0, 1, 2; fragments of iteration 0
   PS_ISSUE(0);
   PS_ISSUE(1);
   PS_ISSUE(2);
   wait_vmcnt<2 * L_BLOCK>();  // iteration 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
-  // iterations, padded to whole ring cycles; a tail piece (always this
-  // workgroup's last segment) leaves the loop with its partial in u
-  for (int j = 0; j < J; j += 3) {
-    PS_STEP(0, j);
-    PS_STEP(1, j + 1);
-    PS_STEP(2, j + 2);
+  PS_LOAD_FRAGS(0, afX, bfX, alX);
+  // iterations, padded to whole cycles of ring slots and fragment registers;
+  // a tail piece (always this workgroup's last segment) leaves the loop with
+  // its partial in u
+  for (int j = 0; j < J; j += 6) {
+    PS_STEP(0, j, afX, bfX, alX, afY, bfY, alY);
+    PS_STEP(1, j + 1, afY, bfY, alY, afX, bfX, alX);
+    PS_STEP(2, j + 2, afX, bfX, alX, afY, bfY, alY);
+    PS_STEP(0, j + 3, afY, bfY, alY, afX, bfX, alX);
+    PS_STEP(1, j + 4, afX, bfX, alX, afY, bfY, alY);
+    PS_STEP(2, j + 5, afY, bfY, alY, afX, bfX, alX);
   }
+  if (pend) PS_STORE_U();
   wait_vmcnt<0>();  // no LDS writes or stores in flight past this point
+  wait_lgkmcnt0();
 
 #undef PS_STEP
+#undef PS_COMPUTE
+#undef PS_LOAD_FRAGS
 #undef PS_FRAG
 #undef PS_ISSUE
 #undef PS_SA
 #undef PS_SB
 #undef PS_SS
+#undef PS_SLOT
 
   if (has_tail) {
     // K-split tail tile: fp32 partial in fragment order (piece pc of tail
@@ -427,9 +522,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #undef PS_LDP
     if (tid == 0)  // ready for the next call on this workspace
       __hip_atomic_store(&counters[cp_t.tail], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    PS_STORE_TILE();
+    PS_MARK_TILE();
+    PS_STORE_U();
   }
-#undef PS_STORE_TILE
+#undef PS_MARK_TILE
+#undef PS_STORE_U
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

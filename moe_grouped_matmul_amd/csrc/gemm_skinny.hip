@@ -345,19 +345,17 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
     if (r >= M || c0 >= N) continue;
     uint16_t* dst = p.D + (int64_t)r * N + c0;
     if (TN == 1) {
-      ushort4 o;
-      o.x = f32_to_bf16_rne(acc[i][0][0]);
-      o.y = f32_to_bf16_rne(acc[i][0][1]);
-      o.z = f32_to_bf16_rne(acc[i][0][2]);
-      o.w = f32_to_bf16_rne(acc[i][0][3]);
-      *reinterpret_cast<ushort4*>(dst) = o;
+      uint2 o;
+      o.x = pack_bf16x2(acc[i][0][0], acc[i][0][1]);
+      o.y = pack_bf16x2(acc[i][0][2], acc[i][0][3]);
+      *reinterpret_cast<uint2*>(dst) = o;
     } else {
       uint4 o;
       uint32_t w[4];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        w[2 * jj] = (uint32_t)f32_to_bf16_rne(acc[i][jj][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][jj][1]) << 16);
-        w[2 * jj + 1] = (uint32_t)f32_to_bf16_rne(acc[i][jj][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][jj][3]) << 16);
+        w[2 * jj] = pack_bf16x2(acc[i][jj][0], acc[i][jj][1]);
+        w[2 * jj + 1] = pack_bf16x2(acc[i][jj][2], acc[i][jj][3]);
       }
       o.x = w[0];
       o.y = w[1];
