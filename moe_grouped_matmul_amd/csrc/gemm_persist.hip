@@ -230,23 +230,32 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   };
   is_setup();
 
-  // all loads of the issue pointer's block into slot st_, then advance it
-#define PS_ISSUE(st_)                                                                                      \
+  // Loads of the issue pointer's block into slot st_: PS_ISSUE_BEGIN selects
+  // the ranges (zero-length past the last iteration, so those loads return
+  // zeros; selected without a branch), PS_ISSUE_LOAD(st_, n) issues load n
+  // (A_INS A loads, B_INS B loads, then alpha), PS_ISSUE_END advances the
+  // pointer.  The three must share one scope.
+#define PS_ISSUE_BEGIN()                                                                                   \
+  const bool in_ = is_seg < nseg;                                                                          \
+  const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(p.A, in_ ? a_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(p.B, in_ ? b_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(p.sfa, in_ ? s_bytes : 0u);                                 \
+  const int ks_ = is_kb << 7
+#define PS_ISSUE_LOAD(st_, n_)                                                                             \
   do {                                                                                                     \
-    const bool in_ = is_seg < nseg;                                                                        \
-    /* past the last iteration: zero-length ranges (loads return zeros), selected without a branch */    \
-    const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(p.A, in_ ? a_bytes : 0u);                                 \
-    const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(p.B, in_ ? b_bytes : 0u);                                 \
-    const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(p.sfa, in_ ? s_bytes : 0u);                               \
-    const int ks_ = is_kb << 7;                                                                            \
-    _Pragma("unroll") for (int i_ = 0; i_ < A_INS; ++i_)                                                   \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(PS_SA(st_) + (i_ * NWAVES + wave) * 1024), \
-                                                 16, is_aoff[i_], ks_, 0, 0);                              \
-    _Pragma("unroll") for (int i_ = 0; i_ < B_INS; ++i_)                                                   \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_, (DG_LDS void*)(PS_SB(st_) + (i_ * NWAVES + wave) * 1024), \
-                                                 16, is_boff[i_], ks_, 0, 0);                              \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(PS_SS(st_) + wave * 64), 4, is_soff,      \
-                                             is_kb * rows * 4, 0, 0);                                      \
+    if ((n_) < A_INS)                                                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(PS_SA(st_) + ((n_) * NWAVES + wave) * 1024), \
+                                               16, is_aoff[(n_) < A_INS ? (n_) : 0], ks_, 0, 0);           \
+    else if ((n_) < A_INS + B_INS)                                                                         \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_,                                                        \
+                                               (DG_LDS void*)(PS_SB(st_) + ((n_) - A_INS) * NWAVES * 1024 + wave * 1024), \
+                                               16, is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0); \
+    else                                                                                                   \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(PS_SS(st_) + wave * 64), 4, is_soff,    \
+                                               is_kb * rows * 4, 0, 0);                                    \
+  } while (0)
+#define PS_ISSUE_END()                                                                                     \
+  do {                                                                                                     \
     if (in_ && ++is_kb == is_t.kb_hi) {                                                                    \
       if (++is_seg < nseg) {                                                                               \
         is_t = seg_of(is_seg);                                                                             \
@@ -254,6 +263,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         is_setup();                                                                                        \
       }                                                                                                    \
     }                                                                                                      \
+  } while (0)
+#define PS_ISSUE(st_)                                                                                      \
+  do {                                                                                                     \
+    PS_ISSUE_BEGIN();                                                                                      \
+    _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, n_);                        \
+    PS_ISSUE_END();                                                                                        \
   } while (0)
 
   int J = n_dp * KB;  // iterations of this workgroup
@@ -343,8 +358,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // The products and promotions of one iteration, with the next iteration's
   // fragment reads from slot (st_ + 1) % 3 interleaved.  Dense: a fixed
   // order of 16 steps, each one MFMA (B fragment j = k / 4, A fragment
-  // i = k % 4), one 16-byte LDS read of the next fragments and the four
-  // promotion FMAs of the MFMA two steps back, so the LDS reads and the FMAs
+  // i = k % 4), one 16-byte LDS read of the next fragments (and, in the first steps,
+  // one of the block's loads) and the four promotion FMAs of the MFMA three
+  // steps back, so the LDS reads and the FMAs
   // overlap the matrix cores.  Masked: all reads first, then the MFMAs of the
   // 16-row tiles holding rows below masked_m.
 #define PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN)                                                          \
@@ -384,17 +400,18 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
       f32x4 t_[TM * TN];                                                                                   \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
-      _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 2; ++k_) {                                         \
+      _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 3; ++k_) {                                         \
         if (k_ < TM * TN) {                                                                                \
           t_[k_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[k_ / TM], AF[k_ % TM], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, k_); /* the block's loads, spread over the first steps */   \
           const int f_ = k_ >> 1; /* fragment: A 0..TM-1, then B */                                        \
           const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +      \
                               ((k_ & 1) ? fr_hi : fr_lo);                                                  \
           if (k_ & 1) nhi_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                               \
           else nlo_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                                      \
         }                                                                                                  \
-        if (k_ >= 2) {                                                                                     \
-          const int kk_ = k_ - 2;                                                                          \
+        if (k_ >= 3) {                                                                                     \
+          const int kk_ = k_ - 3;                                                                          \
           f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
           _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
             uk_[v_] = __builtin_fmaf(t_[kk_][v_], sc_[kk_ % TM], uk_[v_]);                                 \
@@ -434,8 +451,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) u[i_][j_] = f32x4{0.f, 0.f, 0.f, 0.f};           \
       pend = false;                                                                                        \
     }                                                                                                      \
-    PS_ISSUE(st_);                                                                                         \
-    PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN);                                                              \
+    {                                                                                                      \
+      PS_ISSUE_BEGIN();                                                                                    \
+      if constexpr (MODE == kMasked) {                                                                     \
+        _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, n_);                    \
+      }                                                                                                    \
+      PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN);                                                           \
+      PS_ISSUE_END();                                                                                      \
+    }                                                                                                      \
     if (live_ && ++cp_kb == cp_t.kb_hi && cp_t.tail < 0) { /* a whole tile is done */                     \
       PS_MARK_TILE();                                                                                      \
       pend = true;                                                                                         \
@@ -473,9 +496,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 
 #undef PS_STEP
 #undef PS_COMPUTE
+#undef PS_ISSUE
+#undef PS_ISSUE_BEGIN
+#undef PS_ISSUE_LOAD
+#undef PS_ISSUE_END
 #undef PS_LOAD_FRAGS
 #undef PS_FRAG
-#undef PS_ISSUE
 #undef PS_SA
 #undef PS_SB
 #undef PS_SS
