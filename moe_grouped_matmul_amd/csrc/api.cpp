@@ -319,8 +319,15 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  // 128-row tiles: each tile lies inside one 128-row aligned expert segment
-  const bool lds = fits_32bit(M_total, N, K);
+  // 128 x 256 tiles: each tile lies inside one 128-row aligned expert
+  // segment.  The persistent kernel needs its 32-bit offsets to fit and each
+  // workgroup's tiles to fit its table of tile experts.
+  const int64_t ptiles = ceil_div(M_total, 128) * ceil_div(N, 256);
+  const int ecus = effective_cus(cus);
+  const int pgrid = (int)(ptiles < ecus ? ptiles : ecus);
+  const bool persist = fits_persistent(1, M_total, N, K) && fits_persistent(G, 0, N, K) &&
+                       ceil_div(ptiles, pgrid) <= dg::kPersistentMaxContigTiles;
+  const bool lds = persist || fits_32bit(M_total, N, K);
   const int bm = 128;
   const int bn = lds ? 256 : 128;
   dg::GemmParams p{};
@@ -339,10 +346,20 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.splits = 1;
   p.kb_per_split = (int)(K / 128);
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d\n", (long long)M_total,
-                 (long long)N, (long long)K, (long long)G, bm, bn);
-  const hipError_t e = lds ? dg::launch_gemm_lds(dg::kContiguous, dg::kLds128x256, p, static_cast<hipStream_t>(stream))
-                           : dg::launch_gemm(dg::kContiguous, dg::kTile128x128, p, 1, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d kernel=%s\n", (long long)M_total,
+                 (long long)N, (long long)K, (long long)G, bm, bn, persist ? "persistent" : "grid");
+  hipError_t e;
+  if (persist) {
+    p.dp_tiles = (int)ptiles;  // every tile whole: no K-split tail, no workspace
+    p.sk_tiles = 0;
+    p.sk_pieces = 1;
+    p.sk_kb = (int)(K / 128);
+    e = dg::launch_gemm_persistent(dg::kContiguous, pgrid, p, static_cast<hipStream_t>(stream));
+  } else if (lds) {
+    e = dg::launch_gemm_lds(dg::kContiguous, dg::kLds128x256, p, static_cast<hipStream_t>(stream));
+  } else {
+    e = dg::launch_gemm(dg::kContiguous, dg::kTile128x128, p, 1, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -391,7 +408,8 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   hipError_t e;
   if (persist) {
     const int64_t tiles = G * p.m_tiles * p.n_tiles;
-    e = dg::launch_gemm_persistent(dg::kMasked, (int)(tiles < cus ? tiles : effective_cus(cus)), p,
+    const int ecus = effective_cus(cus);
+    e = dg::launch_gemm_persistent(dg::kMasked, (int)(tiles < ecus ? tiles : ecus), p,
                                    static_cast<hipStream_t>(stream));
   } else if (lds) {
     e = dg::launch_gemm_lds(dg::kMasked, cfg, p, static_cast<hipStream_t>(stream));

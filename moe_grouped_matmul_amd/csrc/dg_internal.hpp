@@ -65,11 +65,14 @@ hipError_t launch_gemm_skinny(int bm, int wn, const GemmParams& p, hipStream_t s
 // multiple of it (padding blocks read as zeros), so splits should be multiples
 constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? (wn == 16 ? 8 : 4) : (wn == 16 ? 6 : 4); }
 
-// Enqueue the persistent 256x128-tile kernel (gemm_persist.hip) with `grid`
-// workgroups (one per CU): mode kDense (tail tiles split along K when
+// Enqueue the persistent kernel (gemm_persist.hip) with `grid` workgroups (one
+// per CU): mode kDense over 256x128 tiles (tail tiles split along K when
 // p.sk_tiles > 0, p.ws then holds persistent_workspace_bytes(...) bytes whose
-// counters must be zero on entry and are left zero) or kMasked (G <= 1024).
-// A, B, sfa and D of all groups are addressed with 32-bit offsets.
+// counters must be zero on entry and are left zero), kContiguous over 128x256
+// tiles (p.dp_tiles = all tiles, no split; at most kPersistentMaxContigTiles
+// tiles per workgroup) or kMasked over 256x128 tiles (G <= 1024).  A, B, sfa
+// and D of all groups are addressed with 32-bit offsets.
+constexpr int kPersistentMaxContigTiles = 64;
 size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces);
 hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream);
 

@@ -1,8 +1,9 @@
 // Persistent block-scaled FP8 GEMM for gfx950: one 512-thread workgroup per
-// CU walks a list of 256 x 128 output tiles with one continuous LDS ring, so
-// the next tile's first K blocks load while the current tile finishes and
-// stores.  Used for the dense form with M > 128 and for the M-grouped masked
-// form.
+// CU walks a list of output tiles (256 x 128; 128 x 256 for the contiguous
+// form, whose aligned 128-row blocks each belong to one expert) with one
+// continuous LDS ring, so the next tile's first K blocks load while the
+// current tile finishes and stores.  Used for the dense form with M > 128 and
+// for the two M-grouped forms.
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: for every 128-wide K block the fp8 partial product of
@@ -18,6 +19,11 @@
 //     (coherent across XCDs) and the last piece of a tile to finish (agent-
 //     scope counter) sums the partials in piece order and writes bf16, so the
 //     result does not depend on the order in which pieces finish;
+//   * contiguous (Lesson 13, Fig. 13-3, contiguous layout): tiles as for
+//     dense; at start every workgroup reduces m_indices over the 128 rows of
+//     each of its tiles to the tile's expert (the largest index in [0, G)) and
+//     a mask of the rows tagged with it, kept in LDS: B and beta come from
+//     that expert, and only the masked rows are stored;
 //   * masked (Lesson 13, Fig. 13-3, masked layout): every workgroup reads
 //     masked_m on the device and builds the prefix sums of the active tiles
 //     per group, sum_g ceil(masked_m[g] / 256) * ceil(N / 128); task ids are
@@ -45,6 +51,7 @@ constexpr int kRsrcWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 family
 constexpr int kCoherent = 16;              // sc1: coherent across the XCDs' L2 caches
 constexpr uint32_t kOOB = 0xFFFFFF00u;     // an offset past every buffer range used here
 constexpr int kMaxMaskedGroups = 1024;     // groups the masked task list supports
+constexpr int kMaxContigSegs = kPersistentMaxContigTiles;  // tiles per workgroup the contiguous table holds
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -54,7 +61,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 
 // One segment of a workgroup's work: K blocks [kb_lo, kb_hi) of one tile.
 struct Seg {
-  int mt, nt, grp;   // row tile, column tile, group (masked)
+  int mt, nt, grp;   // row tile, column tile, group of A/alpha/D rows (masked)
+  int bgrp;          // group of B/beta (masked: grp; contiguous: the tile's expert)
   int row_limit;     // rows of the tile that exist (masked: below masked_m)
   int kb_lo, kb_hi;
   int tail;          // -1: whole tile; else index of a K-split tail tile
@@ -64,8 +72,8 @@ struct Seg {
 template <int MODE>
 __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int WGM = 4;
-  constexpr int WGN = 2;
+  constexpr int WGM = MODE == kContiguous ? 2 : 4;
+  constexpr int WGN = MODE == kContiguous ? 4 : 2;
   constexpr int TM = 4;
   constexpr int TN = 4;
   constexpr int BM = WGM * 64;
@@ -87,6 +95,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[SLOT_BYTES];
   __shared__ int pref[MODE == kMasked ? kMaxMaskedGroups + 1 : 1];  // active tiles before each group
   __shared__ int mmv[MODE == kMasked ? kMaxMaskedGroups : 1];       // masked_m clamped to [0, max_m]
+  // contiguous: expert of each of this workgroup's tiles (-1: none) and the
+  // mask of its rows tagged with that expert
+  __shared__ int seg_exp[MODE == kContiguous ? kMaxContigSegs : 1];
+  __shared__ uint32_t seg_mask[MODE == kContiguous ? kMaxContigSegs : 1][4];
   __shared__ int last_piece;
 
   const int tid = threadIdx.x;
@@ -103,7 +115,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int KB = K >> 7;
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;  // dense: M; masked: max_m
-  const int ngrp = MODE == kMasked ? p.G : 1;
+  const int ngrp = MODE == kMasked ? p.G : 1;         // groups of A, alpha and D rows
+  const int nbgrp = MODE == kDense ? 1 : p.G;          // groups of B and beta
 
   // ---- task list
   int T;  // tasks: dense tiles / active masked tiles
@@ -141,9 +154,40 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int nseg = n_dp + (has_tail ? 1 : 0);
   if (nseg == 0) return;  // uniform over the workgroup
 
+  if constexpr (MODE == kContiguous) {
+    // expert and tagged-row mask of each of this workgroup's tiles (the host
+    // keeps nseg <= kMaxContigSegs); one wave per tile, two rows per lane
+    for (int s = wave; s < nseg; s += NWAVES) {
+      int mt, nt;
+      grouped_mn(xcd_tile(b + s * G, T), p.m_tiles, p.n_tiles, GM, &mt, &nt);
+      const int r0 = mt * BM;
+      const int lim = rows - r0 < BM ? rows - r0 : BM;
+      const int v0 = lane < lim ? p.index[r0 + lane] : -1;
+      const int v1 = lane + 64 < lim ? p.index[r0 + 64 + lane] : -1;
+      int e = v0 >= 0 && v0 < p.G ? v0 : -1;
+      if (v1 >= 0 && v1 < p.G && v1 > e) e = v1;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const int o = __shfl_xor(e, off);
+        e = o > e ? o : e;
+      }
+      const unsigned long long m0 = __ballot(e >= 0 && v0 == e);
+      const unsigned long long m1 = __ballot(e >= 0 && v1 == e);
+      if (lane == 0) {
+        seg_exp[s] = e;
+        seg_mask[s][0] = (uint32_t)m0;
+        seg_mask[s][1] = (uint32_t)(m0 >> 32);
+        seg_mask[s][2] = (uint32_t)m1;
+        seg_mask[s][3] = (uint32_t)(m1 >> 32);
+      }
+    }
+    __syncthreads();
+  }
+
   auto seg_of = [&](int s) -> Seg {
     Seg r;
     r.grp = 0;
+    r.bgrp = 0;
     r.tail = -1;
     r.piece = 0;
     r.kb_lo = 0;
@@ -166,6 +210,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         else hi = mid - 1;
       }
       r.grp = __builtin_amdgcn_readfirstlane(lo);
+      r.bgrp = r.grp;
       const int local = d - __builtin_amdgcn_readfirstlane(pref[r.grp]);
       r.mt = local / p.n_tiles;
       r.nt = local - r.mt * p.n_tiles;
@@ -174,13 +219,18 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     } else {
       grouped_mn(xcd_tile(d, T), p.m_tiles, p.n_tiles, GM, &r.mt, &r.nt);
       r.row_limit = rows - r.mt * BM < BM ? rows - r.mt * BM : BM;
+      if (MODE == kContiguous) {
+        const int e = __builtin_amdgcn_readfirstlane(seg_exp[s]);
+        r.bgrp = e < 0 ? 0 : e;
+        if (e < 0) r.row_limit = 0;  // no row tagged with an expert: nothing loaded or stored
+      }
     }
     return r;
   };
 
   // ---- buffer resources over whole arrays (all groups); offsets are 32-bit
   const uint32_t a_bytes = (uint32_t)(ngrp * rows) * (uint32_t)K;
-  const uint32_t b_bytes = (uint32_t)(ngrp * N) * (uint32_t)K;
+  const uint32_t b_bytes = (uint32_t)(nbgrp * N) * (uint32_t)K;
   const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u;
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
 
@@ -215,7 +265,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   uint32_t is_soff;
   auto is_setup = [&]() {
     const int arow = is_t.grp * rows + is_t.mt * BM;
-    const int brow = is_t.grp * N + is_t.nt * BN;
+    const int brow = is_t.bgrp * N + is_t.nt * BN;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int r = 64 * i + a_loc;
@@ -286,7 +336,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   auto cp_setup = [&]() {
     int nblk = (cp_t.nt * BN + wn * 64) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
-    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_t.grp * NB + nblk) * KB);
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_t.bgrp * NB + nblk) * KB);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
@@ -312,19 +362,25 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // the tile.
   bool pend = false;
   int st_row0 = 0, st_col0 = 0, st_rows = 0;
+  uint32_t st_m[4] = {~0u, ~0u, ~0u, ~0u};  // contiguous: rows tagged with the tile's expert
 #define PS_MARK_TILE()                                                                                     \
   do {                                                                                                     \
     st_row0 = cp_t.grp * rows + cp_t.mt * BM;                                                              \
     st_col0 = cp_t.nt * BN;                                                                                \
     st_rows = cp_t.row_limit;                                                                              \
+    if (MODE == kContiguous) {                                                                             \
+      _Pragma("unroll") for (int w_ = 0; w_ < 4; ++w_) st_m[w_] = __builtin_amdgcn_readfirstlane(seg_mask[cp_seg][w_]); \
+    }                                                                                                      \
   } while (0)
 #define PS_STORE_U()                                                                                       \
   do {                                                                                                     \
     const int gc0_ = st_col0 + wn * 64 + q * 16;                                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
       const int r_ = wm * 64 + i_ * 16 + q16;                                                              \
-      const uint32_t off_ =                                                                                \
-          (r_ < st_rows && gc0_ < N) ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u : kOOB;        \
+      const bool tag_ = MODE != kContiguous || ((st_m[r_ >> 5] >> (r_ & 31)) & 1u);                        \
+      const uint32_t off_ = (r_ < st_rows && gc0_ < N && tag_)                                             \
+                                ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u                     \
+                                : kOOB;                                                                    \
       uint32_t w_[8];                                                                                      \
       _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                  \
         w_[2 * j_] = pack_bf16x2(u[i_][j_][0], u[i_][j_][1]);                                              \
@@ -568,6 +624,8 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
   if (grid <= 0) return hipSuccess;
   if (mode == kMasked)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kContiguous)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();

@@ -300,3 +300,67 @@ def test_masked_graph_replay_with_device_side_counts():
             valid[g, :m] = True
         assert np.array_equal(got[~valid], ref[~valid]), counts
         assert_close(got[valid], ref[valid], f"graph replay {counts}")
+
+
+# ---------------------------------------------------------------- few workgroups, many tiles each
+
+@pytest.fixture
+def few_cus():
+    """Cap the persistent kernels at a few workgroups, so each walks many tiles
+    (the LDS ring continues across tiles; a finished tile is stored while the
+    next one computes; in the contiguous form the expert changes between
+    tiles)."""
+    def cap(n):
+        dg.dg_set_num_cus(n)
+    yield cap
+    dg.dg_set_num_cus(0)
+
+
+@pytest.mark.parametrize("cus", [1, 3, 7])
+@pytest.mark.parametrize("M,N,K", [(1000, 528, 512), (777, 400, 384), (2048, 256, 1024)])
+def test_dense_many_tiles_per_workgroup(few_cus, cus, M, N, K):
+    few_cus(cus)
+    a32, b32 = workloads.dense(M, N, K, seed=M + N + cus)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    for ws in (True, False):  # with a workspace the partial last round is split along K
+        assert_close(_gpu_dense(qa, sa, qb, sb, M, N, K, ws), ref, f"dense {M}x{N}x{K} on {cus} CUs")
+
+
+@pytest.mark.parametrize("cus", [1, 4])
+@pytest.mark.parametrize("counts,N,K", [([130, 5, 300, 1, 256], 400, 384), ([128, 0, 900, 77], 528, 256)])
+def test_contiguous_many_tiles_per_workgroup(few_cus, cus, counts, N, K):
+    few_cus(cus)
+    G = len(counts)
+    w, qa, sa, qb, sb = _contig_small(counts, G, N, K, seed=sum(counts) + cus)
+    idx = w["m_indices"].copy()
+    idx[1] = G + 3  # out of range: untouched
+    D = _sentinel(w["m_total"], N)
+    dg.dg_m_grouped_fp8_gemm_nt_contiguous(_t(qa), _t(sa), _t(qb), _t(sb), D, _t(idx))
+    got = _np(D)
+    ref = oracle.grouped_contiguous(qa, sa, qb, sb, idx, np.full((w["m_total"], N), SENTINEL, np.uint16))
+    bad = (idx < 0) | (idx >= G)
+    assert np.array_equal(got[bad], ref[bad])
+    assert np.all(got[bad] == SENTINEL)
+    assert_close(got[~bad], ref[~bad], f"contiguous on {cus} CUs")
+
+
+@pytest.mark.parametrize("cus", [1, 5])
+def test_masked_many_tiles_per_workgroup(few_cus, cus):
+    few_cus(cus)
+    mm, max_m, N, K = [256, 3, 0, 200, 129, 256], 256, 400, 384
+    G = len(mm)
+    w = workloads.masked(G, max_m, N, K, seed=cus + 11, masked_m=mm)
+    qa, sa = oracle.quant_1x128(w["a"])
+    qa, sa = masked_layout(qa, sa, w["rows"], G, max_m)
+    qb, sb = oracle.quant_128x128(w["b"])
+    D = _sentinel(G, max_m, N)
+    dg.dg_m_grouped_fp8_gemm_nt_masked(_t(qa), _t(sa), _t(qb), _t(sb), D, _t(w["masked_m"]))
+    got = _np(D)
+    ref = oracle.grouped_masked(qa, sa, qb, sb, w["masked_m"], np.full((G, max_m, N), SENTINEL, np.uint16))
+    valid = np.zeros((G, max_m), bool)
+    for g, m in enumerate(mm):
+        valid[g, :m] = True
+    assert np.array_equal(got[~valid], ref[~valid])
+    assert_close(got[valid], ref[valid], f"masked on {cus} CUs")
