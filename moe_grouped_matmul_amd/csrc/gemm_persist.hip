@@ -591,15 +591,23 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #define PS_LDP(pc_, i_, j_)                                                                                \
   __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(                                         \
                                 rw, w_off + (uint32_t)((i_) * TN + (j_)) * 1024u, (uint32_t)(pc_) * tile_bytes, kCoherent))
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) u[i][j] = PS_LDP(0, i, j);
-    for (int pc = 1; pc < P; ++pc) {
+    // two pieces' loads in flight at a time, added in piece order
+    for (int pc0 = 0; pc0 < P; pc0 += 2) {
+      f32x4 t0[TM][TN], t1[TM][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) u[i][j] += PS_LDP(pc, i, j);
+        for (int j = 0; j < TN; ++j) {
+          t0[i][j] = PS_LDP(pc0, i, j);
+          if (pc0 + 1 < P) t1[i][j] = PS_LDP(pc0 + 1, i, j);
+        }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          u[i][j] = pc0 == 0 ? t0[i][j] : u[i][j] + t0[i][j];
+          if (pc0 + 1 < P) u[i][j] += t1[i][j];
+        }
     }
 #undef PS_LDP
     if (tid == 0)  // ready for the next call on this workspace

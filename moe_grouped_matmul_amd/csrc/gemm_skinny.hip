@@ -300,34 +300,31 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
                    (unsigned int)(S - 1);
     __syncthreads();
     if (!last_split) return;
-    // sum of the splits' fragments in split order, into acc
 #define SK_LDP(s_, i_, j_)                                                                                 \
   __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(                                         \
                                 rw, w_off + (uint32_t)((i_) * TN + (j_)) * 1024u, (uint32_t)(s_) * split_bytes, kCoherent))
+    // sum of the splits' fragments in split order, into acc: the loads of up
+    // to SB splits are in flight at once (one round trip per batch), the
+    // additions keep the order 0, 1, 2, ...
+    constexpr int SB = TM * TN <= 4 ? 8 : (TM * TN <= 8 ? 4 : 2);
+    for (int k0 = 0; k0 < S; k0 += SB) {
+      f32x4 t[SB][TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int b = 0; b < SB; ++b)
+        if (k0 + b < S) {
 #pragma unroll
-      for (int jj = 0; jj < TN; ++jj) acc[i][jj] = SK_LDP(0, i, jj);
-    int k = 1;
-    for (; k + 1 < S; k += 2) {  // two splits' loads in flight, added in order
-      f32x4 t0[TM][TN], t1[TM][TN];
+          for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < TN; ++jj) {
-          t0[i][jj] = SK_LDP(k, i, jj);
-          t1[i][jj] = SK_LDP(k + 1, i, jj);
+            for (int jj = 0; jj < TN; ++jj) t[b][i][jj] = SK_LDP(k0 + b, i, jj);
         }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int b = 0; b < SB; ++b)
+        if (k0 + b < S) {
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj) acc[i][jj] = (acc[i][jj] + t0[i][jj]) + t1[i][jj];
-    }
-    if (k < S) {
+          for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < TN; ++jj) acc[i][jj] += SK_LDP(k, i, jj);
+            for (int jj = 0; jj < TN; ++jj) acc[i][jj] = (k0 + b == 0) ? t[b][i][jj] : acc[i][jj] + t[b][i][jj];
+        }
     }
 #undef SK_LDP
     if (tid == 0)  // ready for the next call on this workspace
