@@ -82,6 +82,39 @@ def test_quant_1x128_rounding_ties_and_subnormals():
     assert np.array_equal(_np(q), qr)
 
 
+def test_quant_1x128_near_rounding_midpoints():
+    # scales other than 1 and values within a few ulps of e4m3 rounding
+    # midpoints times the scale: x * (1 / alpha) and fl32(x / alpha) can then
+    # fall on different sides of a midpoint, so the kernel must take the exact
+    # quotient there to match the oracle's bytes
+    rng = np.random.default_rng(11)
+    rows = []
+    for c in (3.0, 5.0, 0.3, 7e-3, 1.7e5, 1.0 / 3.0):
+        amax = np.float32(448.0 * c)
+        alpha = np.float32(amax / np.float32(448.0))
+        row = [amax]
+        while len(row) < 128:
+            e = int(rng.integers(-5, 8))
+            k = int(rng.integers(0, 8))
+            mid = np.float32((1.0 + (2 * k + 1) / 16.0) * 2.0 ** e)  # halfway between two e4m3 codes
+            x = np.float32(mid * alpha)
+            for j in range(-3, 4):
+                v = x
+                step = np.float32(np.inf) if j > 0 else np.float32(-np.inf)
+                for _ in range(abs(j)):
+                    v = np.nextafter(v, step, dtype=np.float32)
+                if abs(v) < amax and len(row) < 128:
+                    row.append(v if rng.random() < 0.5 else -v)
+        rows.append(row)
+    x = np.array(rows, np.float32)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    s = torch.empty((1, x.shape[0]), dtype=torch.float32, device=DEV)
+    dg.dg_quant_1x128(_t(x), q, s)
+    qr, sr = oracle.quant_1x128(x)
+    assert np.array_equal(_np(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(_np(q), qr)
+
+
 @pytest.mark.parametrize("G,N,K", [(1, 16, 128), (1, 200, 384), (2, 136, 256), (1, 2112, 1024)])
 def test_quant_128x128_bit_exact(G, N, K):
     rng = np.random.default_rng(N + K)
