@@ -32,6 +32,7 @@ sign of zero codes -- are marked "parity unpinned" where they are defined.
 from .e4m3 import E4M3_MAX, decode_e4m3, encode_e4m3
 from .bf16 import bf16_rne_bits, bf16_bits_to_f64
 from .quant import quant_1x128, quant_128x128
+from .gemm_bf16 import gemm_bf16_nt
 from .gemm import (
     gemm_nt_acc,
     gemm_nt,
@@ -51,4 +52,5 @@ __all__ = [
     "gemm_nt",
     "grouped_contiguous",
     "grouped_masked",
+    "gemm_bf16_nt",
 ]

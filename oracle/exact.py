@@ -89,3 +89,30 @@ def gemm_nt_exact(a_codes, sfa, b_codes, sfb):
             out[i, j] = bf16_bits_from_fraction(total)
         exact.append(row)
     return exact, out
+
+
+def bf16_fraction(bits: int) -> Fraction:
+    """Exact value of a finite bf16 bit pattern, from the format definition
+    (1 sign, 8 exponent bits with bias 127, 7 mantissa bits, subnormals)."""
+    sign = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    assert e != 0xFF, "inf/nan have no rational value"
+    if e == 0:
+        return sign * Fraction(m, 128) * Fraction(2) ** -126
+    return sign * (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+
+
+def gemm_bf16_nt_exact(a_bits, b_bits):
+    """Exact sum of products of bf16 operands, rounded once to bf16 (bits)."""
+    a_bits = np.asarray(a_bits, dtype=np.uint16)
+    b_bits = np.asarray(b_bits, dtype=np.uint16)
+    M, K = a_bits.shape
+    N = b_bits.shape[0]
+    A = [[bf16_fraction(int(c)) for c in row] for row in a_bits]
+    B = [[bf16_fraction(int(c)) for c in row] for row in b_bits]
+    out = np.zeros((M, N), dtype=np.uint16)
+    for i in range(M):
+        for j in range(N):
+            out[i, j] = bf16_bits_from_fraction(sum(A[i][k] * B[j][k] for k in range(K)))
+    return out
