@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published, no sparsity)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA (published, no sparsity)
 ROTATE_BYTES = 768 << 20  # per-shape rotation footprint (3x the 256 MB MALL)
 CPU_SAMPLE_ROWS = 2048  # rows per shape in the CPU-oracle baseline sample
 COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
@@ -104,7 +105,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -406,6 +407,57 @@ def cpu_baseline(shapes, workloads):
                        "weights pre-quantised untimed")
 
 
+def run_bf16(args, torch, dg, workloads):
+    """BF16 dense GEMM 4096 x 7168 x 16384 (the second dense workload the
+    pages measure): one step = one call over one of the rotating buffer sets."""
+    dev = torch.device("cuda:0")
+    M, N, K = 4096, 7168, 16384
+    a, b = workloads.dense_bf16(M, N, K, seed=500)
+    A = torch.from_numpy(a.view(np.int16)).to(dev)
+    B = torch.from_numpy(b.view(np.int16)).to(dev)
+    per_set = 2 * (M * K + N * K + M * N)
+    nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+    sets = [dict(a=A if i == 0 else A.clone(), b=B if i == 0 else B.clone(),
+                 d=torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for i in range(nsets)]
+    wsz = dg.dg_get_workspace_size(dg.DG_OP_BF16_GEMM_NT, M, N, K, 1)
+    ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
+    timer = Timer(torch)
+
+    def step(i):
+        st = sets[i % nsets]
+        dg.dg_bf16_gemm_nt(st["a"], st["b"], st["d"], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = [capture(torch, lambda i=i: step(i)) for i in range(nsets)]
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    t0 = timer.ev()
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % nsets].replay()
+    t1 = timer.ev()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    del graphs
+    flops = 2.0 * M * N * K
+    nbytes = 2.0 * (M * K + N * K + M * N)
+    us = ms_per_step * 1e3
+    achieved = flops / us / 1e6
+    roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None, kernel="fp8_gemm_persistent_kernel<bf16>",
+                launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
+                algorithmic_flops_per_launch=round(flops))
+    per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1),
+                      gbs=round(nbytes / us / 1e3, 1), bound="mfma",
+                      roof_frac=round(max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6 / us, 4),
+                      kernel="fp8_gemm_persistent_kernel<bf16>")]
+    config = dict(workload="dense_bf16_nt_4096x7168x16384", shapes=[f"{M}x{N}x{K}"], out="bf16",
+                  step="dg_bf16_gemm_nt", cold_hbm=True)
+    return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],
+                config=config)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -436,6 +488,10 @@ def main():
         config = dict(workload=name, shapes=[f"{m}x{n}x{k}" for m, n, k in r["shapes"]],
                       scales="1x128 activations, 128x128 weights, fp32", out="bf16",
                       step="dg_quant_1x128 + dg_fp8_gemm_nt per shape", cold_hbm=True)
+    elif args.workload == "bf16":
+        r = run_bf16(args, torch, dg, workloads)
+        name = r["name"]
+        config = r["config"]
     else:
         r = run_grouped(args, torch, dg, workloads)
         name = r["name"]
@@ -453,8 +509,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
-        "data": "synthetic (seeded DeepSeek-V3-shaped fp32 sources, quantised on device)",
+        "dtype": "bf16" if args.workload == "bf16" else "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) / N(0,1/K) bf16 operands)" if args.workload == "bf16" else
+                "synthetic (seeded DeepSeek-V3-shaped fp32 sources, quantised on device)",
         "config": config,
         "per_shape": r["per_shape"],
         "roofline": r["roofline"],

@@ -53,7 +53,7 @@ extern "C" {
 enum {
   DG_OK = 0,
   DG_ERR_INVALID_ARG = 1, /* null pointer, bad enum value */
-  DG_ERR_SHAPE = 2,       /* K % 128, N % 16, negative sizes, G out of range */
+  DG_ERR_SHAPE = 2,       /* K % 128 (K % 64 for bf16), N % 16, negative sizes, G out of range */
   DG_ERR_ALIGN = 3,       /* pointer alignment */
   DG_ERR_WORKSPACE = 4,   /* workspace pointer given with a size that is not a multiple of 4 */
   DG_ERR_DEVICE = 5,      /* no HIP device, or the current device is not gfx950 */
@@ -61,7 +61,7 @@ enum {
 };
 
 /* Operation ids for dg_get_workspace_size. */
-enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2 };
+enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2, DG_OP_BF16_GEMM_NT = 3 };
 
 /*
  * Dense GEMM.  Lesson 13, Fig. 13-1; DeepGEMM's "normal" GEMM (the Feb-2025
@@ -124,6 +124,21 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
                                     int64_t G, int64_t max_m, int64_t N, int64_t K,
                                     int64_t expected_m, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * BF16 dense GEMM, D = A . B^T, no scales.  BF16 is among the library's
+ * precisions (deep-dive blog, section 1 overview table); the Ascend 950
+ * article (benchmarks section) measures this GEMM at M=4096, N=7168, K=16384.
+ *   A [M,K] bf16, row-major      B [N,K] bf16, row-major
+ *   D [M,N] bf16, row-major (written); fp32 accumulation, round-to-nearest-even
+ * K must be a multiple of 64, N of 16.  workspace: as for dg_fp8_gemm_nt
+ * (optional, lets a partial last round of tiles split along K; size from
+ * dg_get_workspace_size(DG_OP_BF16_GEMM_NT, M, N, K, 1); zero-filled before
+ * first use, left reusable).  Problems whose byte offsets exceed 32 bits are
+ * rejected with DG_ERR_SHAPE.
+ */
+int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * 1x128 activation quantiser.  Lesson 13, Fig. 13-1 (one scale per token per

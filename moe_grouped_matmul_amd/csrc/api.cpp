@@ -302,6 +302,52 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   return ok();
 }
 
+int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (K <= 0 || K % 64 != 0) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 64 (got %lld)", (long long)K);
+  if (N <= 0 || N % 16 != 0) return fail(DG_ERR_SHAPE, "N must be a positive multiple of 16 (got %lld)", (long long)N);
+  if (K > (int64_t)1 << 29 || N > (int64_t)1 << 30) return fail(DG_ERR_SHAPE, "N or K too large");
+  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if (M == 0) return ok();
+  if (!A || !B || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16))
+    return fail(DG_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
+    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
+  int rc = 0;
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  // the persistent kernel's schedule over K blocks of 128 bytes (64 bf16)
+  if (!fits_persistent(1, M, N, 2 * K)) return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
+  DensePlan pl;
+  plan_persistent(pl, M, N, 2 * K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  dg::GemmParams p{};
+  p.A = reinterpret_cast<const uint8_t*>(A);
+  p.B = reinterpret_cast<const uint8_t*>(B);
+  p.D = D;
+  p.ws = static_cast<float*>(workspace);
+  p.rows = M;
+  p.N = (int)N;
+  p.K = (int)K;  // elements; the kernel addresses rows of 2 K bytes
+  p.G = 1;
+  p.m_tiles = pl.m_tiles;
+  p.n_tiles = pl.n_tiles;
+  p.splits = 1;
+  p.kb_per_split = pl.kb_per_split;
+  p.dp_tiles = pl.dp_tiles;
+  p.sk_tiles = pl.sk_tiles;
+  p.sk_pieces = pl.sk_pieces;
+  p.sk_kb = pl.sk_kb;
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] bf16_gemm_nt M=%lld N=%lld K=%lld grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                 (long long)M, (long long)N, (long long)K, pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
+                 pl.sk_pieces, pl.sk_kb);
+  const hipError_t e = dg::launch_gemm_persistent(dg::kDenseBf16, pl.grid, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                                         uint16_t* D, const int32_t* m_indices, int64_t M_total, int64_t N,
                                         int64_t K, int64_t G, void* workspace, size_t workspace_bytes,
@@ -456,8 +502,8 @@ int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t 
 
 size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G) {
   (void)G;
-  if (op != DG_OP_GEMM_NT) return 0;
-  if (rows <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+  if (op != DG_OP_GEMM_NT && op != DG_OP_BF16_GEMM_NT) return 0;
+  if (rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128)) return 0;
   int cus = 0;
   int dev = -1;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
@@ -466,6 +512,12 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   }
   (void)hipGetLastError();
   if (cus <= 0) cus = 256;
+  if (op == DG_OP_BF16_GEMM_NT) {
+    if (!fits_persistent(1, rows, N, 2 * K)) return 0;
+    DensePlan pb;
+    plan_persistent(pb, rows, N, 2 * K, effective_cus(cus), (size_t)-1);
+    return (dg::persistent_workspace_bytes(pb.sk_tiles, pb.sk_pieces) + 15) / 16 * 16;
+  }
   const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1);
   if (pl.persist) return (dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces) + 15) / 16 * 16;
   if (pl.splits <= 1) return 0;

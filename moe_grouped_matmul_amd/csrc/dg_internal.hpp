@@ -32,7 +32,9 @@ struct GemmParams {
   int sk_kb;
 };
 
-enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kDenseBf16: the dense schedule over bf16 operands (no scales): a K block
+// is 64 bf16 = 128 bytes per row, the same LDS row as an fp8 K block.
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3 };
 
 // Tile configurations compiled for gfx950 (workgroup tile BM x BN, K step 128).
 enum TileCfg { kTile128x128 = 0, kTile64x128 = 1, kTile64x64 = 2, kNumTileCfgs = 3 };

@@ -1,4 +1,5 @@
-// Persistent block-scaled FP8 GEMM for gfx950: one 512-thread workgroup per
+// Persistent block-scaled FP8 GEMM for gfx950 (and, in mode kDenseBf16, the
+// plain BF16 GEMM on the same schedule): one 512-thread workgroup per
 // CU walks a list of output tiles (256 x 128; 128 x 256 for the contiguous
 // form, whose aligned 128-row blocks each belong to one expert) with one
 // continuous LDS ring, so the next tile's first K blocks load while the
@@ -54,6 +55,8 @@ constexpr int kMaxMaskedGroups = 1024;     // groups the masked task list suppor
 constexpr int kMaxContigSegs = kPersistentMaxContigTiles;  // tiles per workgroup the contiguous table holds
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
@@ -72,6 +75,7 @@ struct Seg {
 template <int MODE>
 __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
   constexpr int WGM = MODE == kContiguous ? 2 : 4;
   constexpr int WGN = MODE == kContiguous ? 4 : 2;
   constexpr int TM = 4;
@@ -81,7 +85,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   constexpr int NWAVES = 8;
   constexpr int A_INS = BM / 8 / NWAVES;  // 1 KB (8-row) loads per wave per K block
   constexpr int B_INS = BN / 8 / NWAVES;
-  constexpr int L_BLOCK = A_INS + B_INS + 1;  // + one alpha load per wave
+  constexpr int L_BLOCK = A_INS + B_INS + (BF16 ? 0 : 1);  // + one alpha load per wave
   constexpr int GM = 4;                       // m-tiles per tile group
   static_assert(2 * L_BLOCK < 64, "vmcnt range");
 
@@ -110,7 +114,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int b = (int)blockIdx.x;
   const int G = (int)gridDim.x;
 
-  const int K = p.K;
+  const int K = BF16 ? 2 * p.K : p.K;  // bytes per operand row
   const int N = p.N;
   const int KB = K >> 7;
   const int NB = (N + 127) >> 7;
@@ -150,7 +154,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int dp_tiles = MODE == kMasked ? T : p.dp_tiles;  // tasks run as whole tiles
   const int P = p.sk_pieces;                               // pieces per tail tile (dense)
   const int n_dp = b < dp_tiles ? (dp_tiles - b + G - 1) / G : 0;
-  const bool has_tail = MODE == kDense && b < p.sk_tiles * P;
+  const bool has_tail = (MODE == kDense || BF16) && b < p.sk_tiles * P;
   const int nseg = n_dp + (has_tail ? 1 : 0);
   if (nseg == 0) return;  // uniform over the workgroup
 
@@ -406,9 +410,49 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     const uint8_t* bs_ = PS_SB(st_) + b_row0;                                                              \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
       PS_FRAG(AF[i_], as_, i_ * 2048);                                                                     \
-      AL[i_] = PS_SS(st_)[wm * 64 + i_ * 16 + q16];                                                        \
+      AL[i_] = BF16 ? 1.f : PS_SS(st_)[wm * 64 + i_ * 16 + q16];                                           \
     }                                                                                                      \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) PS_FRAG(BF[j_], bs_, j_ * 2048);                    \
+  } while (0)
+
+  // BF16 mode: the products of one iteration accumulate straight into u.  A
+  // fragment's 16 bytes at chunk q hold K elements 8 q .. 8 q + 7 of the
+  // block's first 32, those at chunk q + 4 the same of its second 32 (both
+  // operands use the same mapping, so the dot products are the block's), so
+  // each 16x16 tile takes two 16x16x32 bf16 MFMAs: all first halves, then all
+  // second halves (each depends on its first half 16 MFMAs earlier).  The
+  // next iteration's fragment reads and the block's loads are interleaved as
+  // in the FP8 path.
+#define PS_COMPUTE_BF16(st_, AF, BF, AN, BN_)                                                              \
+  do {                                                                                                     \
+    const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                        \
+    uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                    \
+    _Pragma("unroll") for (int k_ = 0; k_ < 2 * TM * TN; ++k_) {                                           \
+      const int t_ = k_ % (TM * TN);                                                                       \
+      const int i_ = t_ % TM;                                                                              \
+      const int j_ = t_ / TM;                                                                              \
+      const i32x4 av_ = k_ < TM * TN ? i32x4{AF[i_][0], AF[i_][1], AF[i_][2], AF[i_][3]}                   \
+                                     : i32x4{AF[i_][4], AF[i_][5], AF[i_][6], AF[i_][7]};                  \
+      const i32x4 bv_ = k_ < TM * TN ? i32x4{BF[j_][0], BF[j_][1], BF[j_][2], BF[j_][3]}                   \
+                                     : i32x4{BF[j_][4], BF[j_][5], BF[j_][6], BF[j_][7]};                  \
+      u[i_][j_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bv_),                \
+                                                         __builtin_bit_cast(bf16x8, av_), u[i_][j_], 0, 0, 0); \
+      if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, k_);                                                            \
+      if (k_ < 2 * (TM + TN)) {                                                                            \
+        const int f_ = k_ >> 1; /* fragment: A 0..TM-1, then B */                                          \
+        const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +        \
+                            ((k_ & 1) ? fr_hi : fr_lo);                                                    \
+        if (k_ & 1) nhi_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                                 \
+        else nlo_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                                        \
+      }                                                                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                                   \
+    }                                                                                                      \
+    _Pragma("unroll") for (int f_ = 0; f_ < TM + TN; ++f_) {                                               \
+      const i32x8 v8_ = i32x8{(int)nlo_[f_].x, (int)nlo_[f_].y, (int)nlo_[f_].z, (int)nlo_[f_].w,          \
+                              (int)nhi_[f_].x, (int)nhi_[f_].y, (int)nhi_[f_].z, (int)nhi_[f_].w};         \
+      if (f_ < TM) AN[f_] = v8_;                                                                           \
+      else BN_[f_ - TM] = v8_;                                                                             \
+    }                                                                                                      \
   } while (0)
 
   // The products and promotions of one iteration, with the next iteration's
@@ -423,7 +467,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   do {                                                                                                     \
     float sc_[TM];                                                                                         \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) sc_[i_] = AL[i_] * beta_;                            \
-    if constexpr (MODE == kMasked) {                                                                       \
+    if constexpr (BF16) {                                                                                  \
+      PS_COMPUTE_BF16(st_, AF, BF, AN, BN_);                                                               \
+      (void)sc_;                                                                                           \
+    } else if constexpr (MODE == kMasked) {                                                                       \
       const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
       uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
@@ -497,7 +544,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #define PS_STEP(st_, jj_, AF, BF, AL, AN, BN_, ALN)                                                        \
   do {                                                                                                     \
     const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = live_ ? sfb_w[cp_kb] : 0.f;                                                        \
+    const float beta_ = BF16 ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                        \
     wait_vmcnt<L_BLOCK>();                                                                                 \
     wait_lgkmcnt0(); /* own reads of this slot done before anyone may refill it */                        \
     __builtin_amdgcn_s_barrier();                                                                          \
@@ -552,6 +599,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 
 #undef PS_STEP
 #undef PS_COMPUTE
+#undef PS_COMPUTE_BF16
 #undef PS_ISSUE
 #undef PS_ISSUE_BEGIN
 #undef PS_ISSUE_LOAD
@@ -632,6 +680,8 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
   if (grid <= 0) return hipSuccess;
   if (mode == kMasked)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kDenseBf16)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else

@@ -28,9 +28,11 @@ DG_ERR_LAUNCH = 6
 DG_OP_GEMM_NT = 0
 DG_OP_CONTIGUOUS = 1
 DG_OP_MASKED = 2
+DG_OP_BF16_GEMM_NT = 3
 
 EXPORTED = (
     "dg_fp8_gemm_nt",
+    "dg_bf16_gemm_nt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
     "dg_quant_1x128",
@@ -66,6 +68,7 @@ def load_library(path=None):
     lib = ctypes.CDLL(p)
     P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
+    lib.dg_bf16_gemm_nt.argtypes = [P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, SZ, P]
     lib.dg_quant_1x128.argtypes = [P, P, P, I64, I64, I64, P]
@@ -77,7 +80,7 @@ def load_library(path=None):
     lib.dg_get_num_cus.argtypes = []
     lib.dg_get_last_error.restype = ctypes.c_char_p
     lib.dg_version.restype = ctypes.c_char_p
-    for name in ("dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
+    for name in ("dg_fp8_gemm_nt", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
                  "dg_quant_1x128", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
                  "dg_get_m_alignment_for_contiguous_layout"):
         getattr(lib, name).restype = I
@@ -170,6 +173,25 @@ def dg_fp8_gemm_nt(A, sfa, B, sfb, D, workspace=None, stream=None):
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().dg_fp8_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), M, N, K,
                                          _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dg_bf16_gemm_nt(A, B, D, workspace=None, stream=None):
+    """D[M,N] (bf16, written) = A[M,K] . B[N,K]^T, all bf16 (int16/uint16 bit views accepted)."""
+    A = _bf16_out(A, "A")
+    B = _bf16_out(B, "B")
+    D = _bf16_out(D)
+    for t, n in ((A, "A"), (B, "B"), (D, "D")):
+        _need(t, n, t.dtype, 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(D.shape) != (M, N):
+        raise ValueError("shape mismatch between A, B, D")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype, workspace.dim())
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().dg_bf16_gemm_nt(_ptr(A), _ptr(B), _ptr(D), M, N, K, _ptr(workspace), ws_bytes,
+                                          _stream(stream)))
 
 
 def dg_m_grouped_fp8_gemm_nt_contiguous(A, sfa, B, sfb, D, m_indices, stream=None):

@@ -138,3 +138,16 @@ def place_rows(codes: np.ndarray, scales: np.ndarray, rows: np.ndarray, total_ro
     out_q[rows] = codes
     out_s[:, rows] = scales
     return out_q, out_s
+
+
+def dense_bf16(M: int, N: int, K: int, seed: int):
+    """BF16 operands (uint16 bit patterns): A ~ N(0, 1), B ~ N(0, 1/K), drawn in
+    fp32 as for the FP8 workloads and cast to bf16 by torch (round to nearest
+    even)."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    b = rng.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))
+    cast = lambda x: torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return cast(a), cast(b)
