@@ -36,6 +36,7 @@ from .gemm_bf16 import gemm_bf16_nt
 from .gemm import (
     gemm_nt_acc,
     gemm_nt,
+    gemm_nt_c,
     grouped_contiguous,
     grouped_masked,
 )
@@ -50,6 +51,7 @@ __all__ = [
     "quant_128x128",
     "gemm_nt_acc",
     "gemm_nt",
+    "gemm_nt_c",
     "grouped_contiguous",
     "grouped_masked",
     "gemm_bf16_nt",

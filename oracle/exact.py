@@ -116,3 +116,39 @@ def gemm_bf16_nt_exact(a_bits, b_bits):
         for j in range(N):
             out[i, j] = bf16_bits_from_fraction(sum(A[i][k] * B[j][k] for k in range(K)))
     return out
+
+
+def f32_from_fraction(x: Fraction) -> np.float32:
+    """Round an exact rational to fp32 (ties to even); +-inf past the range."""
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    v = abs(x)
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    e = max(e, -126)  # below the smallest normal the spacing stays 2^-149
+    q = Fraction(2) ** (e - 23)
+    t = v / q
+    n = t.numerator // t.denominator
+    rem = t - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * q
+    if r >= Fraction(2) ** 128:
+        return np.float32(sign * np.inf)
+    return np.float32(sign * float(r))  # r has <= 24 significant bits: exact in fp64 and fp32
+
+
+def gemm_nt_c_exact(a_codes, sfa, b_codes, sfb, c):
+    """Exact closed form plus C, rounded once to fp32."""
+    exact, _ = gemm_nt_exact(a_codes, sfa, b_codes, sfb)
+    M, N = len(exact), len(exact[0]) if exact else 0
+    out = np.zeros((M, N), dtype=np.float32)
+    for i in range(M):
+        for j in range(N):
+            cc = f32_fraction(c[i][j]) if c is not None else Fraction(0)
+            out[i, j] = f32_from_fraction(exact[i][j] + cc)
+    return out

@@ -22,6 +22,11 @@ Exactness of the fp64 evaluation below:
   relative error ~1e-16 per K block.
 The final bf16 rounding is round-to-nearest-even taken directly from fp64.
 
+Accumulating form ("DeepGEMM architecture deep dive", section 3: every GEMM
+of the library is D = C + A @ B, the NT one D = C + A @ B^T): with an fp32
+input C the output is fp32, D = fl32(C + accumulator), rounded once
+(round-to-nearest-even) from the fp64 sum.
+
 Grouped forms (Lesson 13, Fig. 13-3 and the Q3 answer; deep-dive blog,
 section 3 table): every expert shares N and K.
 * contiguous: rows of all experts are concatenated; row i belongs to expert
@@ -107,3 +112,13 @@ def grouped_masked(a_codes, sfa, b_codes, sfb, masked_m, d_init) -> np.ndarray:
             continue
         d[g, :m] = gemm_nt(a_codes[g, :m], sfa[g][:, :m], b_codes[g], sfb[g])
     return d
+
+
+def gemm_nt_c(a_codes, sfa, b_codes, sfb, c) -> np.ndarray:
+    """fp32 [M, N] of D = C + A . B^T (C fp32 [M, N]; None means zero), one
+    round-to-nearest-even from fp64 (numpy's fp64 -> fp32 cast rounds to
+    nearest even)."""
+    acc = gemm_nt_acc(a_codes, sfa, b_codes, sfb)
+    if c is not None:
+        acc = acc + np.asarray(c, dtype=np.float32).astype(np.float64)
+    return acc.astype(np.float32)
