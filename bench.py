@@ -105,7 +105,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -458,6 +458,64 @@ def run_bf16(args, torch, dg, workloads):
                 config=config)
 
 
+def run_acc(args, torch, dg, workloads):
+    """Accumulating FP8 GEMM D = C + A.B^T (fp32 C, D in place) at
+    4096 x 7168 x 16384: one step = one call over one rotating buffer set."""
+    dev = torch.device("cuda:0")
+    M, N, K = 4096, 7168, 16384
+    a32, b32 = workloads.dense(M, N, K, 200)
+    A32 = torch.from_numpy(a32).to(dev)
+    B32 = torch.from_numpy(b32).to(dev)
+    A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    SA = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    B8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    SB = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=dev)
+    dg.dg_quant_1x128(A32, A8, SA)
+    dg.dg_quant_128x128(B32, B8, SB)
+    del A32, B32
+    per_set = M * K + N * K + 4 * M * N
+    nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+    sets = [dict(a=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(), b=B8 if i == 0 else B8.clone(),
+                 sb=SB if i == 0 else SB.clone(), c=torch.zeros((M, N), dtype=torch.float32, device=dev))
+            for i in range(nsets)]
+    wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
+    ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
+    timer = Timer(torch)
+
+    def step(i):
+        st = sets[i % nsets]
+        dg.dg_fp8_gemm_nt_acc(st["a"], st["sa"], st["b"], st["sb"], st["c"], st["c"], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = [capture(torch, lambda i=i: step(i)) for i in range(nsets)]
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    t0 = timer.ev()
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % nsets].replay()
+    t1 = timer.ev()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    del graphs
+    flops, nbytes = dense_work(M, N, K)
+    nbytes += 6.0 * M * N  # fp32 C read and fp32 D written instead of bf16 D
+    us = ms_per_step * 1e3
+    achieved = flops / us / 1e6
+    roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel="fp8_gemm_persistent_kernel<acc>",
+                launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
+                algorithmic_flops_per_launch=round(flops))
+    per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1), gbs=round(nbytes / us / 1e3, 1),
+                      bound="mfma", roof_frac=round(roof_time_us(flops, nbytes) / us, 4),
+                      kernel="fp8_gemm_persistent_kernel<acc>")]
+    config = dict(workload="dense_fp8_nt_acc_4096x7168x16384", shapes=[f"{M}x{N}x{K}"], out="fp32 D = C + A.B^T",
+                  step="dg_fp8_gemm_nt_acc (C = D, in place)", cold_hbm=True)
+    return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],
+                config=config)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -488,8 +546,8 @@ def main():
         config = dict(workload=name, shapes=[f"{m}x{n}x{k}" for m, n, k in r["shapes"]],
                       scales="1x128 activations, 128x128 weights, fp32", out="bf16",
                       step="dg_quant_1x128 + dg_fp8_gemm_nt per shape", cold_hbm=True)
-    elif args.workload == "bf16":
-        r = run_bf16(args, torch, dg, workloads)
+    elif args.workload in ("bf16", "acc"):
+        r = (run_bf16 if args.workload == "bf16" else run_acc)(args, torch, dg, workloads)
         name = r["name"]
         config = r["config"]
     else:

@@ -126,6 +126,21 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
                                     void* stream);
 
 /*
+ * Accumulating dense GEMM, D = C + A . B^T in fp32.  Deep-dive blog, section 3:
+ * every GEMM of the library has the form D = C + A @ B (NT: A @ B^T).
+ *   A, sfa, B, sfb as for dg_fp8_gemm_nt
+ *   C [M,N] fp32, row-major, or NULL (read as zeros); may equal D (in place)
+ *   D [M,N] fp32, row-major (written)
+ * D = fl32(C + acc): the fp32 accumulator of the promoted GEMM plus C, rounded
+ * once.  workspace as for dg_fp8_gemm_nt (same size query, DG_OP_GEMM_NT).
+ * Shapes whose fp32 output exceeds 32-bit byte offsets (M > 128) are rejected
+ * with DG_ERR_SHAPE.
+ */
+int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
+                       const float* C, float* D, int64_t M, int64_t N, int64_t K, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * BF16 dense GEMM, D = A . B^T, no scales.  BF16 is among the library's
  * precisions (deep-dive blog, section 1 overview table); the Ascend 950
  * article (benchmarks section) measures this GEMM at M=4096, N=7168, K=16384.

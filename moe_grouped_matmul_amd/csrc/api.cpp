@@ -302,6 +302,52 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   return ok();
 }
 
+int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, const float* C,
+                       float* D, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if (M == 0) return ok();
+  if (!A || !sfa || !B || !sfb || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
+    return fail(DG_ERR_ALIGN, "A, B, C and D must be 16-byte aligned");
+  if (!aligned(sfa, 4) || !aligned(sfb, 4)) return fail(DG_ERR_ALIGN, "scale arrays must be 4-byte aligned");
+  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
+    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  if (!pl.persist && !pl.skinny) return fail(DG_ERR_SHAPE, "problem too large for the accumulating form");
+  if (pl.persist && M * N * 4 >= (int64_t)0xFFFFFF00 - 4096)
+    return fail(DG_ERR_SHAPE, "fp32 output too large for 32-bit buffer offsets");
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = sfa;
+  p.B = B;
+  p.sfb = sfb;
+  p.Cacc = C;
+  p.Dacc = D;
+  p.ws = static_cast<float*>(workspace);
+  p.rows = M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = 1;
+  p.m_tiles = pl.m_tiles;
+  p.n_tiles = pl.n_tiles;
+  p.splits = pl.splits;
+  p.kb_per_split = pl.kb_per_split;
+  p.dp_tiles = pl.dp_tiles;
+  p.sk_tiles = pl.sk_tiles;
+  p.sk_pieces = pl.sk_pieces;
+  p.sk_kb = pl.sk_kb;
+  const hipError_t e = pl.persist ? dg::launch_gemm_persistent(dg::kDenseAcc, pl.grid, p, static_cast<hipStream_t>(stream))
+                                  : dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (K <= 0 || K % 64 != 0) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 64 (got %lld)", (long long)K);

@@ -13,6 +13,8 @@ struct GemmParams {
   const uint8_t* B;      // e4m3 weights [G][N][K]
   const float* sfb;      // weight scales [G][ceil(N/128)][K/128]
   uint16_t* D;           // bf16 output
+  const float* Cacc;     // accumulating form: fp32 C [rows][N] (null: zero), fp32 D below
+  float* Dacc;           // accumulating form: fp32 output D = C + A . B^T (may equal Cacc)
   float* ws;             // split-K partials [splits][rows][N] (dense only)
   const int32_t* index;  // m_indices (contiguous) or masked_m (masked); unused when dense
   int64_t rows;          // dense: M; contiguous: M_total; masked: max_m (rows per group)
@@ -34,7 +36,9 @@ struct GemmParams {
 
 // kDenseBf16: the dense schedule over bf16 operands (no scales): a K block
 // is 64 bf16 = 128 bytes per row, the same LDS row as an fp8 K block.
-enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3 };
+// kDenseAcc: the dense fp8 schedule with the fp32 accumulating epilogue
+// (D = C + A . B^T).
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4 };
 
 // Tile configurations compiled for gfx950 (workgroup tile BM x BN, K step 128).
 enum TileCfg { kTile128x128 = 0, kTile64x128 = 1, kTile64x64 = 2, kNumTileCfgs = 3 };

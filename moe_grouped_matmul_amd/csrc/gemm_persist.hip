@@ -76,6 +76,7 @@ template <int MODE>
 __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
+  constexpr bool ACC = MODE == kDenseAcc;    // fp32 output D = C + A . B^T
   constexpr int WGM = MODE == kContiguous ? 2 : 4;
   constexpr int WGN = MODE == kContiguous ? 4 : 2;
   constexpr int TM = 4;
@@ -154,7 +155,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int dp_tiles = MODE == kMasked ? T : p.dp_tiles;  // tasks run as whole tiles
   const int P = p.sk_pieces;                               // pieces per tail tile (dense)
   const int n_dp = b < dp_tiles ? (dp_tiles - b + G - 1) / G : 0;
-  const bool has_tail = (MODE == kDense || BF16) && b < p.sk_tiles * P;
+  const bool has_tail = (MODE == kDense || BF16 || ACC) && b < p.sk_tiles * P;
   const int nseg = n_dp + (has_tail ? 1 : 0);
   if (nseg == 0) return;  // uniform over the workgroup
 
@@ -236,7 +237,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const uint32_t a_bytes = (uint32_t)(ngrp * rows) * (uint32_t)K;
   const uint32_t b_bytes = (uint32_t)(nbgrp * N) * (uint32_t)K;
   const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u;
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
+  const __amdgpu_buffer_rsrc_t rd = ACC ? make_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
+                                        : make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
+  // accumulating form: C (a null C reads as zeros through a zero-length range)
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.Cacc, ACC && p.Cacc ? (uint32_t)rows * (uint32_t)N * 4u : 0u);
 
   // DMA lanes: instruction i of this wave fills LDS rows 64 i + 8 wave + lane / 8;
   // lane chunk (lane % 8) of row r holds K chunk (lane % 8) ^ (r % 8).  B rows
@@ -376,23 +380,43 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       _Pragma("unroll") for (int w_ = 0; w_ < 4; ++w_) st_m[w_] = __builtin_amdgcn_readfirstlane(seg_mask[cp_seg][w_]); \
     }                                                                                                      \
   } while (0)
+#define PS_OUT_OFF(i_)                                                                                     \
+  ([&]() -> uint32_t {                                                                                     \
+    const int gc0_ = st_col0 + wn * 64 + q * 16;                                                           \
+    const int r_ = wm * 64 + (i_) * 16 + q16;                                                              \
+    const bool tag_ = MODE != kContiguous || ((st_m[r_ >> 5] >> (r_ & 31)) & 1u);                          \
+    return (r_ < st_rows && gc0_ < N && tag_) ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u : kOOB; \
+  }())
+  // Accumulating form: fp32 outputs, 64 bytes per lane and row tile (byte
+  // offsets twice the bf16 ones); every C load of the tile is issued before
+  // the first store (C may be D itself), then the sums are stored.
 #define PS_STORE_U()                                                                                       \
   do {                                                                                                     \
-    const int gc0_ = st_col0 + wn * 64 + q * 16;                                                           \
-    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
-      const int r_ = wm * 64 + i_ * 16 + q16;                                                              \
-      const bool tag_ = MODE != kContiguous || ((st_m[r_ >> 5] >> (r_ & 31)) & 1u);                        \
-      const uint32_t off_ = (r_ < st_rows && gc0_ < N && tag_)                                             \
-                                ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u                     \
-                                : kOOB;                                                                    \
-      uint32_t w_[8];                                                                                      \
-      _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                  \
-        w_[2 * j_] = pack_bf16x2(u[i_][j_][0], u[i_][j_][1]);                                              \
-        w_[2 * j_ + 1] = pack_bf16x2(u[i_][j_][2], u[i_][j_][3]);                                          \
+    if constexpr (ACC) {                                                                                   \
+      uint32_t o_[TM];                                                                                     \
+      f32x4 c_[TM][TN];                                                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
+        const uint32_t b_ = PS_OUT_OFF(i_);                                                                \
+        o_[i_] = b_ == kOOB ? kOOB : 2u * b_;                                                              \
+        _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                  \
+          c_[i_][j_] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, o_[i_] + 16u * j_, 0, 0)); \
       }                                                                                                    \
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[0], w_[1], w_[2], w_[3]}, rd, off_, 0, 0);           \
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rd,                        \
-                                             off_ == kOOB ? kOOB : off_ + 16u, 0, 0);                      \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                    \
+        _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                  \
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, u[i_][j_] + c_[i_][j_]), rd,    \
+                                                 o_[i_] + 16u * j_, 0, 0);                                 \
+    } else {                                                                                               \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
+        const uint32_t off_ = PS_OUT_OFF(i_);                                                              \
+        uint32_t w_[8];                                                                                    \
+        _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) {                                                \
+          w_[2 * j_] = pack_bf16x2(u[i_][j_][0], u[i_][j_][1]);                                            \
+          w_[2 * j_ + 1] = pack_bf16x2(u[i_][j_][2], u[i_][j_][3]);                                        \
+        }                                                                                                  \
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[0], w_[1], w_[2], w_[3]}, rd, off_, 0, 0);         \
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rd,                      \
+                                               off_ == kOOB ? kOOB : off_ + 16u, 0, 0);                    \
+      }                                                                                                    \
     }                                                                                                      \
   } while (0)
 
@@ -665,6 +689,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   }
 #undef PS_MARK_TILE
 #undef PS_STORE_U
+#undef PS_OUT_OFF
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -682,6 +707,8 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseBf16)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kDenseAcc)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else

@@ -51,7 +51,7 @@ constexpr int kCoherent = 16;  // sc1
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM, int WN, int P>
+template <int BM, int WN, int P, bool ACC>
 __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4;
@@ -336,6 +336,29 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
   // bytes per store).  N is a multiple of 16 and 4 TN divides 16, so a lane's
   // columns are all inside N or all outside.
   const int c0 = wn0 + q * 4 * TN;
+  if constexpr (ACC) {
+    // accumulating form: fp32 D = C + acc (4 TN consecutive floats per row
+    // tile); every C load before the first store, since C may be D itself
+    f32x4 cv[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = m0 + i * 16 + (lane & 15);
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+        cv[i][jj] = (r < M && c0 < N && p.Cacc)
+                        ? *reinterpret_cast<const f32x4*>(p.Cacc + (int64_t)r * N + c0 + 4 * jj)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = m0 + i * 16 + (lane & 15);
+      if (r >= M || c0 >= N) continue;
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+        *reinterpret_cast<f32x4*>(p.Dacc + (int64_t)r * N + c0 + 4 * jj) = acc[i][jj] + cv[i][jj];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int r = m0 + i * 16 + (lane & 15);
@@ -369,8 +392,12 @@ hipError_t launch_skinny_cfg(const GemmParams& p, hipStream_t stream) {
   const int64_t units = (int64_t)p.n_tiles * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.m_tiles;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, skinny_depth(BM, WN)>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     p);
+  if (p.Dacc)
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, skinny_depth(BM, WN), true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, skinny_depth(BM, WN), false>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ DG_OP_BF16_GEMM_NT = 3
 
 EXPORTED = (
     "dg_fp8_gemm_nt",
+    "dg_fp8_gemm_nt_acc",
     "dg_bf16_gemm_nt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
@@ -69,6 +70,7 @@ def load_library(path=None):
     P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_bf16_gemm_nt.argtypes = [P, P, P, I64, I64, I64, P, SZ, P]
+    lib.dg_fp8_gemm_nt_acc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, SZ, P]
     lib.dg_quant_1x128.argtypes = [P, P, P, I64, I64, I64, P]
@@ -80,7 +82,7 @@ def load_library(path=None):
     lib.dg_get_num_cus.argtypes = []
     lib.dg_get_last_error.restype = ctypes.c_char_p
     lib.dg_version.restype = ctypes.c_char_p
-    for name in ("dg_fp8_gemm_nt", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
+    for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
                  "dg_quant_1x128", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
                  "dg_get_m_alignment_for_contiguous_layout"):
         getattr(lib, name).restype = I
@@ -173,6 +175,30 @@ def dg_fp8_gemm_nt(A, sfa, B, sfb, D, workspace=None, stream=None):
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().dg_fp8_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), M, N, K,
                                          _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dg_fp8_gemm_nt_acc(A, sfa, B, sfb, C, D, workspace=None, stream=None):
+    """D[M,N] (fp32, written) = C[M,N] (fp32, or None for zeros; may be D) + A[M,K] . B[N,K]^T."""
+    A = _bytes_view(A, "A")
+    B = _bytes_view(B, "B")
+    _need(A, "A", torch.uint8, 2)
+    _need(B, "B", torch.uint8, 2)
+    _need(sfa, "sfa", torch.float32, 2)
+    _need(sfb, "sfb", torch.float32, 2)
+    _need(D, "D", torch.float32, 2)
+    if C is not None:
+        _need(C, "C", torch.float32, 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(sfa.shape) != (K // 128, M) or tuple(sfb.shape) != ((N + 127) // 128, K // 128) \
+            or tuple(D.shape) != (M, N) or (C is not None and tuple(C.shape) != (M, N)):
+        raise ValueError("shape mismatch between A, sfa, B, sfb, C, D")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype, workspace.dim())
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().dg_fp8_gemm_nt_acc(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), M, N, K,
+                                             _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dg_bf16_gemm_nt(A, B, D, workspace=None, stream=None):
