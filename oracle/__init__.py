@@ -1,4 +1,5 @@
-"""CPU oracle for block-scaled FP8 GEMM (dense, M-grouped contiguous, M-grouped masked).
+"""CPU oracle for block-scaled FP8 GEMM (dense, M-grouped contiguous, M-grouped
+masked, K-grouped contiguous, the fp32 accumulating form) and the BF16 GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -33,6 +34,7 @@ from .e4m3 import E4M3_MAX, decode_e4m3, encode_e4m3
 from .bf16 import bf16_rne_bits, bf16_bits_to_f64
 from .quant import quant_1x128, quant_128x128
 from .gemm_bf16 import gemm_bf16_nt
+from .gemm_kgrouped import k_grouped_contiguous
 from .gemm import (
     gemm_nt_acc,
     gemm_nt,
@@ -55,4 +57,5 @@ __all__ = [
     "grouped_contiguous",
     "grouped_masked",
     "gemm_bf16_nt",
+    "k_grouped_contiguous",
 ]

@@ -152,3 +152,29 @@ def gemm_nt_c_exact(a_codes, sfa, b_codes, sfb, c):
             cc = f32_fraction(c[i][j]) if c is not None else Fraction(0)
             out[i, j] = f32_from_fraction(exact[i][j] + cc)
     return out
+
+
+def k_grouped_exact(a_codes, sfa, b_codes, sfb, ks, c):
+    """Exact K-grouped form: per group, C plus the sum over the group's K
+    blocks of alpha[block][row] * beta[block][col] * (exact block partial),
+    rounded once to fp32.  Segment bounds are walked here from ks directly."""
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    b_codes = np.asarray(b_codes, dtype=np.uint8)
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    A = [[e4m3_fraction(int(v)) for v in row] for row in a_codes]
+    B = [[e4m3_fraction(int(v)) for v in row] for row in b_codes]
+    G = len(ks)
+    out = np.zeros((G, M, N), dtype=np.float32)
+    start = 0
+    for g in range(G):
+        stop = start + int(ks[g])
+        for i in range(M):
+            for j in range(N):
+                total = f32_fraction(c[g][i][j]) if c is not None else Fraction(0)
+                for k0 in range(start, stop, 128):
+                    part = sum(A[i][k] * B[j][k] for k in range(k0, k0 + 128))
+                    total += f32_fraction(sfa[k0 // 128][i]) * f32_fraction(sfb[k0 // 128][j]) * part
+                out[g, i, j] = f32_from_fraction(total)
+        start = stop
+    return out
