@@ -141,6 +141,35 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
                        size_t workspace_bytes, void* stream);
 
 /*
+ * K-grouped contiguous GEMM (MoE weight gradient), D[g] = C[g] + A_g . B_g^T
+ * in fp32.  Deep-dive blog, section 3: the K-grouped contiguous family groups
+ * along K with M and N fixed and serves the backward pass of MoE weights;
+ * every GEMM there has the form D = C + A @ B, and contiguous segments are
+ * aligned to the block size (M and K).  Group g owns the K range that starts
+ * after the first g segments: A_g = A[:, seg g], B_g = B[:, seg g].
+ *   A   [M,K] e4m3, row-major (K = the sum of the segments, e.g. tokens)
+ *   sfa [K/128][M] fp32: one scale per row per 128 K (1x128, Lesson 13 Fig. 13-1)
+ *   B   [N,K] e4m3, row-major
+ *   sfb [K/128][N] fp32: also per row per 128 K (both operands are activations)
+ *   ks  [G] int32, device: K length of each group, a multiple of 128 (zero
+ *       allowed).  Read by the kernel: group g covers K blocks
+ *       [sum_{h<g} floor(ks[h]/128), + floor(ks[g]/128)), negative lengths
+ *       count as 0 and blocks past K/128 are dropped; K positions after the
+ *       last segment belong to no group.
+ *   C   [G,M,N] fp32 or NULL (zeros); may equal D (in place)
+ *   D   [G,M,N] fp32 (written, every group; a group without K blocks gets C[g])
+ * D[g] = fl32(C[g] + acc_g), acc_g the fp32 accumulator of the promoted
+ * products over the group's blocks.  G must be in [1, 1024]; problems whose
+ * A, B or per-group D byte offsets exceed 32 bits are rejected with
+ * DG_ERR_SHAPE.  workspace: unused, pass NULL/0.
+ */
+int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B,
+                                        const float* sfb, const float* C, float* D,
+                                        const int32_t* ks, int64_t G, int64_t M, int64_t N,
+                                        int64_t K, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
  * BF16 dense GEMM, D = A . B^T, no scales.  BF16 is among the library's
  * precisions (deep-dive blog, section 1 overview table); the Ascend 950
  * article (benchmarks section) measures this GEMM at M=4096, N=7168, K=16384.

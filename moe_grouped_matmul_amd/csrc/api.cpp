@@ -348,6 +348,61 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
   return ok();
 }
 
+int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
+                                        const float* C, float* D, const int32_t* ks, int64_t G, int64_t M,
+                                        int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (G < 1 || G > 1024) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
+  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if (M == 0) return ok();
+  if (!A || !sfa || !B || !sfb || !D || !ks) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
+    return fail(DG_ERR_ALIGN, "A, B, C and D must be 16-byte aligned");
+  if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(ks, 4))
+    return fail(DG_ERR_ALIGN, "scale arrays and ks must be 4-byte aligned");
+  // one 256 x 128 tile grid per group over the shared operands; fp32 C and D
+  // are addressed per group
+  if (!fits_persistent(1, M, N, K) || (M + 256) * N * 4 >= (int64_t)0xFFFFFF00 - 4096)
+    return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = sfa;
+  p.B = B;
+  p.sfb = sfb;
+  p.Cacc = C;
+  p.Dacc = D;
+  p.index = ks;
+  p.rows = M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = (int)G;
+  p.m_tiles = (int)ceil_div(M, 256);
+  p.n_tiles = (int)ceil_div(N, 128);
+  p.splits = 1;
+  p.kb_per_split = (int)(K / 128);
+  p.dp_tiles = 0;
+  p.sk_tiles = 0;
+  p.sk_pieces = 1;
+  p.sk_kb = (int)(K / 128);
+  const int64_t tiles = G * p.m_tiles * p.n_tiles;
+  if (tiles > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "too many tiles");
+  const int ecus = effective_cus(cus);
+  const int grid = (int)(tiles < ecus ? tiles : ecus);
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] k_grouped G=%lld M=%lld N=%lld K=%lld tiles=%lld grid=%d\n", (long long)G, (long long)M,
+                 (long long)N, (long long)K, (long long)tiles, grid);
+  const hipError_t e = dg::launch_gemm_persistent(dg::kKGrouped, grid, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (K <= 0 || K % 64 != 0) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 64 (got %lld)", (long long)K);

@@ -13,10 +13,10 @@ struct GemmParams {
   const uint8_t* B;      // e4m3 weights [G][N][K]
   const float* sfb;      // weight scales [G][ceil(N/128)][K/128]
   uint16_t* D;           // bf16 output
-  const float* Cacc;     // accumulating form: fp32 C [rows][N] (null: zero), fp32 D below
-  float* Dacc;           // accumulating form: fp32 output D = C + A . B^T (may equal Cacc)
+  const float* Cacc;     // accumulating forms: fp32 C [G][rows][N] (null: zero), fp32 D below
+  float* Dacc;           // accumulating forms: fp32 output D = C + A . B^T (may equal Cacc)
   float* ws;             // split-K partials [splits][rows][N] (dense only)
-  const int32_t* index;  // m_indices (contiguous) or masked_m (masked); unused when dense
+  const int32_t* index;  // m_indices (contiguous), masked_m (masked) or ks (K-grouped); unused when dense
   int64_t rows;          // dense: M; contiguous: M_total; masked: max_m (rows per group)
   int N;
   int K;
@@ -38,7 +38,11 @@ struct GemmParams {
 // is 64 bf16 = 128 bytes per row, the same LDS row as an fp8 K block.
 // kDenseAcc: the dense fp8 schedule with the fp32 accumulating epilogue
 // (D = C + A . B^T).
-enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4 };
+// kKGrouped: groups along K (index = ks, the K length of each group), A
+// [rows][K] and B [N][K] shared by all groups, per-row 1x128 scales on both
+// operands (sfa [K/128][rows], sfb [K/128][N]) and one fp32 output
+// D[g] = C[g] + A[:, seg g] . B[:, seg g]^T per group.
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4, kKGrouped = 5 };
 
 // Tile configurations compiled for gfx950 (workgroup tile BM x BN, K step 128).
 enum TileCfg { kTile128x128 = 0, kTile64x128 = 1, kTile64x64 = 2, kNumTileCfgs = 3 };
@@ -76,8 +80,9 @@ constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? (wn == 16 ? 8 : 4
 // p.sk_tiles > 0, p.ws then holds persistent_workspace_bytes(...) bytes whose
 // counters must be zero on entry and are left zero), kContiguous over 128x256
 // tiles (p.dp_tiles = all tiles, no split; at most kPersistentMaxContigTiles
-// tiles per workgroup) or kMasked over 256x128 tiles (G <= 1024).  A, B, sfa
-// and D of all groups are addressed with 32-bit offsets.
+// tiles per workgroup), kMasked over 256x128 tiles (G <= 1024) or kKGrouped
+// over 256x128 tiles of every group (G <= 1024, no split).  A, B, sfa and D of
+// all groups are addressed with 32-bit offsets (K-grouped: D and C per group).
 constexpr int kPersistentMaxContigTiles = 64;
 size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces);
 hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream);

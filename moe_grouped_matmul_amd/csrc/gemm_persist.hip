@@ -29,7 +29,16 @@
 //     masked_m on the device and builds the prefix sums of the active tiles
 //     per group, sum_g ceil(masked_m[g] / 256) * ceil(N / 128); task ids are
 //     walked round-robin and located by binary search, so only the rows below
-//     masked_m are computed and the launch shape is fixed (graph-capturable).
+//     masked_m are computed and the launch shape is fixed (graph-capturable);
+//   * K-grouped (the weight-gradient family of the deep-dive blog, section 3):
+//     every workgroup reads the group lengths ks on the device and builds the
+//     first K block of each group; the tiles of all groups are walked in
+//     rounds of one tile per workgroup, each round mapped XCD-contiguously,
+//     so workgroups share the long and the short groups alike.  A tile runs
+//     over its group's K blocks only; a group without K blocks runs one
+//     iteration over zero operands, so its tiles still store C.  Both
+//     operands carry per-row scales: alpha as in the other forms, beta of the
+//     tile's 128 columns through a 6-slot LDS ring of its own.
 //
 // Main loop (one iteration = one K block of one tile): the three ring slots
 // are separate LDS arrays; iteration j's operands sit in slot j % 3.  A wave
@@ -70,6 +79,7 @@ struct Seg {
   int kb_lo, kb_hi;
   int tail;          // -1: whole tile; else index of a K-split tail tile
   int piece;         // piece of that tail tile
+  int zero;          // K-grouped tile of a group without K blocks: one iteration over zeros
 };
 
 template <int MODE>
@@ -77,6 +87,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
   constexpr bool ACC = MODE == kDenseAcc;    // fp32 output D = C + A . B^T
+  constexpr bool KG = MODE == kKGrouped;     // groups along K, per-column beta, fp32 D[g] = C[g] + ...
+  constexpr bool F32OUT = ACC || KG;
   constexpr int WGM = MODE == kContiguous ? 2 : 4;
   constexpr int WGN = MODE == kContiguous ? 4 : 2;
   constexpr int TM = 4;
@@ -98,13 +110,17 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[SLOT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[SLOT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[SLOT_BYTES];
-  __shared__ int pref[MODE == kMasked ? kMaxMaskedGroups + 1 : 1];  // active tiles before each group
+  // masked: active tiles before each group; K-grouped: first K block of each group
+  __shared__ int pref[MODE == kMasked || KG ? kMaxMaskedGroups + 1 : 1];
   __shared__ int mmv[MODE == kMasked ? kMaxMaskedGroups : 1];       // masked_m clamped to [0, max_m]
   // contiguous: expert of each of this workgroup's tiles (-1: none) and the
   // mask of its rows tagged with that expert
   __shared__ int seg_exp[MODE == kContiguous ? kMaxContigSegs : 1];
   __shared__ uint32_t seg_mask[MODE == kContiguous ? kMaxContigSegs : 1][4];
   __shared__ int last_piece;
+  // K-grouped: beta of the tile's BN columns, slot j % 6 for iteration j (the
+  // loads of iteration j + 3 go to another slot than the reads of iteration j)
+  __shared__ __attribute__((aligned(16))) float bring[KG ? 6 : 1][KG ? BN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,7 +137,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;  // dense: M; masked: max_m
   const int ngrp = MODE == kMasked ? p.G : 1;         // groups of A, alpha and D rows
-  const int nbgrp = MODE == kDense ? 1 : p.G;          // groups of B and beta
+  const int nbgrp = MODE == kContiguous || MODE == kMasked ? p.G : 1;  // groups of B and beta
 
   // ---- task list
   int T;  // tasks: dense tiles / active masked tiles
@@ -149,10 +165,35 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     }
     __syncthreads();
     T = __builtin_amdgcn_readfirstlane(pref[ngrp]);
+  } else if constexpr (KG) {
+    // pref[g] = first K block of group g: prefix of floor(ks / 128), clamped to KB
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < p.G; base += 64) {
+        const int g = base + lane;
+        int v = 0;
+        if (g < p.G) {
+          const int k = p.index[g];
+          v = k > 0 ? (k >> 7) : 0;
+          v = v < KB ? v : KB;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(v, off);
+          if (lane >= off) v += o;
+        }
+        if (g < p.G) pref[g + 1] = carry + v < KB ? carry + v : KB;
+        carry += __shfl(v, 63);
+        carry = carry < KB ? carry : KB;
+      }
+      if (lane == 0) pref[0] = 0;
+    }
+    __syncthreads();
+    T = p.G * p.m_tiles * p.n_tiles;
   } else {
     T = p.m_tiles * p.n_tiles;
   }
-  const int dp_tiles = MODE == kMasked ? T : p.dp_tiles;  // tasks run as whole tiles
+  const int dp_tiles = MODE == kMasked || KG ? T : p.dp_tiles;  // tasks run as whole tiles
   const int P = p.sk_pieces;                               // pieces per tail tile (dense)
   const int n_dp = b < dp_tiles ? (dp_tiles - b + G - 1) / G : 0;
   const bool has_tail = (MODE == kDense || BF16 || ACC) && b < p.sk_tiles * P;
@@ -195,6 +236,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     r.bgrp = 0;
     r.tail = -1;
     r.piece = 0;
+    r.zero = 0;
     r.kb_lo = 0;
     r.kb_hi = KB;
     int d;
@@ -221,6 +263,21 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       r.nt = local - r.mt * p.n_tiles;
       const int mm = __builtin_amdgcn_readfirstlane(mmv[r.grp]);
       r.row_limit = mm - r.mt * BM < BM ? mm - r.mt * BM : BM;
+    } else if constexpr (KG) {
+      // round s of one tile per workgroup, XCD-contiguous inside the round
+      const int left = T - s * G;
+      const int t = s * G + xcd_tile(b, left < G ? left : G);
+      const int tpg = p.m_tiles * p.n_tiles;
+      r.grp = t / tpg;
+      r.bgrp = 0;
+      grouped_mn(t - r.grp * tpg, p.m_tiles, p.n_tiles, GM, &r.mt, &r.nt);
+      r.row_limit = rows - r.mt * BM < BM ? rows - r.mt * BM : BM;
+      r.kb_lo = __builtin_amdgcn_readfirstlane(pref[r.grp]);
+      r.kb_hi = __builtin_amdgcn_readfirstlane(pref[r.grp + 1]);
+      if (r.kb_hi == r.kb_lo) {
+        r.zero = 1;
+        r.kb_hi = r.kb_lo + 1;
+      }
     } else {
       grouped_mn(xcd_tile(d, T), p.m_tiles, p.n_tiles, GM, &r.mt, &r.nt);
       r.row_limit = rows - r.mt * BM < BM ? rows - r.mt * BM : BM;
@@ -237,7 +294,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const uint32_t a_bytes = (uint32_t)(ngrp * rows) * (uint32_t)K;
   const uint32_t b_bytes = (uint32_t)(nbgrp * N) * (uint32_t)K;
   const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u;
-  const __amdgpu_buffer_rsrc_t rd = ACC ? make_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
+  const uint32_t sb_bytes = KG ? (uint32_t)N * (uint32_t)KB * 4u : 0u;  // K-grouped beta [KB][N]
+  const __amdgpu_buffer_rsrc_t rd = F32OUT ? make_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
                                         : make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
   // accumulating form: C (a null C reads as zeros through a zero-length range)
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.Cacc, ACC && p.Cacc ? (uint32_t)rows * (uint32_t)N * 4u : 0u);
@@ -265,6 +323,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // ---- issue pointer: iteration j + 3 of this workgroup's sequence.  Its
   // per-lane source offsets change only with its tile (rows outside the tile
   // get an offset past the buffer end); the K block enters through soffset.
+  // K-grouped: waves 4 and 5 load beta of the tile's columns instead of alpha
+  const bool bwave = KG && (wave == 4 || wave == 5);
   int is_seg = 0;
   Seg is_t = seg_of(0);
   int is_kb = is_t.kb_lo;
@@ -272,7 +332,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   uint32_t is_boff[B_INS];
   uint32_t is_soff;
   auto is_setup = [&]() {
-    const int arow = is_t.grp * rows + is_t.mt * BM;
+    const int agrp = KG ? 0 : is_t.grp;  // K-grouped: A and alpha are shared by all groups
+    const int arow = agrp * rows + is_t.mt * BM;
     const int brow = is_t.bgrp * N + is_t.nt * BN;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -284,7 +345,16 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       const int c = 64 * i + b_perm;
       is_boff[i] = is_t.nt * BN + c < N ? (uint32_t)(brow + c) * (uint32_t)K + dma_chunk : kOOB;
     }
-    is_soff = (uint32_t)((is_t.grp * KB * rows + is_t.mt * BM + wave * 64 + lane) * 4);
+    // scale lanes: alpha of the tile's rows that exist; beta (K-grouped) of
+    // its columns below N; every other lane addresses past the range
+    const int srow = wave * 64 + lane;
+    is_soff = srow < BM && srow < is_t.row_limit
+                  ? (uint32_t)((agrp * KB * rows + is_t.mt * BM + srow) * 4)
+                  : kOOB;
+    if (KG && bwave) {
+      const int scol = is_t.nt * BN + (wave - 4) * 64 + lane;
+      is_soff = scol < N ? (uint32_t)(scol * 4) : kOOB;
+    }
   };
   is_setup();
 
@@ -295,11 +365,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // pointer.  The three must share one scope.
 #define PS_ISSUE_BEGIN()                                                                                   \
   const bool in_ = is_seg < nseg;                                                                          \
-  const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(p.A, in_ ? a_bytes : 0u);                                   \
-  const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(p.B, in_ ? b_bytes : 0u);                                   \
-  const __amdgpu_buffer_rsrc_t rs_ = make_rsrc(p.sfa, in_ ? s_bytes : 0u);                                 \
+  const bool ld_ = in_ && !(KG && is_t.zero);                                                              \
+  const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(p.A, ld_ ? a_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(p.B, ld_ ? b_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rs_ = bwave ? make_rsrc(p.sfb, ld_ ? sb_bytes : 0u)                         \
+                                           : make_rsrc(p.sfa, ld_ ? s_bytes : 0u);                         \
   const int ks_ = is_kb << 7
-#define PS_ISSUE_LOAD(st_, n_)                                                                             \
+#define PS_ISSUE_LOAD(st_, bs_, n_)                                                                        \
   do {                                                                                                     \
     if ((n_) < A_INS)                                                                                      \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(PS_SA(st_) + ((n_) * NWAVES + wave) * 1024), \
@@ -309,8 +381,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
                                                (DG_LDS void*)(PS_SB(st_) + ((n_) - A_INS) * NWAVES * 1024 + wave * 1024), \
                                                16, is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0); \
     else                                                                                                   \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(PS_SS(st_) + wave * 64), 4, is_soff,    \
-                                               is_kb * rows * 4, 0, 0);                                    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                            \
+          rs_, (DG_LDS void*)(bwave ? &bring[KG ? (bs_) : 0][(wave - 4) * 64] : PS_SS(st_) + wave * 64), 4,     \
+          is_soff, is_kb * (bwave ? N : rows) * 4, 0, 0);                                                  \
   } while (0)
 #define PS_ISSUE_END()                                                                                     \
   do {                                                                                                     \
@@ -322,14 +395,21 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       }                                                                                                    \
     }                                                                                                      \
   } while (0)
-#define PS_ISSUE(st_)                                                                                      \
+#define PS_ISSUE(st_, bs_)                                                                                 \
   do {                                                                                                     \
     PS_ISSUE_BEGIN();                                                                                      \
-    _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, n_);                        \
+    _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, bs_, n_);                   \
     PS_ISSUE_END();                                                                                        \
   } while (0)
 
   int J = n_dp * KB;  // iterations of this workgroup
+  if constexpr (KG) {
+    J = 0;
+    for (int s = 0; s < nseg; ++s) {
+      const Seg t = seg_of(s);
+      J += t.kb_hi - t.kb_lo;
+    }
+  }
   if (has_tail) {
     const Seg t = seg_of(n_dp);
     J += t.kb_hi - t.kb_lo;
@@ -369,13 +449,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // wait can depend on their completion.  (st_row0, st_col0, st_rows) locate
   // the tile.
   bool pend = false;
-  int st_row0 = 0, st_col0 = 0, st_rows = 0;
+  int st_row0 = 0, st_col0 = 0, st_rows = 0, st_grp = 0;
   uint32_t st_m[4] = {~0u, ~0u, ~0u, ~0u};  // contiguous: rows tagged with the tile's expert
 #define PS_MARK_TILE()                                                                                     \
   do {                                                                                                     \
-    st_row0 = cp_t.grp * rows + cp_t.mt * BM;                                                              \
+    st_row0 = (KG ? 0 : cp_t.grp * rows) + cp_t.mt * BM;                                                  \
     st_col0 = cp_t.nt * BN;                                                                                \
     st_rows = cp_t.row_limit;                                                                              \
+    st_grp = cp_t.grp;                                                                                     \
     if (MODE == kContiguous) {                                                                             \
       _Pragma("unroll") for (int w_ = 0; w_ < 4; ++w_) st_m[w_] = __builtin_amdgcn_readfirstlane(seg_mask[cp_seg][w_]); \
     }                                                                                                      \
@@ -387,23 +468,28 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     const bool tag_ = MODE != kContiguous || ((st_m[r_ >> 5] >> (r_ & 31)) & 1u);                          \
     return (r_ < st_rows && gc0_ < N && tag_) ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u : kOOB; \
   }())
-  // Accumulating form: fp32 outputs, 64 bytes per lane and row tile (byte
+  // Accumulating forms: fp32 outputs, 64 bytes per lane and row tile (byte
   // offsets twice the bf16 ones); every C load of the tile is issued before
-  // the first store (C may be D itself), then the sums are stored.
+  // the first store (C may be D itself), then the sums are stored.  K-grouped:
+  // C and D of the tile's group, one [rows][N] matrix each.
 #define PS_STORE_U()                                                                                       \
   do {                                                                                                     \
-    if constexpr (ACC) {                                                                                   \
+    if constexpr (F32OUT) {                                                                                \
+      const size_t gof_ = KG ? (size_t)st_grp * (size_t)rows * (size_t)N : 0;                              \
+      const __amdgpu_buffer_rsrc_t rd_ = KG ? make_rsrc(p.Dacc + gof_, (uint32_t)rows * (uint32_t)N * 4u) : rd; \
+      const __amdgpu_buffer_rsrc_t rc_ =                                                                   \
+          KG ? make_rsrc(p.Cacc + (p.Cacc ? gof_ : 0), p.Cacc ? (uint32_t)rows * (uint32_t)N * 4u : 0u) : rc;   \
       uint32_t o_[TM];                                                                                     \
       f32x4 c_[TM][TN];                                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         const uint32_t b_ = PS_OUT_OFF(i_);                                                                \
         o_[i_] = b_ == kOOB ? kOOB : 2u * b_;                                                              \
         _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                  \
-          c_[i_][j_] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, o_[i_] + 16u * j_, 0, 0)); \
+          c_[i_][j_] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc_, o_[i_] + 16u * j_, 0, 0)); \
       }                                                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                    \
         _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                  \
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, u[i_][j_] + c_[i_][j_]), rd,    \
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, u[i_][j_] + c_[i_][j_]), rd_,   \
                                                  o_[i_] + 16u * j_, 0, 0);                                 \
     } else {                                                                                               \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
@@ -447,7 +533,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // second halves (each depends on its first half 16 MFMAs earlier).  The
   // next iteration's fragment reads and the block's loads are interleaved as
   // in the FP8 path.
-#define PS_COMPUTE_BF16(st_, AF, BF, AN, BN_)                                                              \
+#define PS_COMPUTE_BF16(st_, bs_, AF, BF, AN, BN_)                                                         \
   do {                                                                                                     \
     const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                        \
     uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                    \
@@ -461,7 +547,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
                                      : i32x4{BF[j_][4], BF[j_][5], BF[j_][6], BF[j_][7]};                  \
       u[i_][j_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bv_),                \
                                                          __builtin_bit_cast(bf16x8, av_), u[i_][j_], 0, 0, 0); \
-      if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, k_);                                                            \
+      if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, bs_, k_);                                                       \
       if (k_ < 2 * (TM + TN)) {                                                                            \
         const int f_ = k_ >> 1; /* fragment: A 0..TM-1, then B */                                          \
         const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +        \
@@ -487,12 +573,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // steps back, so the LDS reads and the FMAs
   // overlap the matrix cores.  Masked: all reads first, then the MFMAs of the
   // 16-row tiles holding rows below masked_m.
-#define PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN)                                                          \
+#define PS_COMPUTE(st_, bs_, br_, AF, BF, AL, AN, BN_, ALN)                                                \
   do {                                                                                                     \
     float sc_[TM];                                                                                         \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) sc_[i_] = AL[i_] * beta_;                            \
     if constexpr (BF16) {                                                                                  \
-      PS_COMPUTE_BF16(st_, AF, BF, AN, BN_);                                                               \
+      PS_COMPUTE_BF16(st_, bs_, AF, BF, AN, BN_);                                                          \
       (void)sc_;                                                                                           \
     } else if constexpr (MODE == kMasked) {                                                                       \
       const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
@@ -526,11 +612,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
       uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
       f32x4 t_[TM * TN];                                                                                   \
+      f32x4 bt_[2]; /* K-grouped: beta of the 4 columns of fragment j, two j in flight */                  \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
       _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 3; ++k_) {                                         \
         if (k_ < TM * TN) {                                                                                \
           t_[k_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[k_ / TM], AF[k_ % TM], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
-          if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, k_); /* the block's loads, spread over the first steps */   \
+          if (KG && k_ % TM == 0)                                                                          \
+            bt_[(k_ / TM) & 1] = *reinterpret_cast<const f32x4*>(&bring[KG ? (br_) : 0][KG ? wn * 64 + q * 16 + 4 * (k_ / TM) : 0]); \
+          if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, bs_, k_); /* the block's loads, spread over the first steps */ \
           const int f_ = k_ >> 1; /* fragment: A 0..TM-1, then B */                                        \
           const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +      \
                               ((k_ & 1) ? fr_hi : fr_lo);                                                  \
@@ -540,6 +629,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         if (k_ >= 3) {                                                                                     \
           const int kk_ = k_ - 3;                                                                          \
           f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
+          if constexpr (KG) t_[kk_] *= bt_[(kk_ / TM) & 1];                                                \
           _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
             uk_[v_] = __builtin_fmaf(t_[kk_][v_], sc_[kk_ % TM], uk_[v_]);                                 \
           /* keeps these FMAs in this step: instruction selection would sink them to the block's end */    \
@@ -565,10 +655,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // (those only add to the count).  Iterations past this workgroup's last one
   // read zero operands (their loads address zero-length ranges) and a zero
   // scale, so their products add exactly nothing.
-#define PS_STEP(st_, jj_, AF, BF, AL, AN, BN_, ALN)                                                        \
+#define PS_STEP(c_, jj_, AF, BF, AL, AN, BN_, ALN)                                                         \
   do {                                                                                                     \
+    constexpr int st_ = (c_) % 3;                                                                          \
     const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = BF16 ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                        \
+    const float beta_ = BF16 || KG ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                  \
     wait_vmcnt<L_BLOCK>();                                                                                 \
     wait_lgkmcnt0(); /* own reads of this slot done before anyone may refill it */                        \
     __builtin_amdgcn_s_barrier();                                                                          \
@@ -581,9 +672,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     {                                                                                                      \
       PS_ISSUE_BEGIN();                                                                                    \
       if constexpr (MODE == kMasked) {                                                                     \
-        _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, n_);                    \
+        _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, (c_ + 3) % 6, n_);      \
       }                                                                                                    \
-      PS_COMPUTE(st_, AF, BF, AL, AN, BN_, ALN);                                                           \
+      PS_COMPUTE(st_, (c_ + 3) % 6, c_, AF, BF, AL, AN, BN_, ALN);                                         \
       PS_ISSUE_END();                                                                                      \
     }                                                                                                      \
     if (live_ && ++cp_kb == cp_t.kb_hi && cp_t.tail < 0) { /* a whole tile is done */                     \
@@ -600,9 +691,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   i32x8 afX[TM], bfX[TN], afY[TM], bfY[TN];
   float alX[TM], alY[TM];
   // prologue: iterations 0, 1, 2 into slots 0, 1, 2; fragments of iteration 0
-  PS_ISSUE(0);
-  PS_ISSUE(1);
-  PS_ISSUE(2);
+  PS_ISSUE(0, 0);
+  PS_ISSUE(1, 1);
+  PS_ISSUE(2, 2);
   wait_vmcnt<2 * L_BLOCK>();  // iteration 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
   PS_LOAD_FRAGS(0, afX, bfX, alX);
@@ -613,9 +704,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     PS_STEP(0, j, afX, bfX, alX, afY, bfY, alY);
     PS_STEP(1, j + 1, afY, bfY, alY, afX, bfX, alX);
     PS_STEP(2, j + 2, afX, bfX, alX, afY, bfY, alY);
-    PS_STEP(0, j + 3, afY, bfY, alY, afX, bfX, alX);
-    PS_STEP(1, j + 4, afX, bfX, alX, afY, bfY, alY);
-    PS_STEP(2, j + 5, afY, bfY, alY, afX, bfX, alX);
+    PS_STEP(3, j + 3, afY, bfY, alY, afX, bfX, alX);
+    PS_STEP(4, j + 4, afX, bfX, alX, afY, bfY, alY);
+    PS_STEP(5, j + 5, afY, bfY, alY, afX, bfX, alX);
   }
   if (pend) PS_STORE_U();
   wait_vmcnt<0>();  // no LDS writes or stores in flight past this point
@@ -709,6 +800,8 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseAcc)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kKGrouped)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else

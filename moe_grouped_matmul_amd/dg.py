@@ -36,6 +36,7 @@ EXPORTED = (
     "dg_bf16_gemm_nt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
     "dg_m_grouped_fp8_gemm_nt_masked",
+    "dg_k_grouped_fp8_gemm_nt_contiguous",
     "dg_quant_1x128",
     "dg_quant_128x128",
     "dg_get_workspace_size",
@@ -73,6 +74,7 @@ def load_library(path=None):
     lib.dg_fp8_gemm_nt_acc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, SZ, P]
+    lib.dg_k_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_quant_1x128.argtypes = [P, P, P, I64, I64, I64, P]
     lib.dg_quant_128x128.argtypes = [P, P, P, I64, I64, I64, P]
     lib.dg_get_workspace_size.argtypes = [I, I64, I64, I64, I64]
@@ -83,7 +85,7 @@ def load_library(path=None):
     lib.dg_get_last_error.restype = ctypes.c_char_p
     lib.dg_version.restype = ctypes.c_char_p
     for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
-                 "dg_quant_1x128", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
+                 "dg_k_grouped_fp8_gemm_nt_contiguous", "dg_quant_1x128", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
                  "dg_get_m_alignment_for_contiguous_layout"):
         getattr(lib, name).restype = I
     if path is None:
@@ -263,6 +265,31 @@ def dg_m_grouped_fp8_gemm_nt_masked(A, sfa, B, sfb, D, masked_m, expected_m=0, s
         raise ValueError("shape mismatch between A, sfa, B, sfb, D, masked_m")
     _check(load_library().dg_m_grouped_fp8_gemm_nt_masked(
         _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), _ptr(masked_m), G, max_m, N, K, int(expected_m),
+        ctypes.c_void_p(0), 0, _stream(stream)))
+
+
+def dg_k_grouped_fp8_gemm_nt_contiguous(A, sfa, B, sfb, C, D, ks, stream=None):
+    """K-grouped contiguous: A [M,K], sfa [K/128,M], B [N,K], sfb [K/128,N] (per-row scales on both),
+    ks [G] int32 on device (K length of each group, multiples of 128), C [G,M,N] fp32 or None (zeros;
+    may be D), D [G,M,N] fp32 written: D[g] = C[g] + A[:, seg g] . B[:, seg g]^T."""
+    A = _bytes_view(A, "A")
+    B = _bytes_view(B, "B")
+    _need(A, "A", torch.uint8, 2)
+    _need(B, "B", torch.uint8, 2)
+    _need(sfa, "sfa", torch.float32, 2)
+    _need(sfb, "sfb", torch.float32, 2)
+    _need(D, "D", torch.float32, 3)
+    _need(ks, "ks", torch.int32, 1)
+    if C is not None:
+        _need(C, "C", torch.float32, 3)
+    M, K = A.shape
+    N = B.shape[0]
+    G = ks.shape[0]
+    if B.shape[1] != K or tuple(sfa.shape) != (K // 128, M) or tuple(sfb.shape) != (K // 128, N) \
+            or tuple(D.shape) != (G, M, N) or (C is not None and tuple(C.shape) != (G, M, N)):
+        raise ValueError("shape mismatch between A, sfa, B, sfb, C, D, ks")
+    _check(load_library().dg_k_grouped_fp8_gemm_nt_contiguous(
+        _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(C), _ptr(D), _ptr(ks), G, M, N, K,
         ctypes.c_void_p(0), 0, _stream(stream)))
 
 

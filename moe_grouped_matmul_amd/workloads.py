@@ -14,6 +14,10 @@ Recipe (numpy PCG64, ``numpy.random.default_rng(seed)``), draws in this order:
    multiplied by 20 (0.1% outliers);
 3. weights B: (G*N) x K standard normal fp32 times fp32(1/sqrt(K)), i.e.
    N(0, 1/K).
+K-grouped (weight-gradient) inputs: G token counts uniform on [0, max_tokens],
+each segment padded to a multiple of 128 positions; A (the output gradient,
+transposed) M x K and B (the layer input, transposed) N x K drawn as
+activations for the valid positions, zero in the padding.
 The pages benchmark "all DeepSeek-V3/R1 inference shapes" on H800 without
 listing them (the chart was not preserved), so these generators stand in for
 those shapes; no dataset or trained weight is involved.
@@ -49,6 +53,8 @@ CONFIGS = {
     "dense_large": [dict(M=4096, N=7168, K=16384, seed=200)],
     "contiguous": [dict(G=8, N=4096, K=7168, seed=300), dict(G=8, N=7168, K=2048, seed=301)],
     "masked": [dict(G=32, max_m=256, N=4096, K=7168, seed=400), dict(G=32, max_m=256, N=7168, K=2048, seed=401)],
+    # weight gradients of 8 local experts' up (4096 x 7168) and down (7168 x 2048) projections
+    "k_grouped": [dict(G=8, M=4096, N=7168, seed=500), dict(G=8, M=7168, N=2048, seed=501)],
 }
 
 
@@ -151,3 +157,32 @@ def dense_bf16(M: int, N: int, K: int, seed: int):
     b = rng.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / np.sqrt(K))
     cast = lambda x: torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     return cast(a), cast(b)
+
+
+def k_grouped(G: int, M: int, N: int, seed: int, max_tokens: int = 8192, counts=None):
+    """K-grouped (weight-gradient) workload.
+
+    Returns dict with
+      counts int64 [G]   tokens per expert (0 allowed)
+      ks     int32 [G]   segment lengths: counts padded to multiples of 128
+      a      fp32 [M, K] output gradient, transposed (tokens along K)
+      b      fp32 [N, K] layer input, transposed
+    Padding positions of every segment are zero in both operands.
+    """
+    rng = np.random.default_rng(seed)
+    if counts is None:
+        counts = rng.integers(0, max_tokens + 1, G)
+    counts = np.asarray(counts, dtype=np.int64)
+    ks = ((counts + 127) // 128 * 128).astype(np.int32)
+    K = int(ks.sum())
+    valid = np.zeros(K, dtype=bool)
+    lo = 0
+    for g in range(G):
+        valid[lo:lo + int(counts[g])] = True
+        lo += int(ks[g])
+    a = np.zeros((M, K), dtype=np.float32)
+    b = np.zeros((N, K), dtype=np.float32)
+    nv = int(valid.sum())
+    a[:, valid] = _activations(rng, M, nv)
+    b[:, valid] = _activations(rng, N, nv)
+    return dict(counts=counts, ks=ks, a=a, b=b)

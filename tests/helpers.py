@@ -68,3 +68,28 @@ def acc_tolerance(qa, sa, qb, sb, c):
         s += np.abs(sa[g].astype(np.float64))[:, None] * np.abs(sb[cb, g].astype(np.float64))[None, :] * (a[:, ks] @ b[:, ks].T)
     total = s + (np.abs(c.astype(np.float64)) if c is not None else 0.0)
     return 2.0 * (2.0 ** -10 * s + 2.0 ** -24 * (KB + 2) * total)
+
+
+def kg_tolerance(qa, sa, qb, sb, ks, c):
+    """Per-element bound for the K-grouped fp32 GEMM, the accumulating bound
+    (acc_tolerance) taken per group over the group's K blocks, with per-row
+    scales on both operands; the extra fp32 rounding of partial * beta per
+    block is one more 2^-24 relative term of the same partial sums."""
+    import numpy as np
+
+    a = np.abs(oracle.decode_e4m3(qa))
+    b = np.abs(oracle.decode_e4m3(qb))
+    G = len(ks)
+    out = np.zeros((G, a.shape[0], b.shape[0]))
+    lo = 0
+    for g in range(G):
+        nb = int(ks[g]) // 128
+        s = np.zeros((a.shape[0], b.shape[0]))
+        for blk in range(lo // 128, lo // 128 + nb):
+            cols = slice(128 * blk, 128 * blk + 128)
+            s += np.abs(sa[blk].astype(np.float64))[:, None] * np.abs(sb[blk].astype(np.float64))[None, :] * \
+                (a[:, cols] @ b[:, cols].T)
+        total = s + (np.abs(c[g].astype(np.float64)) if c is not None else 0.0)
+        out[g] = 2.0 * (2.0 ** -10 * s + 2.0 ** -24 * (2 * nb + 2) * total)
+        lo += int(ks[g])
+    return out

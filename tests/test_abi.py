@@ -92,6 +92,17 @@ def test_status_codes_from_host(lib):
     assert masked(P16, P16, P16, P16, P16, P16, 4, -1, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
     assert masked(None, None, None, None, None, None, 4, 0, 128, 256, 0, None, 0, s) == dg.DG_OK
     assert masked(P16, P16, P16, P16, P16, None, 4, 8, 128, 256, 0, None, 0, s) == dg.DG_ERR_INVALID_ARG
+    kg = lib.dg_k_grouped_fp8_gemm_nt_contiguous
+    # (A, sfa, B, sfb, C, D, ks, G, M, N, K, ws, ws_bytes, stream)
+    assert kg(P16, P16, P16, P16, None, P16, P16, 0, 256, 128, 256, None, 0, s) == dg.DG_ERR_SHAPE
+    assert kg(P16, P16, P16, P16, None, P16, P16, 1025, 256, 128, 256, None, 0, s) == dg.DG_ERR_SHAPE
+    assert kg(P16, P16, P16, P16, None, P16, P16, 2, 256, 128, 200, None, 0, s) == dg.DG_ERR_SHAPE
+    assert kg(P16, P16, P16, P16, None, P16, P16, 2, -1, 128, 256, None, 0, s) == dg.DG_ERR_SHAPE
+    assert kg(None, None, None, None, None, None, None, 2, 0, 128, 256, None, 0, s) == dg.DG_OK
+    assert kg(P16, P16, P16, P16, None, P16, None, 2, 256, 128, 256, None, 0, s) == dg.DG_ERR_INVALID_ARG
+    assert kg(P16, P16, P16, P16, P16 + 4, P16, P16, 2, 256, 128, 256, None, 0, s) == dg.DG_ERR_ALIGN
+    assert kg(P16, P16, P16, P16, None, P16, P16 + 2, 2, 256, 128, 256, None, 0, s) == dg.DG_ERR_ALIGN
+    assert kg(P16, P16, P16, P16, None, P16, P16, 2, 1 << 20, 4096, 4096, None, 0, s) == dg.DG_ERR_SHAPE
     q1 = lib.dg_quant_1x128
     assert q1(P16, P16, P16, 1, 4, 100, s) == dg.DG_ERR_SHAPE
     assert q1(None, P16, P16, 1, 4, 128, s) == dg.DG_ERR_INVALID_ARG
