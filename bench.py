@@ -105,7 +105,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc",
+                                                              "kgrouped"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -369,7 +370,7 @@ def run_grouped(args, torch, dg, workloads):
     else:
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
-    kname = "fp8_gemm_lds_kernel<2,4,contiguous>" if args.workload == "contiguous" else "fp8_gemm_persistent_kernel<masked>"
+    kname = "fp8_gemm_persistent_kernel<contiguous>" if args.workload == "contiguous" else "fp8_gemm_persistent_kernel<masked>"
     roof.update(traffic=None, kernel=f"{kname} ({big['N']}x{big['K']})",
                 avg_launch_us=big["gemm_us"])
     name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
@@ -516,6 +517,96 @@ def run_acc(args, torch, dg, workloads):
                 config=config)
 
 
+def kgrouped_work(M, N, counts, K):
+    """Algorithmic work of one K-grouped call: flops of the valid tokens; bytes
+    of both operands and their per-row scales over the padded K layout, fp32 C
+    read and D written for every group, and the lengths."""
+    G = len(counts)
+    flops = 2.0 * M * N * float(sum(counts))
+    nbytes = (M + N) * K + 4 * (M + N) * (K // 128) + 8.0 * G * M * N + 4 * G
+    return flops, float(nbytes)
+
+
+def run_kgrouped(args, torch, dg, workloads):
+    """K-grouped contiguous weight-gradient GEMMs of 8 local experts (tokens
+    per expert uniform in [0, 8192], segments padded to 128): the up
+    projection (4096 x 7168) and the down projection (7168 x 2048), each
+    accumulated in place into its fp32 gradient (C = D).  A step is the two
+    calls."""
+    dev = torch.device("cuda:0")
+    prepared = []
+    for c in workloads.CONFIGS["k_grouped"]:
+        G, M, N = c["G"], c["M"], c["N"]
+        w = workloads.k_grouped(G, M, N, c["seed"])
+        K = int(w["ks"].sum())
+
+        def quant(x):
+            X = torch.from_numpy(x).to(dev)
+            q = torch.empty(X.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty((K // 128, X.shape[0]), dtype=torch.float32, device=dev)
+            dg.dg_quant_1x128(X, q, sc)
+            del X
+            return q, sc
+
+        A8, SA = quant(w["a"])
+        B8, SB = quant(w["b"])
+        ks = torch.from_numpy(w["ks"]).to(dev)
+        per_set = (M + N) * K + 4 * (M + N) * (K // 128) + 4 * G * M * N
+        nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        sets = [dict(a8=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(),
+                     b8=B8 if i == 0 else B8.clone(), sb=SB if i == 0 else SB.clone(),
+                     d=torch.zeros((G, M, N), dtype=torch.float32, device=dev)) for i in range(nsets)]
+        flops, nbytes = kgrouped_work(M, N, [int(x) for x in w["counts"]], K)
+        prepared.append(dict(G=G, M=M, N=N, K=K, sets=sets, ks=ks, flops=flops, bytes=nbytes))
+        del w
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+
+    def gemm(p, i):
+        st = p["sets"][i % len(p["sets"])]
+        dg.dg_k_grouped_fp8_gemm_nt_contiguous(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], st["d"], p["ks"])
+
+    def step(i):
+        for p in prepared:
+            gemm(p, i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n_graphs = max(len(p["sets"]) for p in prepared)
+    graphs = [capture(torch, lambda i=i: step(i)) for i in range(n_graphs)]
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    t_start = timer.ev()
+    for i in range(args.steps):
+        graphs[(args.warmup + i) % n_graphs].replay()
+    t_end = timer.ev()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    del graphs
+    per_shape = []
+    for p in prepared:
+        launches = max(len(p["sets"]), 4)
+        gg = capture(torch, lambda p=p: [gemm(p, i) for i in range(launches)])
+        t_us = time_graph(torch, timer, gg, PER_SHAPE_REPS) / launches * 1e3
+        del gg
+        per_shape.append(dict(G=p["G"], M=p["M"], N=p["N"], K=p["K"], gemm_us=round(t_us, 2),
+                              tflops=round(p["flops"] / t_us / 1e6, 1), gbs=round(p["bytes"] / t_us / 1e3, 1),
+                              bound="mfma", roof_frac=round(roof_time_us(p["flops"], p["bytes"]) / t_us, 4),
+                              algorithmic_flops_per_launch=round(p["flops"]),
+                              algorithmic_bytes_per_launch=round(p["bytes"])))
+    big = max(per_shape, key=lambda r: r["gemm_us"])
+    roof = dict(bound="mfma", achieved=big["tflops"], peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                frac=round(big["tflops"] / PEAK_FP8_TFLOPS, 4), traffic=None,
+                kernel=f"fp8_gemm_persistent_kernel<k_grouped> ({big['M']}x{big['N']})", avg_launch_us=big["gemm_us"])
+    name = "k_grouped_wgrad_8x_tokens_0to8192"
+    config = dict(workload=name, shapes=[f"G={p['G']} M={p['M']} N={p['N']} K={p['K']}" for p in prepared],
+                  out="fp32 D[g] += A_g . B_g^T (in place)", step="dg_k_grouped_fp8_gemm_nt_contiguous per shape",
+                  cold_hbm=True)
+    return dict(ms_per_step=ms_per_step, step_flops=sum(p["flops"] for p in prepared), per_shape=per_shape,
+                roofline=roof, name=name, config=config)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -546,8 +637,8 @@ def main():
         config = dict(workload=name, shapes=[f"{m}x{n}x{k}" for m, n, k in r["shapes"]],
                       scales="1x128 activations, 128x128 weights, fp32", out="bf16",
                       step="dg_quant_1x128 + dg_fp8_gemm_nt per shape", cold_hbm=True)
-    elif args.workload in ("bf16", "acc"):
-        r = (run_bf16 if args.workload == "bf16" else run_acc)(args, torch, dg, workloads)
+    elif args.workload in ("bf16", "acc", "kgrouped"):
+        r = {"bf16": run_bf16, "acc": run_acc, "kgrouped": run_kgrouped}[args.workload](args, torch, dg, workloads)
         name = r["name"]
         config = r["config"]
     else:

@@ -82,7 +82,8 @@ struct Seg {
   int zero;          // K-grouped tile of a group without K blocks: one iteration over zeros
 };
 
-template <int MODE>
+// HASC (fp32-output modes): C is given and read; without it nothing is loaded.
+template <int MODE, bool HASC>
 __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
@@ -469,9 +470,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     return (r_ < st_rows && gc0_ < N && tag_) ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u : kOOB; \
   }())
   // Accumulating forms: fp32 outputs, 64 bytes per lane and row tile (byte
-  // offsets twice the bf16 ones); every C load of the tile is issued before
-  // the first store (C may be D itself), then the sums are stored.  K-grouped:
-  // C and D of the tile's group, one [rows][N] matrix each.
+  // offsets twice the bf16 ones); with C given, every C load of the tile is
+  // issued before the first store (C may be D itself), then the sums are
+  // stored; without C, u is stored.  K-grouped: C and D of the tile's group,
+  // one [rows][N] matrix each.
 #define PS_STORE_U()                                                                                       \
   do {                                                                                                     \
     if constexpr (F32OUT) {                                                                                \
@@ -485,7 +487,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         const uint32_t b_ = PS_OUT_OFF(i_);                                                                \
         o_[i_] = b_ == kOOB ? kOOB : 2u * b_;                                                              \
         _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                  \
-          c_[i_][j_] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc_, o_[i_] + 16u * j_, 0, 0)); \
+          c_[i_][j_] = HASC ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rc_, o_[i_] + 16u * j_, 0, 0)) \
+                            : f32x4{0.f, 0.f, 0.f, 0.f};                                                   \
       }                                                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                    \
         _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                  \
@@ -794,18 +797,24 @@ size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces) {
 
 hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
+  const dim3 g((unsigned)grid), t(512);
+  const bool c = p.Cacc != nullptr;
   if (mode == kMasked)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked, false>), g, t, 0, stream, p);
   else if (mode == kDenseBf16)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16, false>), g, t, 0, stream, p);
+  else if (mode == kDenseAcc && c)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc, true>), g, t, 0, stream, p);
   else if (mode == kDenseAcc)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc, false>), g, t, 0, stream, p);
+  else if (mode == kKGrouped && c)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, true>), g, t, 0, stream, p);
   else if (mode == kKGrouped)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, false>), g, t, 0, stream, p);
   else if (mode == kContiguous)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous, false>), g, t, 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense, false>), g, t, 0, stream, p);
   return hipGetLastError();
 }
 
