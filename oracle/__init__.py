@@ -1,5 +1,6 @@
 """CPU oracle for block-scaled FP8 GEMM (dense, M-grouped contiguous, M-grouped
-masked, K-grouped contiguous, the fp32 accumulating form) and the BF16 GEMM.
+masked, K-grouped contiguous, the fp32 accumulating form, UE8M0 scales) and the
+BF16 GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -35,6 +36,7 @@ from .bf16 import bf16_rne_bits, bf16_bits_to_f64
 from .quant import quant_1x128, quant_128x128
 from .gemm_bf16 import gemm_bf16_nt
 from .gemm_kgrouped import k_grouped_contiguous
+from .ue8m0 import gemm_nt_ue8m0, quant_1x128_ue8m0, quant_128x128_ue8m0
 from .gemm import (
     gemm_nt_acc,
     gemm_nt,
@@ -58,4 +60,7 @@ __all__ = [
     "grouped_masked",
     "gemm_bf16_nt",
     "k_grouped_contiguous",
+    "quant_1x128_ue8m0",
+    "quant_128x128_ue8m0",
+    "gemm_nt_ue8m0",
 ]
