@@ -61,7 +61,7 @@ enum {
 };
 
 /* Operation ids for dg_get_workspace_size. */
-enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2, DG_OP_BF16_GEMM_NT = 3 };
+enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2, DG_OP_BF16_GEMM_NT = 3, DG_OP_GEMM_NT_UE8M0 = 4 };
 
 /*
  * Dense GEMM.  Lesson 13, Fig. 13-1; DeepGEMM's "normal" GEMM (the Feb-2025
@@ -208,6 +208,32 @@ int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M,
  */
 int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t N, int64_t K,
                      void* stream);
+
+/*
+ * UE8M0 (power-of-two) scale variant.  Lesson 13 (the notes after Fig. 13-1):
+ * newer library versions accept UE8M0 scales besides fp32; deep-dive blog,
+ * section 3: on the newer architecture four UE8M0 scales are packed into one
+ * 32-bit integer.  Same granularity and per-128-K promotion as the fp32 form.
+ * A code c means 2^(c - 127); codes of four consecutive K blocks share one
+ * int32, block 4w + j in byte j (bits 8j..8j+7), unused bytes zero.
+ *   sfa [ceil(K/512)][M] int32 (MN-major, as the fp32 layout)
+ *   sfb [ceil(N/128)][ceil(K/512)] int32
+ * The quantisers choose c so that 2^(c-127) is the smallest power of two not
+ * below amax/448 (clamped to codes [0, 254]; an all-zero group gets 127) and
+ * write q = e4m3_RNE(x * 2^(127-c)), an exact power-of-two scaling.
+ * dg_fp8_gemm_nt_ue8m0: D [M,N] bf16 = A . B^T with those scales; the matrix
+ * cores apply the scales and add each K block's product to the fp32
+ * accumulator, rounded once.  workspace as for dg_fp8_gemm_nt (size from
+ * dg_get_workspace_size(DG_OP_GEMM_NT_UE8M0, M, N, K, 1)); problems whose
+ * byte offsets exceed 32 bits are rejected with DG_ERR_SHAPE.
+ */
+int dg_quant_1x128_ue8m0(const float* x, uint8_t* q, int32_t* sfa, int64_t G, int64_t M, int64_t K,
+                         void* stream);
+int dg_quant_128x128_ue8m0(const float* x, uint8_t* q, int32_t* sfb, int64_t G, int64_t N, int64_t K,
+                           void* stream);
+int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B, const int32_t* sfb,
+                         uint16_t* D, int64_t M, int64_t N, int64_t K, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that let `op` use its full K split for this shape (0 = none used). */
 size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G);

@@ -348,6 +348,50 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
   return ok();
 }
 
+int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B, const int32_t* sfb, uint16_t* D,
+                         int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if (M == 0) return ok();
+  if ((rc = check_operands(A, reinterpret_cast<const float*>(sfa), B, reinterpret_cast<const float*>(sfb), D)))
+    return rc;
+  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
+    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
+  if (!fits_persistent(1, M, N, K)) return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  DensePlan pl;
+  plan_persistent(pl, M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = reinterpret_cast<const float*>(sfa);  // packed UE8M0 words, read as such by the kernel
+  p.B = B;
+  p.sfb = reinterpret_cast<const float*>(sfb);
+  p.D = D;
+  p.ws = static_cast<float*>(workspace);
+  p.rows = M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = 1;
+  p.m_tiles = pl.m_tiles;
+  p.n_tiles = pl.n_tiles;
+  p.splits = 1;
+  p.kb_per_split = pl.kb_per_split;
+  p.dp_tiles = pl.dp_tiles;
+  p.sk_tiles = pl.sk_tiles;
+  p.sk_pieces = pl.sk_pieces;
+  p.sk_kb = pl.sk_kb;
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] gemm_nt_ue8m0 M=%lld N=%lld K=%lld grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                 (long long)M, (long long)N, (long long)K, pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
+                 pl.sk_pieces, pl.sk_kb);
+  const hipError_t e = dg::launch_gemm_persistent(dg::kDenseUe8m0, pl.grid, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                                         const float* C, float* D, const int32_t* ks, int64_t G, int64_t M,
                                         int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
@@ -579,7 +623,7 @@ int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M,
   int cus = 0;
   int rc = check_device(&cus);
   if (rc) return rc;
-  const hipError_t e = dg::launch_quant_1x128(x, q, sfa, G, M, K, static_cast<hipStream_t>(stream));
+  const hipError_t e = dg::launch_quant_1x128(x, q, sfa, G, M, K, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -596,14 +640,48 @@ int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t 
   int cus = 0;
   int rc = check_device(&cus);
   if (rc) return rc;
-  const hipError_t e = dg::launch_quant_128x128(x, q, sfb, G, N, K, static_cast<hipStream_t>(stream));
+  const hipError_t e = dg::launch_quant_128x128(x, q, sfb, G, N, K, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_quant_1x128_ue8m0(const float* x, uint8_t* q, int32_t* sfa, int64_t G, int64_t M, int64_t K, void* stream) {
+  if (K <= 0 || K % 128) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (G < 0 || M < 0) return fail(DG_ERR_SHAPE, "G and M must be >= 0");
+  if (G > ((int64_t)1 << 31) || M > ((int64_t)1 << 31) || G * M * (K / 128) > ((int64_t)1 << 35))
+    return fail(DG_ERR_SHAPE, "problem too large");
+  if (G == 0 || M == 0) return ok();
+  if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(DG_ERR_ALIGN, "x and q must be 16-byte aligned");
+  if (!aligned(sfa, 4)) return fail(DG_ERR_ALIGN, "sfa must be 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc) return rc;
+  const hipError_t e = dg::launch_quant_1x128(x, q, sfa, G, M, K, true, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_quant_128x128_ue8m0(const float* x, uint8_t* q, int32_t* sfb, int64_t G, int64_t N, int64_t K, void* stream) {
+  if (K <= 0 || K % 128) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (G < 0 || N < 0) return fail(DG_ERR_SHAPE, "G and N must be >= 0");
+  if (G > ((int64_t)1 << 31) || N > ((int64_t)1 << 31) || G * ceil_div(N, 128) * (K / 128) > ((int64_t)1 << 31) - 1)
+    return fail(DG_ERR_SHAPE, "problem too large");
+  if (G == 0 || N == 0) return ok();
+  if (!x || !q || !sfb) return fail(DG_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16)) return fail(DG_ERR_ALIGN, "x and q must be 16-byte aligned");
+  if (!aligned(sfb, 4)) return fail(DG_ERR_ALIGN, "sfb must be 4-byte aligned");
+  int cus = 0;
+  int rc = check_device(&cus);
+  if (rc) return rc;
+  const hipError_t e = dg::launch_quant_128x128(x, q, sfb, G, N, K, true, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
 size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G) {
   (void)G;
-  if (op != DG_OP_GEMM_NT && op != DG_OP_BF16_GEMM_NT) return 0;
+  if (op != DG_OP_GEMM_NT && op != DG_OP_BF16_GEMM_NT && op != DG_OP_GEMM_NT_UE8M0) return 0;
   if (rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128)) return 0;
   int cus = 0;
   int dev = -1;
@@ -613,10 +691,11 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   }
   (void)hipGetLastError();
   if (cus <= 0) cus = 256;
-  if (op == DG_OP_BF16_GEMM_NT) {
-    if (!fits_persistent(1, rows, N, 2 * K)) return 0;
+  if (op == DG_OP_BF16_GEMM_NT || op == DG_OP_GEMM_NT_UE8M0) {
+    const int64_t kb = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;  // bytes per operand row
+    if (!fits_persistent(1, rows, N, kb)) return 0;
     DensePlan pb;
-    plan_persistent(pb, rows, N, 2 * K, effective_cus(cus), (size_t)-1);
+    plan_persistent(pb, rows, N, kb, effective_cus(cus), (size_t)-1);
     return (dg::persistent_workspace_bytes(pb.sk_tiles, pb.sk_pieces) + 15) / 16 * 16;
   }
   const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1);

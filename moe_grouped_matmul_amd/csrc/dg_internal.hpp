@@ -42,7 +42,10 @@ struct GemmParams {
 // [rows][K] and B [N][K] shared by all groups, per-row 1x128 scales on both
 // operands (sfa [K/128][rows], sfb [K/128][N]) and one fp32 output
 // D[g] = C[g] + A[:, seg g] . B[:, seg g]^T per group.
-enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4, kKGrouped = 5 };
+// kDenseUe8m0: the dense schedule with UE8M0 scales packed four per int32
+// along K (sfa [ceil(KB/4)][rows], sfb [ceil(N/128)][ceil(KB/4)]), applied
+// by the matrix cores' block scaling.
+enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4, kKGrouped = 5, kDenseUe8m0 = 6 };
 
 // Tile configurations compiled for gfx950 (workgroup tile BM x BN, K step 128).
 enum TileCfg { kTile128x128 = 0, kTile64x128 = 1, kTile64x64 = 2, kNumTileCfgs = 3 };
@@ -90,9 +93,10 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
 // Enqueue the GEMM kernel (and the split-K reduction when p.splits > 1).
 hipError_t launch_gemm(int mode, int cfg, const GemmParams& p, int groups, hipStream_t stream);
 
-hipError_t launch_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K,
+// ue8m0: scales as packed UE8M0 codes (int32 words of four K blocks) instead of fp32
+hipError_t launch_quant_1x128(const float* x, uint8_t* q, void* sfa, int64_t G, int64_t M, int64_t K, bool ue8m0,
                               hipStream_t stream);
-hipError_t launch_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t N, int64_t K,
+hipError_t launch_quant_128x128(const float* x, uint8_t* q, void* sfb, int64_t G, int64_t N, int64_t K, bool ue8m0,
                                 hipStream_t stream);
 
 }  // namespace dg

@@ -40,6 +40,15 @@
 //     operands carry per-row scales: alpha as in the other forms, beta of the
 //     tile's 128 columns through a 6-slot LDS ring of its own.
 //
+// UE8M0 scales (dense): alpha and beta are powers of two given by their
+// exponent bytes, four K blocks per 32-bit word.  The matrix cores apply
+// them (v_mfma_scale_f32_16x16x128_f8f6f4, every 32-K sub-block of a row
+// given the row's byte), which is exact, and the promotion is one fp32 add of
+// the scaled block product per element.  Letting the MFMA accumulate into
+// the tile directly would be as precise (its accumulator input is added with
+// one rounding, outside the products' truncating alignment) but its register
+// constraints make the kernel spill.
+//
 // Main loop (one iteration = one K block of one tile): the three ring slots
 // are separate LDS arrays; iteration j's operands sit in slot j % 3.  A wave
 // reads all its fragments of iteration j, waits for its own loads of
@@ -90,6 +99,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   constexpr bool ACC = MODE == kDenseAcc;    // fp32 output D = C + A . B^T
   constexpr bool KG = MODE == kKGrouped;     // groups along K, per-column beta, fp32 D[g] = C[g] + ...
   constexpr bool F32OUT = ACC || KG;
+  constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
   constexpr int WGM = MODE == kContiguous ? 2 : 4;
   constexpr int WGN = MODE == kContiguous ? 4 : 2;
   constexpr int TM = 4;
@@ -135,6 +145,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int K = BF16 ? 2 * p.K : p.K;  // bytes per operand row
   const int N = p.N;
   const int KB = K >> 7;
+  const int KW = (KB + 3) >> 2;  // UE8M0: packed words (four K blocks) per scale row
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;  // dense: M; masked: max_m
   const int ngrp = MODE == kMasked ? p.G : 1;         // groups of A, alpha and D rows
@@ -197,7 +208,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int dp_tiles = MODE == kMasked || KG ? T : p.dp_tiles;  // tasks run as whole tiles
   const int P = p.sk_pieces;                               // pieces per tail tile (dense)
   const int n_dp = b < dp_tiles ? (dp_tiles - b + G - 1) / G : 0;
-  const bool has_tail = (MODE == kDense || BF16 || ACC) && b < p.sk_tiles * P;
+  const bool has_tail = (MODE == kDense || BF16 || ACC || UE) && b < p.sk_tiles * P;
   const int nseg = n_dp + (has_tail ? 1 : 0);
   if (nseg == 0) return;  // uniform over the workgroup
 
@@ -294,7 +305,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // ---- buffer resources over whole arrays (all groups); offsets are 32-bit
   const uint32_t a_bytes = (uint32_t)(ngrp * rows) * (uint32_t)K;
   const uint32_t b_bytes = (uint32_t)(nbgrp * N) * (uint32_t)K;
-  const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)KB * 4u;
+  const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)(UE ? KW : KB) * 4u;
   const uint32_t sb_bytes = KG ? (uint32_t)N * (uint32_t)KB * 4u : 0u;  // K-grouped beta [KB][N]
   const __amdgpu_buffer_rsrc_t rd = F32OUT ? make_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
                                         : make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
@@ -384,7 +395,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     else                                                                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                            \
           rs_, (DG_LDS void*)(bwave ? &bring[KG ? (bs_) : 0][(wave - 4) * 64] : PS_SS(st_) + wave * 64), 4,     \
-          is_soff, is_kb * (bwave ? N : rows) * 4, 0, 0);                                                  \
+          is_soff, (UE ? (is_kb >> 2) : is_kb) * (bwave ? N : rows) * 4, 0, 0);                             \
   } while (0)
 #define PS_ISSUE_END()                                                                                     \
   do {                                                                                                     \
@@ -425,7 +436,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   auto cp_setup = [&]() {
     int nblk = (cp_t.nt * BN + wn * 64) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
-    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_t.bgrp * NB + nblk) * KB);
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_t.bgrp * NB + nblk) * (UE ? KW : KB));
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
@@ -619,7 +630,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
       _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 3; ++k_) {                                         \
         if (k_ < TM * TN) {                                                                                \
-          t_[k_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[k_ / TM], AF[k_ % TM], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          if constexpr (UE) { /* alpha and beta applied by the matrix cores (exact powers of two) */       \
+            t_[k_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                                      \
+                BF[k_ / TM], AF[k_ % TM], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, bcode_, 0,                   \
+                __builtin_bit_cast(int, AL[k_ % TM]) >> ash_);                                             \
+          } else {                                                                                         \
+            t_[k_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[k_ / TM], AF[k_ % TM], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          }                                                                                                \
           if (KG && k_ % TM == 0)                                                                          \
             bt_[(k_ / TM) & 1] = *reinterpret_cast<const f32x4*>(&bring[KG ? (br_) : 0][KG ? wn * 64 + q * 16 + 4 * (k_ / TM) : 0]); \
           if (k_ < L_BLOCK) PS_ISSUE_LOAD(st_, bs_, k_); /* the block's loads, spread over the first steps */ \
@@ -632,9 +649,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
         if (k_ >= 3) {                                                                                     \
           const int kk_ = k_ - 3;                                                                          \
           f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
-          if constexpr (KG) t_[kk_] *= bt_[(kk_ / TM) & 1];                                                \
-          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
-            uk_[v_] = __builtin_fmaf(t_[kk_][v_], sc_[kk_ % TM], uk_[v_]);                                 \
+          if constexpr (UE) {                                                                              \
+            uk_ += t_[kk_]; /* the promotion: one fp32 add of the scaled block product */                 \
+          } else {                                                                                         \
+            if constexpr (KG) t_[kk_] *= bt_[(kk_ / TM) & 1];                                              \
+            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
+              uk_[v_] = __builtin_fmaf(t_[kk_][v_], sc_[kk_ % TM], uk_[v_]);                               \
+          }                                                                                                \
           /* keeps these FMAs in this step: instruction selection would sink them to the block's end */    \
           asm volatile("" : "+v"(uk_));                                                                    \
         }                                                                                                  \
@@ -662,7 +683,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   do {                                                                                                     \
     constexpr int st_ = (c_) % 3;                                                                          \
     const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = BF16 || KG ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                  \
+    const float beta_ = BF16 || KG || UE ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                            \
+    /* UE8M0: the iteration's codes sit in byte cp_kb % 4 of their packed words */                        \
+    const int ash_ = 8 * (cp_kb & 3);                                                                      \
+    const int bcode_ = UE && live_ ? __builtin_bit_cast(int, sfb_w[cp_kb >> 2]) >> ash_ : 0;              \
+    (void)ash_;                                                                                            \
+    (void)bcode_;                                                                                          \
     wait_vmcnt<L_BLOCK>();                                                                                 \
     wait_lgkmcnt0(); /* own reads of this slot done before anyone may refill it */                        \
     __builtin_amdgcn_s_barrier();                                                                          \
@@ -813,6 +839,8 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, false>), g, t, 0, stream, p);
   else if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous, false>), g, t, 0, stream, p);
+  else if (mode == kDenseUe8m0)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseUe8m0, false>), g, t, 0, stream, p);
   else
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense, false>), g, t, 0, stream, p);
   return hipGetLastError();

@@ -29,6 +29,7 @@ DG_OP_GEMM_NT = 0
 DG_OP_CONTIGUOUS = 1
 DG_OP_MASKED = 2
 DG_OP_BF16_GEMM_NT = 3
+DG_OP_GEMM_NT_UE8M0 = 4
 
 EXPORTED = (
     "dg_fp8_gemm_nt",
@@ -39,6 +40,9 @@ EXPORTED = (
     "dg_k_grouped_fp8_gemm_nt_contiguous",
     "dg_quant_1x128",
     "dg_quant_128x128",
+    "dg_quant_1x128_ue8m0",
+    "dg_quant_128x128_ue8m0",
+    "dg_fp8_gemm_nt_ue8m0",
     "dg_get_workspace_size",
     "dg_get_m_alignment_for_contiguous_layout",
     "dg_set_num_cus",
@@ -77,6 +81,9 @@ def load_library(path=None):
     lib.dg_k_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_quant_1x128.argtypes = [P, P, P, I64, I64, I64, P]
     lib.dg_quant_128x128.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.dg_quant_1x128_ue8m0.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.dg_quant_128x128_ue8m0.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_get_workspace_size.argtypes = [I, I64, I64, I64, I64]
     lib.dg_get_workspace_size.restype = SZ
     lib.dg_get_m_alignment_for_contiguous_layout.argtypes = []
@@ -85,7 +92,8 @@ def load_library(path=None):
     lib.dg_get_last_error.restype = ctypes.c_char_p
     lib.dg_version.restype = ctypes.c_char_p
     for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
-                 "dg_k_grouped_fp8_gemm_nt_contiguous", "dg_quant_1x128", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
+                 "dg_k_grouped_fp8_gemm_nt_contiguous", "dg_quant_1x128", "dg_quant_1x128_ue8m0",
+                 "dg_quant_128x128_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
                  "dg_get_m_alignment_for_contiguous_layout"):
         getattr(lib, name).restype = I
     if path is None:
@@ -327,3 +335,69 @@ def dg_quant_128x128(x, q, sfb, stream=None):
     if tuple(q.shape) != tuple(x.shape) or tuple(sfb.shape) != exp_s:
         raise ValueError("shape mismatch between x, q, sfb")
     _check(load_library().dg_quant_128x128(_ptr(x), _ptr(q), _ptr(sfb), G, N, K, _stream(stream)))
+
+
+def _kw(K):
+    return (K // 128 + 3) // 4
+
+
+def dg_quant_1x128_ue8m0(x, q, sfa, stream=None):
+    """x [M,K] or [G,M,K] fp32 -> q (uint8, same shape), sfa [(G,) ceil(K/512), M] int32 (UE8M0
+    codes of four K blocks per word, block 4w+j in byte j)."""
+    q = _bytes_view(q, "q")
+    _need(x, "x", torch.float32, x.dim())
+    _need(q, "q", torch.uint8, x.dim())
+    _need(sfa, "sfa", torch.int32, x.dim())
+    if x.dim() == 2:
+        G, (M, K) = 1, x.shape
+    elif x.dim() == 3:
+        G, M, K = x.shape
+    else:
+        raise ValueError("x must be [M,K] or [G,M,K]")
+    exp_s = (_kw(K), M) if x.dim() == 2 else (G, _kw(K), M)
+    if tuple(q.shape) != tuple(x.shape) or tuple(sfa.shape) != exp_s:
+        raise ValueError("shape mismatch between x, q, sfa")
+    _check(load_library().dg_quant_1x128_ue8m0(_ptr(x), _ptr(q), _ptr(sfa), G, M, K, _stream(stream)))
+
+
+def dg_quant_128x128_ue8m0(x, q, sfb, stream=None):
+    """x [N,K] or [G,N,K] fp32 -> q (uint8, same shape), sfb [(G,) ceil(N/128), ceil(K/512)] int32
+    (UE8M0 codes, four K blocks per word)."""
+    q = _bytes_view(q, "q")
+    _need(x, "x", torch.float32, x.dim())
+    _need(q, "q", torch.uint8, x.dim())
+    _need(sfb, "sfb", torch.int32, x.dim())
+    if x.dim() == 2:
+        G, (N, K) = 1, x.shape
+    elif x.dim() == 3:
+        G, N, K = x.shape
+    else:
+        raise ValueError("x must be [N,K] or [G,N,K]")
+    exp_s = ((N + 127) // 128, _kw(K)) if x.dim() == 2 else (G, (N + 127) // 128, _kw(K))
+    if tuple(q.shape) != tuple(x.shape) or tuple(sfb.shape) != exp_s:
+        raise ValueError("shape mismatch between x, q, sfb")
+    _check(load_library().dg_quant_128x128_ue8m0(_ptr(x), _ptr(q), _ptr(sfb), G, N, K, _stream(stream)))
+
+
+def dg_fp8_gemm_nt_ue8m0(A, sfa, B, sfb, D, workspace=None, stream=None):
+    """D[M,N] (bf16, written) = A[M,K] . B[N,K]^T with packed UE8M0 scales: sfa [ceil(K/512), M] int32,
+    sfb [ceil(N/128), ceil(K/512)] int32."""
+    A = _bytes_view(A, "A")
+    B = _bytes_view(B, "B")
+    D = _bf16_out(D)
+    _need(A, "A", torch.uint8, 2)
+    _need(B, "B", torch.uint8, 2)
+    _need(sfa, "sfa", torch.int32, 2)
+    _need(sfb, "sfb", torch.int32, 2)
+    _need(D, "D", D.dtype, 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(sfa.shape) != (_kw(K), M) or tuple(sfb.shape) != ((N + 127) // 128, _kw(K)) \
+            or tuple(D.shape) != (M, N):
+        raise ValueError("shape mismatch between A, sfa, B, sfb, D")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype, workspace.dim())
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().dg_fp8_gemm_nt_ue8m0(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), M, N, K,
+                                               _ptr(workspace), ws_bytes, _stream(stream)))
