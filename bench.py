@@ -106,7 +106,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc",
-                                                              "kgrouped"])
+                                                              "kgrouped", "ue8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -145,6 +145,26 @@ def time_graph(torch, timer, g, reps):
     e1 = timer.ev()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def timed_steps(torch, timer, step, args):
+    """Milliseconds per step (and wall seconds) over exactly args.steps steps,
+    step indices warmup .. warmup + steps - 1, captured into one HIP graph so
+    the GPU runs them back to back with no host or graph-launch gap between
+    steps; one untimed replay first, the timed replay bracketed by device
+    synchronisation."""
+    g = capture(torch, lambda: [step(args.warmup + i) for i in range(args.steps)])
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = timer.ev()
+    w0 = time.perf_counter()
+    g.replay()
+    t1 = timer.ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = t0.elapsed_time(t1) / args.steps
+    del g
+    return ms, wall
 
 
 PER_SHAPE_LAUNCHES = 16  # minimum launches per per-shape timing graph (cycling over the rotating buffer sets)
@@ -202,21 +222,8 @@ def run_dense(args, torch, dg, workloads):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # one graph per rotation index: replay i runs the whole step on buffer set i of every shape
-    n_graphs = max(len(p["sets"]) for p in prepared)
-    graphs = [capture(torch, lambda i=i: step(i)) for i in range(n_graphs)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    t_start = timer.ev()
-    w0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % n_graphs].replay()
-    t_end = timer.ev()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    del graphs
+    # step i runs on buffer set i (mod the set count) of every shape
+    ms_per_step, wall = timed_steps(torch, timer, step, args)
 
     # per-shape kernel times: graphs of back-to-back launches over the rotating sets
     per_shape = []
@@ -338,19 +345,7 @@ def run_grouped(args, torch, dg, workloads):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    n_graphs = max(len(p["sets"]) for p in prepared)
-    graphs = [capture(torch, lambda i=i: step(i)) for i in range(n_graphs)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    t_start = timer.ev()
-    w0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % n_graphs].replay()
-    t_end = timer.ev()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    del graphs
+    ms_per_step, wall = timed_steps(torch, timer, step, args)
     per_shape = []
     for p in prepared:
         launches = max(len(p["sets"]), 4)  # every set once per replay: cold HBM
@@ -431,16 +426,7 @@ def run_bf16(args, torch, dg, workloads):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    graphs = [capture(torch, lambda i=i: step(i)) for i in range(nsets)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    t0 = timer.ev()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % nsets].replay()
-    t1 = timer.ev()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    del graphs
+    ms_per_step, _ = timed_steps(torch, timer, step, args)
     flops = 2.0 * M * N * K
     nbytes = 2.0 * (M * K + N * K + M * N)
     us = ms_per_step * 1e3
@@ -490,16 +476,7 @@ def run_acc(args, torch, dg, workloads):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    graphs = [capture(torch, lambda i=i: step(i)) for i in range(nsets)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    t0 = timer.ev()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % nsets].replay()
-    t1 = timer.ev()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    del graphs
+    ms_per_step, _ = timed_steps(torch, timer, step, args)
     flops, nbytes = dense_work(M, N, K)
     nbytes += 6.0 * M * N  # fp32 C read and fp32 D written instead of bf16 D
     us = ms_per_step * 1e3
@@ -513,6 +490,57 @@ def run_acc(args, torch, dg, workloads):
                       kernel="fp8_gemm_persistent_kernel<acc>")]
     config = dict(workload="dense_fp8_nt_acc_4096x7168x16384", shapes=[f"{M}x{N}x{K}"], out="fp32 D = C + A.B^T",
                   step="dg_fp8_gemm_nt_acc (C = D, in place)", cold_hbm=True)
+    return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],
+                config=config)
+
+
+def run_ue8m0(args, torch, dg, workloads):
+    """Dense FP8 GEMM with UE8M0 (power-of-two) scales packed four per int32
+    at 4096 x 7168 x 16384: one step = one GEMM call over one rotating set."""
+    dev = torch.device("cuda:0")
+    M, N, K = 4096, 7168, 16384
+    KW = (K // 128 + 3) // 4
+    a32, b32 = workloads.dense(M, N, K, 200)
+    A32 = torch.from_numpy(a32).to(dev)
+    B32 = torch.from_numpy(b32).to(dev)
+    A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    SA = torch.empty((KW, M), dtype=torch.int32, device=dev)
+    B8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    SB = torch.empty(((N + 127) // 128, KW), dtype=torch.int32, device=dev)
+    dg.dg_quant_1x128_ue8m0(A32, A8, SA)
+    dg.dg_quant_128x128_ue8m0(B32, B8, SB)
+    del A32, B32
+    per_set = M * K + N * K + 2 * M * N
+    nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+    sets = [dict(a=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(), b=B8 if i == 0 else B8.clone(),
+                 sb=SB if i == 0 else SB.clone(), d=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+            for i in range(nsets)]
+    wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
+    ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
+    timer = Timer(torch)
+
+    def step(i):
+        st = sets[i % nsets]
+        dg.dg_fp8_gemm_nt_ue8m0(st["a"], st["sa"], st["b"], st["sb"], st["d"], ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step, _ = timed_steps(torch, timer, step, args)
+    flops = 2.0 * M * N * K
+    nbytes = float(M * K + N * K + 4 * M * KW + 4 * ((N + 127) // 128) * KW + 2 * M * N)
+    us = ms_per_step * 1e3
+    achieved = flops / us / 1e6
+    roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel="fp8_gemm_persistent_kernel<ue8m0>",
+                launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
+                algorithmic_flops_per_launch=round(flops))
+    per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1), gbs=round(nbytes / us / 1e3, 1),
+                      bound="mfma", roof_frac=round(roof_time_us(flops, nbytes) / us, 4),
+                      kernel="fp8_gemm_persistent_kernel<ue8m0>")]
+    config = dict(workload="dense_fp8_nt_ue8m0_4096x7168x16384", shapes=[f"{M}x{N}x{K}"],
+                  scales="UE8M0 1x128 activations, 128x128 weights, four codes per int32", out="bf16",
+                  step="dg_fp8_gemm_nt_ue8m0", cold_hbm=True)
     return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],
                 config=config)
 
@@ -573,17 +601,7 @@ def run_kgrouped(args, torch, dg, workloads):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    n_graphs = max(len(p["sets"]) for p in prepared)
-    graphs = [capture(torch, lambda i=i: step(i)) for i in range(n_graphs)]
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    t_start = timer.ev()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % n_graphs].replay()
-    t_end = timer.ev()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    del graphs
+    ms_per_step, _ = timed_steps(torch, timer, step, args)
     per_shape = []
     for p in prepared:
         launches = max(len(p["sets"]), 4)
@@ -637,8 +655,9 @@ def main():
         config = dict(workload=name, shapes=[f"{m}x{n}x{k}" for m, n, k in r["shapes"]],
                       scales="1x128 activations, 128x128 weights, fp32", out="bf16",
                       step="dg_quant_1x128 + dg_fp8_gemm_nt per shape", cold_hbm=True)
-    elif args.workload in ("bf16", "acc", "kgrouped"):
-        r = {"bf16": run_bf16, "acc": run_acc, "kgrouped": run_kgrouped}[args.workload](args, torch, dg, workloads)
+    elif args.workload in ("bf16", "acc", "kgrouped", "ue8m0"):
+        r = {"bf16": run_bf16, "acc": run_acc, "kgrouped": run_kgrouped, "ue8m0": run_ue8m0}[args.workload](
+            args, torch, dg, workloads)
         name = r["name"]
         config = r["config"]
     else:
