@@ -45,7 +45,8 @@ COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte cou
 # WRITE_SIZE counters (calibrated against a plain copy) and recorded together with
 # a hash of the kernel's sources: reported only while those sources are unchanged.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_dense_sweep.md")
-KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
+KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_matmul_amd/csrc/gemm_wide.hip",
+                  "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
                   "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/csrc/api.cpp",
                   "moe_grouped_matmul_amd/build.py")
 
@@ -201,8 +202,11 @@ def run_dense(args, torch, dg, workloads):
         wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K, 1)
         ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
         flops, nbytes = dense_work(M, N, K)
-        prepared.append(dict(M=M, N=N, K=K, sets=sets, ws=ws, flops=flops, bytes=nbytes,
-                             kernel="fp8_gemm_persistent_kernel<dense>" if M > 128 else "fp8_gemm_skinny_kernel"))
+        plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT, M, N, K, 1)
+        kernel = ("fp8_gemm_wide_kernel" if "kernel=wide" in plan else
+                  "fp8_gemm_persistent_kernel<dense>" if "kernel=persistent" in plan else
+                  "fp8_gemm_skinny_kernel" if "kernel=skinny" in plan else plan.split()[0] if plan else "?")
+        prepared.append(dict(M=M, N=N, K=K, sets=sets, ws=ws, flops=flops, bytes=nbytes, kernel=kernel))
     torch.cuda.synchronize()
     timer = Timer(torch)
 

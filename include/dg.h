@@ -238,6 +238,13 @@ int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
 /* Workspace bytes that let `op` use its full K split for this shape (0 = none used). */
 size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
 
+/* Text description of the launch plan the library would use for `op` at this
+ * shape on the current device with a full workspace, e.g. "kernel=wide
+ * tile=256x256 grid=256 tiles=448 whole=448 tail=0x1" (DG_OP_GEMM_NT only; ""
+ * for other ops or invalid shapes).  The pointer stays valid until the next
+ * call on the same thread. */
+const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
+
 /* Row alignment of expert segments in the contiguous layout (deep-dive blog,
  * section 3: contiguous segments aligned to the M block).  Always 128. */
 int dg_get_m_alignment_for_contiguous_layout(void);

@@ -21,11 +21,12 @@ LIB_NAME = "libdg_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "gemm.hip", "gemm_lds.hip", "gemm_skinny.hip", "gemm_persist.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_lds.hip", "gemm_skinny.hip", "gemm_persist.hip", "gemm_wide.hip", "api.cpp"]
 # per-source flags: the LDS-ring kernel needs the iterative ILP scheduler to
 # stay within 256 VGPRs (two waves per SIMD) without spilling
 SOURCE_FLAGS = {"gemm_lds.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-                "gemm_persist.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+                "gemm_persist.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+                "gemm_wide.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 COMMON = [
     "-O3",
     "--offload-arch=gfx950",

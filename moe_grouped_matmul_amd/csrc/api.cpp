@@ -95,6 +95,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // output alone has too few tiles.  Splits never exceed the K blocks.
 struct DensePlan {
   bool persist;  // persistent kernel (gemm_persist.hip), M > 128
+  bool wide;     // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
   int grid;      // persistent: workgroups
   int dp_tiles, sk_tiles, sk_pieces, sk_kb;
   bool lds;     // LDS-ring kernel (gemm_lds.hip)
@@ -163,9 +164,10 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
 // tile wins ties; with one, 16-column waves give the most tiles, and the split
 // is at most K / (16 bm) (the fp32 partials then stay below a quarter of the
 // weight bytes), at most 16, and only as large as the workspace holds.
-DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, bool allow_wide) {
   DensePlan pl;
   pl.persist = false;
+  pl.wide = false;
   pl.grid = 0;
   pl.dp_tiles = pl.sk_tiles = 0;
   pl.sk_pieces = 1;
@@ -209,6 +211,24 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) 
     return pl;
   }
   if (M > 128 && fits_persistent(1, M, N, K)) {
+    // 256 x 256 tiles stream a third fewer operand bytes per flop than the
+    // 256 x 128 ones; taken when they fill whole rounds of the CUs to at
+    // least 85% (the wide kernel has no K split for a partial round)
+    const int64_t tw = ceil_div(M, 256) * ceil_div(N, 256);
+    if (allow_wide && M >= 256 && N >= 256 && (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85) {
+      pl.persist = true;
+      pl.wide = true;
+      pl.m_tiles = (int)ceil_div(M, 256);
+      pl.n_tiles = (int)ceil_div(N, 256);
+      pl.grid = (int)(tw < cus ? tw : cus);
+      pl.splits = 1;
+      pl.kb_per_split = KB;
+      pl.dp_tiles = (int)tw;
+      pl.sk_tiles = 0;
+      pl.sk_pieces = 1;
+      pl.sk_kb = KB;
+      return pl;
+    }
     plan_persistent(pl, M, N, K, cus, ws_bytes);
     return pl;
   }
@@ -257,7 +277,7 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
     return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0, true);
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
@@ -280,9 +300,9 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   p.sk_kb = pl.sk_kb;
   if (std::getenv("DG_PRINT_CONFIGS") && pl.persist)
     std::fprintf(stderr,
-                 "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=persistent grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
-                 (long long)M, (long long)N, (long long)K, pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
-                 pl.sk_pieces, pl.sk_kb);
+                 "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                 (long long)M, (long long)N, (long long)K, pl.wide ? "wide" : "persistent", pl.grid,
+                 pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, pl.sk_kb);
   else if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=%s tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
                  (long long)M, (long long)N, (long long)K, pl.skinny ? "skinny" : (pl.lds ? "lds" : "v1"),
@@ -290,7 +310,9 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
                  pl.skinny ? 4 * pl.wn : (pl.lds ? dg::lds_tile_shape(pl.cfg).bn : dg::tile_shape(pl.cfg).bn),
                  pl.m_tiles, pl.n_tiles, pl.splits);
   hipError_t e;
-  if (pl.persist)
+  if (pl.wide)
+    e = dg::launch_gemm_wide(pl.grid, p, static_cast<hipStream_t>(stream));
+  else if (pl.persist)
     e = dg::launch_gemm_persistent(dg::kDense, pl.grid, p, static_cast<hipStream_t>(stream));
   else if (pl.skinny)
     e = dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream));
@@ -318,7 +340,7 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
     return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0, false);
   if (!pl.persist && !pl.skinny) return fail(DG_ERR_SHAPE, "problem too large for the accumulating form");
   if (pl.persist && M * N * 4 >= (int64_t)0xFFFFFF00 - 4096)
     return fail(DG_ERR_SHAPE, "fp32 output too large for 32-bit buffer offsets");
@@ -698,12 +720,42 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
     plan_persistent(pb, rows, N, kb, effective_cus(cus), (size_t)-1);
     return (dg::persistent_workspace_bytes(pb.sk_tiles, pb.sk_pieces) + 15) / 16 * 16;
   }
-  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1);
+  // sized for the 256 x 128 plan, which the accumulating form also uses
+  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, false);
   if (pl.persist) return (dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces) + 15) / 16 * 16;
   if (pl.splits <= 1) return 0;
   if (pl.skinny)
     return (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, pl.splits) + 15) / 16 * 16;
   return (size_t)pl.splits * (size_t)rows * (size_t)N * sizeof(float);
+}
+
+const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G) {
+  (void)G;
+  thread_local std::string text;
+  text.clear();
+  if (op != DG_OP_GEMM_NT || rows <= 0 || N <= 0 || K <= 0 || K % 128 || N % 16) return text.c_str();
+  int cus = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  }
+  (void)hipGetLastError();
+  if (cus <= 0) cus = 256;
+  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, true);
+  char buf[256];
+  if (pl.wide || pl.persist)
+    std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx%d grid=%d tiles=%d whole=%d tail=%dx%d",
+                  pl.wide ? "wide" : "persistent", 256, pl.wide ? 256 : 128, pl.grid, pl.m_tiles * pl.n_tiles,
+                  pl.dp_tiles, pl.sk_tiles, pl.sk_pieces);
+  else if (pl.skinny)
+    std::snprintf(buf, sizeof(buf), "kernel=skinny tile=%dx%d tiles=%d splits=%d", pl.cfg, 4 * pl.wn,
+                  pl.m_tiles * pl.n_tiles, pl.splits);
+  else
+    std::snprintf(buf, sizeof(buf), "kernel=%s tiles=%d splits=%d", pl.lds ? "lds" : "v1", pl.m_tiles * pl.n_tiles,
+                  pl.splits);
+  text = buf;
+  return text.c_str();
 }
 
 int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }

@@ -1,0 +1,299 @@
+// Wide-tile persistent block-scaled FP8 GEMM for gfx950 (dense form, bf16
+// output): one 512-thread workgroup per CU walks 256 x 256 output tiles.
+//
+// The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
+// closed-form equation: every 128-wide K block's fp8 partial product of a
+// tile is formed by the matrix cores and promoted into an fp32 accumulator
+// with alpha[row, k] * beta[k]; the epilogue rounds to bf16.
+//
+// Why a second persistent kernel: with 256 x 128 tiles each CU streams 48 KB
+// of operands per 8.4 MFLOP and the large shapes run at the rate one CU's
+// L2 request path sustains.  A 256 x 256 tile streams 64 KB per 16.8 MFLOP,
+// a third fewer bytes per flop.  Its cost is registers and LDS:
+//   * eight waves (two per SIMD), each a 64 x 128 sub-tile of 4 x 8
+//     v_mfma_f32_16x16x128_f8f6f4 tiles, 128 accumulator registers;
+//   * a two-slot LDS ring (64 KB of operands + 2 KB of alpha per slot; three
+//     slots would not fit): the loads of iteration j + 1 go to the other slot
+//     while iteration j computes, one s_barrier per iteration publishes them;
+//   * fragments are read from the slot of the running iteration: the four
+//     A fragments and the row scales after the barrier, the B fragments one
+//     ahead of their four MFMAs (two B registers sets alternate);
+//   * the promotion FMAs of each MFMA run three MFMAs later, as in the
+//     256 x 128 kernel (gemm_persist.hip), whose operand layout, swizzle, B
+//     row permutation and deferred bf16 store this kernel shares.
+// Tile walk: ids b, b + G, ... per workgroup, mapped so each XCD runs a
+// contiguous, m-grouped range of tiles.  No K split: used where the tiles
+// fill the CUs in whole or nearly whole rounds.
+
+#include "dg_internal.hpp"
+#include "gemm_common.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int kWideRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+constexpr uint32_t kWideOOB = 0xFFFFFF00u;  // an offset past every buffer range used here
+
+typedef unsigned int wu32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kWideRsrcWord3);
+}
+
+__global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int WGN = 2;
+  constexpr int TM = 4;
+  constexpr int TN = 8;
+  constexpr int BM = 256;
+  constexpr int BN = 256;
+  constexpr int NWAVES = 8;
+  constexpr int A_INS = BM / 8 / NWAVES;      // 1 KB (8-row) loads per wave per K block
+  constexpr int B_INS = BN / 8 / NWAVES;
+  constexpr int L_BLOCK = A_INS + B_INS + 1;  // + one alpha load per wave
+  constexpr int GM = 4;                       // m-tiles per tile group of the walk
+  constexpr int SLOT_S = (BM + BN) * 128;
+  constexpr int SLOT_BYTES = SLOT_S + NWAVES * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[SLOT_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN;
+  const int wn = wave % WGN;
+  const int q = lane >> 4;
+  const int q16 = lane & 15;
+  const int b = (int)blockIdx.x;
+  const int G = (int)gridDim.x;
+
+  const int K = p.K;
+  const int N = p.N;
+  const int KB = K >> 7;
+  const int NB = (N + 127) >> 7;
+  const int rows = (int)p.rows;
+  const int T = p.m_tiles * p.n_tiles;
+  const int nseg = b < T ? (T - b + G - 1) / G : 0;
+  if (nseg == 0) return;  // uniform over the workgroup
+  const int J = nseg * KB;
+
+  const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K;
+  const uint32_t s_bytes = (uint32_t)rows * (uint32_t)KB * 4u;
+  const __amdgpu_buffer_rsrc_t rd = wide_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
+
+  // DMA lanes (as gemm_persist.hip): instruction i of this wave fills LDS rows
+  // 64 i + 8 wave + lane / 8, lane chunk (lane % 8) of row r holding K chunk
+  // (lane % 8) ^ (r % 8); B rows permuted inside each 64-row block so each
+  // lane ends with 16 consecutive output columns of a 64-column half.
+  const int dma_chunk = ((lane & 7) ^ ((lane >> 3) & 7)) << 4;
+  const int a_loc = 8 * wave + (lane >> 3);
+  const int b_perm = ((a_loc & 15) >> 2) * 16 + 4 * (a_loc >> 4) + (a_loc & 3);
+  const uint32_t fr_lo = (uint32_t)(q16 * 128 + ((q ^ (lane & 7)) << 4));
+  const uint32_t fr_hi = (uint32_t)(q16 * 128 + (((q + 4) ^ (lane & 7)) << 4));
+  const uint32_t a_row0 = (uint32_t)(wm * 64 * 128);
+  const uint32_t b_row0 = (uint32_t)(BM * 128 + wn * 128 * 128);
+
+  auto tile_of = [&](int s, int* mt, int* nt) { grouped_mn(xcd_tile(b + s * G, T), p.m_tiles, p.n_tiles, GM, mt, nt); };
+
+#define WD_SLOT(st) ((st) == 0 ? slot0 : slot1)
+#define WD_SS(st) (reinterpret_cast<float*>(WD_SLOT(st) + SLOT_S))
+
+  // ---- issue pointer: iteration j + 1 of this workgroup's sequence
+  int is_seg = 0, is_kb = 0;
+  uint32_t is_aoff[A_INS], is_boff[B_INS], is_soff;
+  auto is_setup = [&]() {
+    int mt, nt;
+    tile_of(is_seg, &mt, &nt);
+    const int row_limit = rows - mt * BM < BM ? rows - mt * BM : BM;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = 64 * i + a_loc;
+      is_aoff[i] = r < row_limit ? (uint32_t)(mt * BM + r) * (uint32_t)K + dma_chunk : kWideOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int c = nt * BN + 64 * i + b_perm;
+      is_boff[i] = c < N ? (uint32_t)c * (uint32_t)K + dma_chunk : kWideOOB;
+    }
+    const int srow = wave * 64 + lane;  // alpha of the tile's rows that exist
+    is_soff = srow < BM && srow < row_limit ? (uint32_t)((mt * BM + srow) * 4) : kWideOOB;
+  };
+  is_setup();
+
+#define WD_ISSUE_BEGIN()                                                                                   \
+  const bool in_ = is_seg < nseg;                                                                          \
+  const __amdgpu_buffer_rsrc_t ra_ = wide_rsrc(p.A, in_ ? a_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rb_ = wide_rsrc(p.B, in_ ? b_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rs_ = wide_rsrc(p.sfa, in_ ? s_bytes : 0u);                                 \
+  const int ks_ = is_kb << 7
+#define WD_ISSUE_LOAD(st_, n_)                                                                             \
+  do {                                                                                                     \
+    if ((n_) < A_INS)                                                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(WD_SLOT(st_) + ((n_) * NWAVES + wave) * 1024), \
+                                               16, is_aoff[(n_) < A_INS ? (n_) : 0], ks_, 0, 0);           \
+    else if ((n_) < A_INS + B_INS)                                                                         \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                            \
+          rb_, (DG_LDS void*)(WD_SLOT(st_) + BM * 128 + ((n_) - A_INS) * NWAVES * 1024 + wave * 1024), 16,  \
+          is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0);                   \
+    else                                                                                                   \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(WD_SS(st_) + wave * 64), 4, is_soff,    \
+                                               is_kb * rows * 4, 0, 0);                                    \
+  } while (0)
+#define WD_ISSUE_END()                                                                                     \
+  do {                                                                                                     \
+    if (in_ && ++is_kb == KB) {                                                                            \
+      is_kb = 0;                                                                                           \
+      if (++is_seg < nseg) is_setup();                                                                     \
+    }                                                                                                      \
+  } while (0)
+
+  // ---- compute pointer: iteration j
+  int cp_seg = 0, cp_kb = 0;
+  int cp_mt, cp_nt;
+  tile_of(0, &cp_mt, &cp_nt);
+  const DG_CONST float* sfb_w;
+  auto cp_setup = [&]() {
+    int nblk = (cp_nt * BN + wn * 128) >> 7;
+    nblk = nblk < NB ? nblk : NB - 1;
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + (int64_t)nblk * KB);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
+  };
+  cp_setup();
+
+  f32x4 u[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) u[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // deferred bf16 store of a finished tile (after the next barrier): lane l
+  // of row tile i holds row wm*64 + 16 i + l % 16 and, in 64-column half h,
+  // columns wn*128 + 64 h + 16 q + [0, 16)
+  bool pend = false;
+  int st_row0 = 0, st_col0 = 0;
+#define WD_STORE_U()                                                                                       \
+  do {                                                                                                     \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
+      const int r_ = st_row0 + wm * 64 + i_ * 16 + q16;                                                    \
+      _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                                   \
+        const int c_ = st_col0 + wn * 128 + h_ * 64 + q * 16;                                              \
+        const uint32_t off_ = (r_ < rows && c_ < N) ? ((uint32_t)r_ * (uint32_t)N + (uint32_t)c_) * 2u : kWideOOB; \
+        uint32_t w_[8];                                                                                    \
+        _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                                 \
+          w_[2 * j_] = pack_bf16x2(u[i_][4 * h_ + j_][0], u[i_][4 * h_ + j_][1]);                          \
+          w_[2 * j_ + 1] = pack_bf16x2(u[i_][4 * h_ + j_][2], u[i_][4 * h_ + j_][3]);                      \
+        }                                                                                                  \
+        __builtin_amdgcn_raw_buffer_store_b128(wu32x4{w_[0], w_[1], w_[2], w_[3]}, rd, off_, 0, 0);        \
+        __builtin_amdgcn_raw_buffer_store_b128(wu32x4{w_[4], w_[5], w_[6], w_[7]}, rd,                     \
+                                               off_ == kWideOOB ? kWideOOB : off_ + 16u, 0, 0);            \
+      }                                                                                                    \
+    }                                                                                                      \
+  } while (0)
+
+#define WD_FRAG(dst_, base_, off_)                                                                         \
+  do {                                                                                                     \
+    const uint4 lo_ = *reinterpret_cast<const uint4*>((base_) + fr_lo + (off_));                          \
+    const uint4 hi_ = *reinterpret_cast<const uint4*>((base_) + fr_hi + (off_));                          \
+    dst_ = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w, (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w}; \
+  } while (0)
+
+  // One iteration jj_ in slot st_ (= jj_ % 2).  After the wait for this
+  // wave's loads of jj_ and the barrier (everyone's loads of jj_ landed,
+  // everyone done reading slot st_ ^ 1), a finished tile is stored, the A
+  // fragments, row scales and first B fragment of jj_ are read, and the 32
+  // MFMAs run j-major with the next B fragment read one fragment ahead, the
+  // block's loads for jj_ + 1 (into slot st_ ^ 1) in the first steps and the
+  // promotions three MFMAs behind.
+#define WD_STEP(st_, jj_)                                                                                  \
+  do {                                                                                                     \
+    const bool live_ = (jj_) < J;                                                                          \
+    const float beta_ = live_ ? sfb_w[cp_kb] : 0.f;                                                        \
+    wait_vmcnt<0>();                                                                                       \
+    wait_lgkmcnt0();                                                                                       \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    if (pend) {                                                                                            \
+      WD_STORE_U();                                                                                        \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_)                                                    \
+        _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_) u[i_][j_] = f32x4{0.f, 0.f, 0.f, 0.f};           \
+      pend = false;                                                                                        \
+    }                                                                                                      \
+    const uint8_t* sl_ = WD_SLOT(st_);                                                                     \
+    i32x8 af_[TM], bf_[2];                                                                                 \
+    float sc_[TM];                                                                                         \
+    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
+      WD_FRAG(af_[i_], sl_ + a_row0, i_ * 2048);                                                           \
+      sc_[i_] = WD_SS(st_)[wm * 64 + i_ * 16 + q16] * beta_;                                               \
+    }                                                                                                      \
+    WD_FRAG(bf_[0], sl_ + b_row0, 0);                                                                      \
+    {                                                                                                      \
+      WD_ISSUE_BEGIN();                                                                                    \
+      f32x4 t_[4];                                                                                         \
+      _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 3; ++k_) {                                         \
+        if (k_ < TM * TN) {                                                                                \
+          const int j_ = k_ / TM;                                                                          \
+          if (k_ % TM == 0 && j_ + 1 < TN) WD_FRAG(bf_[(j_ + 1) & 1], sl_ + b_row0, (j_ + 1) * 2048);      \
+          t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],          \
+                                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          if (k_ < L_BLOCK) WD_ISSUE_LOAD((st_) ^ 1, k_);                                                  \
+        }                                                                                                  \
+        if (k_ >= 3) {                                                                                     \
+          const int kk_ = k_ - 3;                                                                          \
+          f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
+          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
+            uk_[v_] = __builtin_fmaf(t_[kk_ & 3][v_], sc_[kk_ % TM], uk_[v_]);                             \
+          asm volatile("" : "+v"(uk_));                                                                    \
+        }                                                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                                 \
+      }                                                                                                    \
+      WD_ISSUE_END();                                                                                      \
+    }                                                                                                      \
+    if (live_ && ++cp_kb == KB) { /* a tile is done */                                                    \
+      st_row0 = cp_mt * BM;                                                                                \
+      st_col0 = cp_nt * BN;                                                                                \
+      pend = true;                                                                                         \
+      cp_kb = 0;                                                                                           \
+      if (++cp_seg < nseg) {                                                                               \
+        tile_of(cp_seg, &cp_mt, &cp_nt);                                                                   \
+        cp_setup();                                                                                        \
+      }                                                                                                    \
+    }                                                                                                      \
+  } while (0)
+
+  // prologue: iteration 0 into slot 0
+  {
+    WD_ISSUE_BEGIN();
+#pragma unroll
+    for (int n_ = 0; n_ < L_BLOCK; ++n_) WD_ISSUE_LOAD(0, n_);
+    WD_ISSUE_END();
+  }
+  for (int j = 0; j < J; j += 2) {
+    WD_STEP(0, j);
+    WD_STEP(1, j + 1);
+  }
+  if (pend) WD_STORE_U();
+  wait_vmcnt<0>();  // no LDS writes or stores in flight past this point
+  wait_lgkmcnt0();
+
+#undef WD_STEP
+#undef WD_FRAG
+#undef WD_STORE_U
+#undef WD_ISSUE_BEGIN
+#undef WD_ISSUE_LOAD
+#undef WD_ISSUE_END
+#undef WD_SS
+#undef WD_SLOT
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+}  // namespace
+
+hipError_t launch_gemm_wide(int grid, const GemmParams& p, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_gemm_wide_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dg

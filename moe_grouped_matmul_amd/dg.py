@@ -44,6 +44,7 @@ EXPORTED = (
     "dg_quant_128x128_ue8m0",
     "dg_fp8_gemm_nt_ue8m0",
     "dg_get_workspace_size",
+    "dg_describe_plan",
     "dg_get_m_alignment_for_contiguous_layout",
     "dg_set_num_cus",
     "dg_get_num_cus",
@@ -86,6 +87,8 @@ def load_library(path=None):
     lib.dg_fp8_gemm_nt_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_get_workspace_size.argtypes = [I, I64, I64, I64, I64]
     lib.dg_get_workspace_size.restype = SZ
+    lib.dg_describe_plan.argtypes = [I, I64, I64, I64, I64]
+    lib.dg_describe_plan.restype = ctypes.c_char_p
     lib.dg_get_m_alignment_for_contiguous_layout.argtypes = []
     lib.dg_set_num_cus.argtypes = [I]
     lib.dg_get_num_cus.argtypes = []
@@ -146,6 +149,11 @@ def _bf16_out(d, name="D"):
 
 def dg_get_workspace_size(op, rows, N, K, G=1):
     return int(load_library().dg_get_workspace_size(op, rows, N, K, G))
+
+
+def dg_describe_plan(op, rows, N, K, G=1):
+    """Text description of the launch plan for op at this shape (DG_OP_GEMM_NT only)."""
+    return load_library().dg_describe_plan(op, rows, N, K, G).decode()
 
 
 def dg_get_m_alignment_for_contiguous_layout():

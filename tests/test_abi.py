@@ -161,3 +161,23 @@ def test_product_path_never_imports_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), f
                 assert "import_module(\"oracle" not in src and "/oracle/" not in src, f
+
+
+def test_dense_planner_choice(lib):
+    # host logic only: 256 x 256 tiles when they fill whole rounds of the CUs
+    # to >= 85%, else 256 x 128 tiles with a K-split tail; M <= 128 skinny
+    from moe_grouped_matmul_amd import dg
+
+    try:
+        dg.dg_set_num_cus(256)
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)      # 448 tiles: 0.875
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 4096, 7168)       # 256 tiles: 1.0
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)  # 144 tiles: 0.56
+        assert "kernel=skinny" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 2048)
+        assert "tail=16x4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)
+        dg.dg_set_num_cus(4)
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 384)          # 4 tiles on 4 CUs
+        assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 100) == ""                      # invalid K
+        assert dg.dg_describe_plan(dg.DG_OP_MASKED, 500, 496, 384) == ""
+    finally:
+        dg.dg_set_num_cus(0)

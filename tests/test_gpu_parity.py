@@ -9,6 +9,8 @@ computes from its own quantisation of the same fp32 sources, after checking
 that the GPU bytes of those rows/blocks equal the oracle's.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -359,6 +361,60 @@ def test_dense_many_tiles_per_workgroup(few_cus, cus, M, N, K):
     ref = oracle.gemm_nt(qa, sa, qb, sb)
     for ws in (True, False):  # with a workspace the partial last round is split along K
         assert_close(_gpu_dense(qa, sa, qb, sb, M, N, K, ws), ref, f"dense {M}x{N}x{K} on {cus} CUs")
+
+
+def _planned_kernel(capfd, fn):
+    """Run fn with the planner's configuration printout on; return which dense kernel it chose."""
+    os.environ["DG_PRINT_CONFIGS"] = "1"
+    try:
+        capfd.readouterr()
+        fn()
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+    finally:
+        del os.environ["DG_PRINT_CONFIGS"]
+    return "wide" if "kernel=wide" in err else ("persistent" if "kernel=persistent" in err else "other")
+
+
+# (cus, M, N, K, kernel): 256 x 256 tiles are planned when they fill whole
+# rounds of the CUs to >= 85%, else 256 x 128 tiles with a K-split tail
+WIDE_CASES = [(1, 256, 256, 128, "wide"), (4, 512, 512, 640, "wide"), (4, 500, 496, 384, "wide"),
+              (3, 300, 608, 1024, "wide"), (7, 1000, 1792, 512, "wide"), (2, 1024, 272, 256, "wide"),
+              (7, 2048, 256, 1024, "persistent"), (5, 777, 400, 384, "persistent")]
+
+
+@pytest.mark.parametrize("cus,M,N,K,kernel", WIDE_CASES)
+def test_dense_wide_and_persistent_planning(few_cus, capfd, cus, M, N, K, kernel):
+    few_cus(cus)
+    a32, b32 = workloads.dense(M, N, K, seed=M + 2 * N + cus)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    out = {}
+    assert _planned_kernel(capfd, lambda: out.setdefault("d", _gpu_dense(qa, sa, qb, sb, M, N, K))) == kernel
+    assert_close(out["d"], oracle.gemm_nt(qa, sa, qb, sb), f"dense {M}x{N}x{K} on {cus} CUs ({kernel})")
+
+
+def test_dense_wide_deterministic_and_untouched_outside():
+    # the wide kernel writes exactly the M x N output (D sits inside a larger
+    # sentinel buffer) and repeats bit for bit
+    M, N, K = 500, 496, 384
+    dg.dg_set_num_cus(4)
+    try:
+        a32, b32 = workloads.dense(M, N, K, seed=5)
+        qa, sa = oracle.quant_1x128(a32)
+        qb, sb = oracle.quant_128x128(b32)
+        big = torch.full((M + 8, N), -1, dtype=torch.int16, device=DEV)
+        D = big[4:4 + M]
+        dg.dg_fp8_gemm_nt(_t(qa), _t(sa), _t(qb), _t(sb), D)
+        first = _np(D).copy()
+        dg.dg_fp8_gemm_nt(_t(qa), _t(sa), _t(qb), _t(sb), D)
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_num_cus(0)
+    assert np.array_equal(first, _np(D))
+    rest = big.cpu().numpy()
+    assert (rest[:4] == -1).all() and (rest[4 + M:] == -1).all()
+    assert_close(first, oracle.gemm_nt(qa, sa, qb, sb), "wide 500x496x384")
 
 
 @pytest.mark.parametrize("cus", [1, 4])
