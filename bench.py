@@ -44,7 +44,7 @@ COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte cou
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE counters (calibrated against a plain copy) and recorded together with
 # a hash of the kernel's sources: reported only while those sources are unchanged.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_dense_sweep.md")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_dense_sweep.md")
 KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_matmul_amd/csrc/gemm_wide.hip",
                   "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
                   "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/csrc/api.cpp",
