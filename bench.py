@@ -369,7 +369,12 @@ def run_grouped(args, torch, dg, workloads):
     else:
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
-    kname = "fp8_gemm_persistent_kernel<contiguous>" if args.workload == "contiguous" else "fp8_gemm_persistent_kernel<masked>"
+    if args.workload == "contiguous":
+        big_p = next(p for p in prepared if p["N"] == big["N"] and p["K"] == big["K"])
+        plan = dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, big_p["rows"], big_p["N"], big_p["K"], big_p["G"])
+        kname = "fp8_gemm_wide_kernel<contiguous>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<contiguous>"
+    else:
+        kname = "fp8_gemm_persistent_kernel<masked>"
     roof.update(traffic=None, kernel=f"{kname} ({big['N']}x{big['K']})",
                 avg_launch_us=big["gemm_us"])
     name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"

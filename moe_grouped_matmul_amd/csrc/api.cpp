@@ -261,6 +261,36 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, 
   return pl;
 }
 
+// Contiguous-form plan: the wide kernel (256 x 256 tiles) when K >= 4096,
+// its tiles fill whole rounds of the CUs to >= 85% and each workgroup's tiles
+// fit its pass table; else the persistent kernel over 128 x 256 tiles when
+// that fits.
+struct ContigPlan {
+  bool wide;
+  bool persist;
+  int grid;
+};
+ContigPlan plan_contiguous(int64_t M_total, int64_t N, int64_t K, int64_t G, int cus) {
+  ContigPlan cp{false, false, 0};
+  const bool fits = fits_persistent(1, M_total, N, K) && fits_persistent(G, 0, N, K);
+  const int64_t tw = ceil_div(M_total, 256) * ceil_div(N, 256);
+  const int64_t gw = tw < cus ? tw : cus;
+  // K >= 4096: with fewer K blocks per tile the second passes of tiles at
+  // expert boundaries and the per-tile overheads outweigh the wider tile
+  if (fits && M_total >= 256 && N >= 256 && K >= 4096 && ceil_div(tw, gw) <= dg::kWideMaxContigTiles &&
+      (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85) {
+    cp.wide = true;
+    cp.persist = true;
+    cp.grid = (int)gw;
+    return cp;
+  }
+  const int64_t ptiles = ceil_div(M_total, 128) * ceil_div(N, 256);
+  const int pgrid = (int)(ptiles < cus ? ptiles : cus);
+  cp.persist = fits && ceil_div(ptiles, pgrid) <= dg::kPersistentMaxContigTiles;
+  cp.grid = pgrid;
+  return cp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,7 +341,7 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
                  pl.m_tiles, pl.n_tiles, pl.splits);
   hipError_t e;
   if (pl.wide)
-    e = dg::launch_gemm_wide(pl.grid, p, static_cast<hipStream_t>(stream));
+    e = dg::launch_gemm_wide(dg::kDense, pl.grid, p, static_cast<hipStream_t>(stream));
   else if (pl.persist)
     e = dg::launch_gemm_persistent(dg::kDense, pl.grid, p, static_cast<hipStream_t>(stream));
   else if (pl.skinny)
@@ -532,14 +562,16 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  // 128 x 256 tiles: each tile lies inside one 128-row aligned expert
-  // segment.  The persistent kernel needs its 32-bit offsets to fit and each
-  // workgroup's tiles to fit its table of tile experts.
-  const int64_t ptiles = ceil_div(M_total, 128) * ceil_div(N, 256);
+  // 256 x 256 tiles (wide kernel, two passes where a tile straddles two
+  // experts) when they fill whole rounds of the CUs to >= 85%; otherwise
+  // 128 x 256 tiles, each inside one 128-row aligned expert segment.  Both
+  // need their 32-bit offsets to fit and each workgroup's tiles to fit its
+  // table.
   const int ecus = effective_cus(cus);
+  const ContigPlan cp = plan_contiguous(M_total, N, K, G, ecus);
+  const int64_t ptiles = ceil_div(M_total, 128) * ceil_div(N, 256);
   const int pgrid = (int)(ptiles < ecus ? ptiles : ecus);
-  const bool persist = fits_persistent(1, M_total, N, K) && fits_persistent(G, 0, N, K) &&
-                       ceil_div(ptiles, pgrid) <= dg::kPersistentMaxContigTiles;
+  const bool persist = cp.persist;
   const bool lds = persist || fits_32bit(M_total, N, K);
   const int bm = 128;
   const int bn = lds ? 256 : 128;
@@ -560,9 +592,14 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.kb_per_split = (int)(K / 128);
   if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d kernel=%s\n", (long long)M_total,
-                 (long long)N, (long long)K, (long long)G, bm, bn, persist ? "persistent" : "grid");
+                 (long long)N, (long long)K, (long long)G, cp.wide ? 256 : bm, bn,
+                 cp.wide ? "wide" : (persist ? "persistent" : "grid"));
   hipError_t e;
-  if (persist) {
+  if (cp.wide) {
+    p.m_tiles = (int)ceil_div(M_total, 256);
+    p.n_tiles = (int)ceil_div(N, 256);
+    e = dg::launch_gemm_wide(dg::kContiguous, cp.grid, p, static_cast<hipStream_t>(stream));
+  } else if (persist) {
     p.dp_tiles = (int)ptiles;  // every tile whole: no K-split tail, no workspace
     p.sk_tiles = 0;
     p.sk_pieces = 1;
@@ -733,7 +770,8 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   (void)G;
   thread_local std::string text;
   text.clear();
-  if (op != DG_OP_GEMM_NT || rows <= 0 || N <= 0 || K <= 0 || K % 128 || N % 16) return text.c_str();
+  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS) || rows <= 0 || N <= 0 || K <= 0 || K % 128 || N % 16)
+    return text.c_str();
   int cus = 0;
   int dev = -1;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
@@ -742,8 +780,15 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   }
   (void)hipGetLastError();
   if (cus <= 0) cus = 256;
-  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, true);
   char buf[256];
+  if (op == DG_OP_CONTIGUOUS) {
+    const ContigPlan cp = plan_contiguous(rows, N, K, G < 1 ? 1 : G, effective_cus(cus));
+    std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx256 grid=%d", cp.wide ? "wide" : (cp.persist ? "persistent" : "grid"),
+                  cp.wide ? 256 : 128, cp.grid);
+    text = buf;
+    return text.c_str();
+  }
+  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, true);
   if (pl.wide || pl.persist)
     std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx%d grid=%d tiles=%d whole=%d tail=%dx%d",
                   pl.wide ? "wide" : "persistent", 256, pl.wide ? 256 : 128, pl.grid, pl.m_tiles * pl.n_tiles,

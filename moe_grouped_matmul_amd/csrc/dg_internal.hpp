@@ -90,10 +90,13 @@ constexpr int kPersistentMaxContigTiles = 64;
 size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces);
 hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream);
 
-// Enqueue the wide-tile persistent kernel (gemm_wide.hip): dense form over
-// 256 x 256 tiles (p.m_tiles = ceil(M/256), p.n_tiles = ceil(N/256)), no K
-// split, `grid` workgroups; 32-bit offsets as for the persistent kernel.
-hipError_t launch_gemm_wide(int grid, const GemmParams& p, hipStream_t stream);
+// Enqueue the wide-tile persistent kernel (gemm_wide.hip): mode kDense or
+// kContiguous over 256 x 256 tiles (p.m_tiles = ceil(rows/256), p.n_tiles =
+// ceil(N/256)), no K split, `grid` workgroups; contiguous: at most
+// kWideMaxContigTiles tiles per workgroup; 32-bit offsets as for the
+// persistent kernel.
+constexpr int kWideMaxContigTiles = 64;
+hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t stream);
 
 // Enqueue the GEMM kernel (and the split-K reduction when p.splits > 1).
 hipError_t launch_gemm(int mode, int cfg, const GemmParams& p, int groups, hipStream_t stream);

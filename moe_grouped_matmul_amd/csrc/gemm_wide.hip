@@ -24,6 +24,17 @@
 // Tile walk: ids b, b + G, ... per workgroup, mapped so each XCD runs a
 // contiguous, m-grouped range of tiles.  No K split: used where the tiles
 // fill the CUs in whole or nearly whole rounds.
+//
+// M-grouped contiguous form (Lesson 13, Fig. 13-3, contiguous layout): only
+// aligned 128-row blocks are guaranteed to hold one expert, so a 256-row tile
+// may straddle two.  Every workgroup reads m_indices of its own tiles at
+// start and lists its passes in LDS: a tile whose two halves belong to one
+// expert (or whose other half has none) is one pass; a tile straddling two
+// experts is two passes, each with its expert's weights and storing only the
+// rows tagged with that expert; a tile without a valid index is none.  A
+// pass whose rows lie in one 128-row half runs the MFMAs of that half's four
+// waves only (each SIMD holds one wave of each half) and loads no A rows of
+// the other half, so a straddling tile costs about one full pass.
 
 #include "dg_internal.hpp"
 #include "gemm_common.hpp"
@@ -40,8 +51,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kWideRsrcWord3);
 }
 
+template <int MODE>
 __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool CONTIG = MODE == kContiguous;
+  constexpr int MAXT = kWideMaxContigTiles;  // tiles per workgroup the contiguous pass table holds
   constexpr int WGN = 2;
   constexpr int TM = 4;
   constexpr int TN = 8;
@@ -56,6 +70,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   constexpr int SLOT_BYTES = SLOT_S + NWAVES * 64 * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[SLOT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[SLOT_BYTES];
+  // contiguous: passes of this workgroup (tile id, expert, tagged-row mask)
+  // and, per tile, its pass count then first pass
+  __shared__ int pass_tile[CONTIG ? 2 * MAXT : 1];
+  __shared__ int pass_exp[CONTIG ? 2 * MAXT : 1];
+  __shared__ int pass_half[CONTIG ? 2 * MAXT : 1];  // bit h: rows of 128-row half h take part
+  __shared__ uint32_t pass_mask[CONTIG ? 2 * MAXT : 1][8];
+  __shared__ int tile_np[CONTIG ? MAXT + 1 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -73,12 +94,87 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;
   const int T = p.m_tiles * p.n_tiles;
-  const int nseg = b < T ? (T - b + G - 1) / G : 0;
-  if (nseg == 0) return;  // uniform over the workgroup
+  const int n_dp = b < T ? (T - b + G - 1) / G : 0;  // tiles of this workgroup
+  if (n_dp == 0) return;  // uniform over the workgroup
+  auto dense_tile = [&](int s, int* mt, int* nt) { grouped_mn(xcd_tile(b + s * G, T), p.m_tiles, p.n_tiles, GM, mt, nt); };
+
+  int nseg = n_dp;  // passes (dense: one per tile)
+  if constexpr (CONTIG) {
+    // m_indices of tile s's 256 rows: lane l holds rows 64 k + l, k < 4 (the
+    // first two in the lower 128-row half); -1 for rows past M or indices
+    // outside [0, G)
+    auto tile_idx = [&](int s, int* v) {
+      int mt, nt;
+      dense_tile(s, &mt, &nt);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = mt * BM + 64 * k + lane;
+        const int x = r < rows ? p.index[r] : -1;
+        v[k] = x >= 0 && x < p.G ? x : -1;
+      }
+    };
+    auto wave_max = [&](int x) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const int o = __shfl_xor(x, off);
+        x = o > x ? o : x;
+      }
+      return x;
+    };
+    for (int s = wave; s < n_dp; s += NWAVES) {
+      int v[4];
+      tile_idx(s, v);
+      const int e0 = wave_max(v[0] > v[1] ? v[0] : v[1]);
+      const int e1 = wave_max(v[2] > v[3] ? v[2] : v[3]);
+      if (lane == 0) tile_np[s] = (e0 < 0 && e1 < 0) ? 0 : ((e0 < 0 || e1 < 0 || e0 == e1) ? 1 : 2);
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix of the pass counts (n_dp <= MAXT = 64)
+      int c = lane < n_dp ? tile_np[lane] : 0;
+      const int own = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(c, off);
+        if (lane >= off) c += o;
+      }
+      if (lane < n_dp) tile_np[lane] = c - own;
+      if (lane == 63) tile_np[MAXT] = c;
+    }
+    __syncthreads();
+    for (int s = wave; s < n_dp; s += NWAVES) {
+      int v[4];
+      tile_idx(s, v);
+      const int e0 = wave_max(v[0] > v[1] ? v[0] : v[1]);
+      const int e1 = wave_max(v[2] > v[3] ? v[2] : v[3]);
+      const int first = tile_np[s];
+      const int np = (e0 < 0 && e1 < 0) ? 0 : ((e0 < 0 || e1 < 0 || e0 == e1) ? 1 : 2);
+      for (int pp = 0; pp < np; ++pp) {
+        const int e = np == 2 ? (pp == 0 ? e0 : e1) : (e0 > e1 ? e0 : e1);
+        const int hm = (e0 == e ? 1 : 0) | (e1 == e ? 2 : 0);
+        uint32_t m[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const unsigned long long bb = __ballot(v[k] == e);
+          m[2 * k] = (uint32_t)bb;
+          m[2 * k + 1] = (uint32_t)(bb >> 32);
+        }
+        if (lane == 0) {
+          pass_tile[first + pp] = s;
+          pass_exp[first + pp] = e;
+          pass_half[first + pp] = hm;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) pass_mask[first + pp][w] = m[w];
+        }
+      }
+    }
+    __syncthreads();
+    nseg = __builtin_amdgcn_readfirstlane(tile_np[MAXT]);
+    if (nseg == 0) return;  // no row of these tiles is tagged: nothing to store
+  }
   const int J = nseg * KB;
 
   const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
-  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K;
+  const uint32_t b_bytes = (uint32_t)(CONTIG ? p.G : 1) * (uint32_t)N * (uint32_t)K;
   const uint32_t s_bytes = (uint32_t)rows * (uint32_t)KB * 4u;
   const __amdgpu_buffer_rsrc_t rd = wide_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
 
@@ -94,7 +190,19 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const uint32_t a_row0 = (uint32_t)(wm * 64 * 128);
   const uint32_t b_row0 = (uint32_t)(BM * 128 + wn * 128 * 128);
 
-  auto tile_of = [&](int s, int* mt, int* nt) { grouped_mn(xcd_tile(b + s * G, T), p.m_tiles, p.n_tiles, GM, mt, nt); };
+  // pass s: tile (mt, nt), the expert whose weights it uses and the 128-row
+  // halves taking part (bit h for half h)
+  auto tile_of = [&](int s, int* mt, int* nt, int* e, int* hm) {
+    if constexpr (CONTIG) {
+      dense_tile(__builtin_amdgcn_readfirstlane(pass_tile[s]), mt, nt);
+      *e = __builtin_amdgcn_readfirstlane(pass_exp[s]);
+      *hm = __builtin_amdgcn_readfirstlane(pass_half[s]);
+    } else {
+      dense_tile(s, mt, nt);
+      *e = 0;
+      *hm = 3;
+    }
+  };
 
 #define WD_SLOT(st) ((st) == 0 ? slot0 : slot1)
 #define WD_SS(st) (reinterpret_cast<float*>(WD_SLOT(st) + SLOT_S))
@@ -103,21 +211,21 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   int is_seg = 0, is_kb = 0;
   uint32_t is_aoff[A_INS], is_boff[B_INS], is_soff;
   auto is_setup = [&]() {
-    int mt, nt;
-    tile_of(is_seg, &mt, &nt);
+    int mt, nt, e, hm;
+    tile_of(is_seg, &mt, &nt, &e, &hm);
     const int row_limit = rows - mt * BM < BM ? rows - mt * BM : BM;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int r = 64 * i + a_loc;
-      is_aoff[i] = r < row_limit ? (uint32_t)(mt * BM + r) * (uint32_t)K + dma_chunk : kWideOOB;
+      is_aoff[i] = r < row_limit && ((hm >> (r >> 7)) & 1) ? (uint32_t)(mt * BM + r) * (uint32_t)K + dma_chunk : kWideOOB;
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const int c = nt * BN + 64 * i + b_perm;
-      is_boff[i] = c < N ? (uint32_t)c * (uint32_t)K + dma_chunk : kWideOOB;
+      is_boff[i] = c < N ? (uint32_t)(e * N + c) * (uint32_t)K + dma_chunk : kWideOOB;
     }
     const int srow = wave * 64 + lane;  // alpha of the tile's rows that exist
-    is_soff = srow < BM && srow < row_limit ? (uint32_t)((mt * BM + srow) * 4) : kWideOOB;
+    is_soff = srow < BM && srow < row_limit && ((hm >> (srow >> 7)) & 1) ? (uint32_t)((mt * BM + srow) * 4) : kWideOOB;
   };
   is_setup();
 
@@ -150,13 +258,15 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 
   // ---- compute pointer: iteration j
   int cp_seg = 0, cp_kb = 0;
-  int cp_mt, cp_nt;
-  tile_of(0, &cp_mt, &cp_nt);
+  int cp_mt, cp_nt, cp_e, cp_hm;
+  tile_of(0, &cp_mt, &cp_nt, &cp_e, &cp_hm);
   const DG_CONST float* sfb_w;
+  bool cp_act;  // this wave's rows take part in the pass
   auto cp_setup = [&]() {
+    cp_act = !CONTIG || ((cp_hm >> (wm >> 1)) & 1);
     int nblk = (cp_nt * BN + wn * 128) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
-    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + (int64_t)nblk * KB);
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_e * NB + nblk) * KB);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
@@ -174,13 +284,16 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   // columns wn*128 + 64 h + 16 q + [0, 16)
   bool pend = false;
   int st_row0 = 0, st_col0 = 0;
+  uint32_t st_m[8] = {~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u};  // contiguous: rows tagged with the pass's expert
 #define WD_STORE_U()                                                                                       \
   do {                                                                                                     \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
-      const int r_ = st_row0 + wm * 64 + i_ * 16 + q16;                                                    \
+      const int rr_ = wm * 64 + i_ * 16 + q16;                                                             \
+      const int r_ = st_row0 + rr_;                                                                        \
+      const bool tag_ = !CONTIG || ((st_m[rr_ >> 5] >> (rr_ & 31)) & 1u);                                  \
       _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                                   \
         const int c_ = st_col0 + wn * 128 + h_ * 64 + q * 16;                                              \
-        const uint32_t off_ = (r_ < rows && c_ < N) ? ((uint32_t)r_ * (uint32_t)N + (uint32_t)c_) * 2u : kWideOOB; \
+        const uint32_t off_ = (r_ < rows && c_ < N && tag_) ? ((uint32_t)r_ * (uint32_t)N + (uint32_t)c_) * 2u : kWideOOB; \
         uint32_t w_[8];                                                                                    \
         _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                                                 \
           w_[2 * j_] = pack_bf16x2(u[i_][4 * h_ + j_][0], u[i_][4 * h_ + j_][1]);                          \
@@ -221,14 +334,18 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
       pend = false;                                                                                        \
     }                                                                                                      \
     const uint8_t* sl_ = WD_SLOT(st_);                                                                     \
-    i32x8 af_[TM], bf_[2];                                                                                 \
-    float sc_[TM];                                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
-      WD_FRAG(af_[i_], sl_ + a_row0, i_ * 2048);                                                           \
-      sc_[i_] = WD_SS(st_)[wm * 64 + i_ * 16 + q16] * beta_;                                               \
-    }                                                                                                      \
-    WD_FRAG(bf_[0], sl_ + b_row0, 0);                                                                      \
-    {                                                                                                      \
+    if (!cp_act) { /* no rows of this wave in the pass: only this wave's share of the loads */             \
+      WD_ISSUE_BEGIN();                                                                                    \
+      _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) WD_ISSUE_LOAD((st_) ^ 1, n_);                \
+      WD_ISSUE_END();                                                                                      \
+    } else {                                                                                               \
+      i32x8 af_[TM], bf_[2];                                                                               \
+      float sc_[TM];                                                                                       \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
+        WD_FRAG(af_[i_], sl_ + a_row0, i_ * 2048);                                                         \
+        sc_[i_] = WD_SS(st_)[wm * 64 + i_ * 16 + q16] * beta_;                                             \
+      }                                                                                                    \
+      WD_FRAG(bf_[0], sl_ + b_row0, 0);                                                                    \
       WD_ISSUE_BEGIN();                                                                                    \
       f32x4 t_[4];                                                                                         \
       _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 3; ++k_) {                                         \
@@ -253,10 +370,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     if (live_ && ++cp_kb == KB) { /* a tile is done */                                                    \
       st_row0 = cp_mt * BM;                                                                                \
       st_col0 = cp_nt * BN;                                                                                \
+      if (CONTIG) {                                                                                        \
+        _Pragma("unroll") for (int w_ = 0; w_ < 8; ++w_) st_m[w_] = __builtin_amdgcn_readfirstlane(pass_mask[cp_seg][w_]); \
+      }                                                                                                    \
       pend = true;                                                                                         \
       cp_kb = 0;                                                                                           \
       if (++cp_seg < nseg) {                                                                               \
-        tile_of(cp_seg, &cp_mt, &cp_nt);                                                                   \
+        tile_of(cp_seg, &cp_mt, &cp_nt, &cp_e, &cp_hm);                                                    \
         cp_setup();                                                                                        \
       }                                                                                                    \
     }                                                                                                      \
@@ -290,9 +410,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 
 }  // namespace
 
-hipError_t launch_gemm_wide(int grid, const GemmParams& p, hipStream_t stream) {
+hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fp8_gemm_wide_kernel, dim3((unsigned)grid), dim3(512), 0, stream, p);
+  if (mode == kContiguous)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -435,6 +435,33 @@ def test_contiguous_many_tiles_per_workgroup(few_cus, cus, counts, N, K):
     assert_close(got[~bad], ref[~bad], f"contiguous on {cus} CUs")
 
 
+# (cus, counts, N, K, kernel): 256 x 256 tiles (two half passes where a tile
+# straddles two experts) when K >= 4096 and they fill whole rounds to >= 85%
+CONTIG_WIDE = [(1, [130, 5, 300, 1, 256], 400, 4096, "wide"), (2, [256, 256, 100], 272, 4224, "wide"),
+               (4, [300, 256, 256], 528, 4096, "wide"), (3, [130, 5, 300, 1, 256], 400, 4096, "persistent"),
+               (1, [130, 5, 300, 1, 256], 400, 2048, "persistent")]
+
+
+@pytest.mark.parametrize("cus,counts,N,K,kernel", CONTIG_WIDE)
+def test_contiguous_wide_planning_and_passes(few_cus, capfd, cus, counts, N, K, kernel):
+    few_cus(cus)
+    G = len(counts)
+    w, qa, sa, qb, sb = _contig_small(counts, G, N, K, seed=sum(counts) + 7 * cus)
+    idx = w["m_indices"].copy()
+    if len(counts) == 3 and counts[0] == 300:
+        idx[:256] = -1          # a whole 256-row tile without a valid index: no pass
+        idx[300] = G + 1        # out of range inside a padded block: untouched
+    D = _sentinel(w["m_total"], N)
+    got_kernel = _planned_kernel(capfd, lambda: dg.dg_m_grouped_fp8_gemm_nt_contiguous(
+        _t(qa), _t(sa), _t(qb), _t(sb), D, _t(idx)))
+    assert got_kernel == kernel
+    got = _np(D)
+    ref = oracle.grouped_contiguous(qa, sa, qb, sb, idx, np.full((w["m_total"], N), SENTINEL, np.uint16))
+    bad = (idx < 0) | (idx >= G)
+    assert np.all(got[bad] == SENTINEL)
+    assert_close(got[~bad], ref[~bad], f"contiguous {counts} on {cus} CUs ({kernel})")
+
+
 @pytest.mark.parametrize("cus", [1, 5])
 def test_masked_many_tiles_per_workgroup(few_cus, cus):
     few_cus(cus)
