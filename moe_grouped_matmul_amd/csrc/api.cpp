@@ -162,8 +162,9 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
 // Skinny kernel (one workgroup per CU): column width and K split chosen so
 // the workgroups fill the CUs in whole rounds.  Without a split the wider
 // tile wins ties; with one, 16-column waves give the most tiles, and the split
-// is at most K / (16 bm) (the fp32 partials then stay below a quarter of the
-// weight bytes), at most 16, and only as large as the workspace holds.
+// is at most K / (20 bm) (the fp32 partials then stay below a fifth of the
+// weight bytes; more splits lose more in the fix-up than they gain), at most
+// 16, and only as large as the workspace holds.
 DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, bool allow_wide) {
   DensePlan pl;
   pl.persist = false;
@@ -192,7 +193,7 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, 
     int splits = 1;
     if (tiles < cus) {
       splits = (int)(cus / tiles);
-      const int cap = (int)(K / (16 * pl.cfg));  // partials (splits * bm * 4 B per column) <= K / 4
+      const int cap = (int)(K / (20 * pl.cfg));  // partials (splits * bm * 4 B per column) <= K / 5
       if (splits > cap) splits = cap;
       if (splits > 16) splits = 16;
       while (splits > 1 && (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes ||

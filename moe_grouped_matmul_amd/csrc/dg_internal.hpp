@@ -74,9 +74,11 @@ hipError_t launch_gemm_lds(int mode, int cfg, const GemmParams& p, hipStream_t s
 size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int splits);
 hipError_t launch_gemm_skinny(int bm, int wn, const GemmParams& p, hipStream_t stream);
 // K blocks in flight per wave (ring depth; LDS per slot is (bm + 4 wn) * 128 B
-// plus 1 KB, one workgroup per CU); a split's block count is padded to a
-// multiple of it (padding blocks read as zeros), so splits should be multiples
-constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? (wn == 16 ? 8 : 4) : (wn == 16 ? 6 : 4); }
+// plus 1 KB); a split's block count is padded to a multiple of it (padding
+// blocks read as zeros), so splits should be multiples.  Four slots for 64-row
+// tiles of 16-column waves (about 70 KB, two workgroups per CU) measured
+// faster than eight (one per CU) on every decode shape tried.
+constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? 4 : (wn == 16 ? 6 : 4); }
 
 // Enqueue the persistent kernel (gemm_persist.hip) with `grid` workgroups (one
 // per CU): mode kDense over 256x128 tiles (tail tiles split along K when
