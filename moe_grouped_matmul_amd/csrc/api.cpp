@@ -649,13 +649,15 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   p.N = (int)N;
   p.K = (int)K;
   p.G = (int)G;
-  p.m_tiles = (int)ceil_div(max_m, ts.bm);
-  p.n_tiles = (int)ceil_div(N, ts.bn);
+  // the persistent kernel runs 128 x 256 tiles
+  p.m_tiles = (int)ceil_div(max_m, persist ? 128 : ts.bm);
+  p.n_tiles = (int)ceil_div(N, persist ? 256 : ts.bn);
   p.splits = 1;
   p.kb_per_split = (int)(K / 128);
   if (std::getenv("DG_PRINT_CONFIGS"))
     std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=%dx%d kernel=%s\n", (long long)G,
-                 (long long)max_m, (long long)N, (long long)K, ts.bm, ts.bn, persist ? "persistent" : "grid");
+                 (long long)max_m, (long long)N, (long long)K, persist ? 128 : ts.bm, persist ? 256 : ts.bn,
+                 persist ? "persistent" : "grid");
   hipError_t e;
   if (persist) {
     const int64_t tiles = G * p.m_tiles * p.n_tiles;

@@ -1,7 +1,8 @@
 // Persistent block-scaled FP8 GEMM for gfx950 (and, in mode kDenseBf16, the
 // plain BF16 GEMM on the same schedule): one 512-thread workgroup per
-// CU walks a list of output tiles (256 x 128; 128 x 256 for the contiguous
-// form, whose aligned 128-row blocks each belong to one expert) with one
+// CU walks a list of output tiles (256 x 128; 128 x 256 for the M-grouped
+// forms: an aligned 128-row block of the contiguous form belongs to one
+// expert, and a masked expert's rows fill fewer padded MFMA rows) with one
 // continuous LDS ring, so the next tile's first K blocks load while the
 // current tile finishes and stores.  Used for the dense form with M > 128 and
 // for the two M-grouped forms.
@@ -27,9 +28,10 @@
 //     that expert, and only the masked rows are stored;
 //   * masked (Lesson 13, Fig. 13-3, masked layout): every workgroup reads
 //     masked_m on the device and builds the prefix sums of the active tiles
-//     per group, sum_g ceil(masked_m[g] / 256) * ceil(N / 128); task ids are
-//     walked round-robin and located by binary search, so only the rows below
-//     masked_m are computed and the launch shape is fixed (graph-capturable);
+//     per group, sum_g ceil(masked_m[g] / 128) * ceil(N / 256); task ids are
+//     walked round-robin and located by binary search, so only the 128-row
+//     tiles holding rows below masked_m are computed, only those rows are
+//     loaded and stored, and the launch shape is fixed (graph-capturable);
 //   * K-grouped (the weight-gradient family of the deep-dive blog, section 3):
 //     every workgroup reads the group lengths ks on the device and builds the
 //     first K block of each group; the tiles of all groups are walked in
@@ -100,8 +102,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   constexpr bool KG = MODE == kKGrouped;     // groups along K, per-column beta, fp32 D[g] = C[g] + ...
   constexpr bool F32OUT = ACC || KG;
   constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
-  constexpr int WGM = MODE == kContiguous ? 2 : 4;
-  constexpr int WGN = MODE == kContiguous ? 4 : 2;
+  // 128-row tiles for the grouped forms: a contiguous 128-row block belongs to
+  // one expert, and a masked expert's rows fill fewer padded MFMA rows
+  constexpr int WGM = MODE == kContiguous || MODE == kMasked ? 2 : 4;
+  constexpr int WGN = MODE == kContiguous || MODE == kMasked ? 4 : 2;
   constexpr int TM = 4;
   constexpr int TN = 4;
   constexpr int BM = WGM * 64;
@@ -432,7 +436,6 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   Seg cp_t = seg_of(0);
   int cp_kb = cp_t.kb_lo;
   const DG_CONST float* sfb_w;
-  int act;
   auto cp_setup = [&]() {
     int nblk = (cp_t.nt * BN + wn * 64) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
@@ -440,9 +443,6 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
-    int a_ = (cp_t.row_limit - wm * 64 + 15) >> 4;  // 16-row MFMA tiles holding stored rows
-    a_ = a_ < 0 ? 0 : (a_ > TM ? TM : a_);
-    act = __builtin_amdgcn_readfirstlane(a_);
   };
   cp_setup();
 
@@ -585,8 +585,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   // i = k % 4), one 16-byte LDS read of the next fragments (and, in the first steps,
   // one of the block's loads) and the four promotion FMAs of the MFMA three
   // steps back, so the LDS reads and the FMAs
-  // overlap the matrix cores.  Masked: all reads first, then the MFMAs of the
-  // 16-row tiles holding rows below masked_m.
+  // overlap the matrix cores.
 #define PS_COMPUTE(st_, bs_, br_, AF, BF, AL, AN, BN_, ALN)                                                \
   do {                                                                                                     \
     float sc_[TM];                                                                                         \
@@ -594,34 +593,6 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     if constexpr (BF16) {                                                                                  \
       PS_COMPUTE_BF16(st_, bs_, AF, BF, AN, BN_);                                                          \
       (void)sc_;                                                                                           \
-    } else if constexpr (MODE == kMasked) {                                                                       \
-      const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
-      uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
-      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) ALN[i_] = PS_SS(((st_) + 1) % 3)[wm * 64 + i_ * 16 + q16]; \
-      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
-        _Pragma("unroll") for (int h_ = 0; h_ < 4; ++h_) {                                                 \
-          const int k_ = 4 * i_ + h_;                                                                      \
-          const int f_ = k_ >> 1;                                                                          \
-          const uint32_t o_ = (f_ < TM ? a_row0 + f_ * 2048 : BM * 128 + b_row0 + (f_ - TM) * 2048) +      \
-                              ((k_ & 1) ? fr_hi : fr_lo);                                                  \
-          if (k_ & 1) nhi_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                               \
-          else nlo_[f_] = *reinterpret_cast<const uint4*>(nsl_ + o_);                                      \
-        }                                                                                                  \
-        if (i_ < act) { /* 16-row tiles holding rows below masked_m */                                     \
-          f32x4 t_[TN];                                                                                    \
-          _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                \
-            t_[j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(BF[j_], AF[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
-          _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                \
-            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
-              u[i_][j_][v_] = __builtin_fmaf(t_[j_][v_], sc_[i_], u[i_][j_][v_]);                          \
-        }                                                                                                  \
-      }                                                                                                    \
-      _Pragma("unroll") for (int f_ = 0; f_ < TM + TN; ++f_) {                                             \
-        const i32x8 v8_ = i32x8{(int)nlo_[f_].x, (int)nlo_[f_].y, (int)nlo_[f_].z, (int)nlo_[f_].w,        \
-                                (int)nhi_[f_].x, (int)nhi_[f_].y, (int)nhi_[f_].z, (int)nhi_[f_].w};       \
-        if (f_ < TM) AN[f_] = v8_;                                                                         \
-        else BN_[f_ - TM] = v8_;                                                                           \
-      }                                                                                                    \
     } else {                                                                                               \
       const uint8_t* nsl_ = PS_SLOT(((st_) + 1) % 3);                                                      \
       uint4 nlo_[TM + TN], nhi_[TM + TN];                                                                  \
@@ -700,9 +671,6 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     }                                                                                                      \
     {                                                                                                      \
       PS_ISSUE_BEGIN();                                                                                    \
-      if constexpr (MODE == kMasked) {                                                                     \
-        _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) PS_ISSUE_LOAD(st_, (c_ + 3) % 6, n_);      \
-      }                                                                                                    \
       PS_COMPUTE(st_, (c_ + 3) % 6, c_, AF, BF, AL, AN, BN_, ALN);                                         \
       PS_ISSUE_END();                                                                                      \
     }                                                                                                      \
