@@ -188,12 +188,29 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, 
     const int64_t t32 = pl.m_tiles * ceil_div(N, 128);
     auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
     pl.wn = (t16 >= cus && fill(t32) >= fill(t16)) ? 32 : 16;
+    int cap_rows = pl.cfg;  // K split capped at K / (20 * cap_rows): partials (splits * bm * 4 B per column) <= K / 5
+    // 64 < M <= 128 with two 64-row tiles: each streams all of A beside its
+    // columns of B; one 128 x 128 tile halves those A reads, and wins where it
+    // still fills the CUs through a K split (partials then up to K / 2.5 per column)
+    if (M > 64 && pl.cfg == 64) {
+      const int64_t t128 = ceil_div(N, 128);
+      int64_t s128 = t128 < cus ? cus / t128 : 1;
+      if (s128 > K / 1280) s128 = K / 1280;
+      if (s128 > 16) s128 = 16;
+      if (s128 >= 2 && (double)(t128 * s128) >= 0.85 * cus &&
+          dg::skinny_workspace_bytes(128, 1, (int)t128, 32, (int)s128) <= ws_bytes) {
+        pl.cfg = 128;
+        pl.m_tiles = 1;
+        pl.wn = 32;
+        cap_rows = 64;
+      }
+    }
     pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
     const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
     int splits = 1;
     if (tiles < cus) {
       splits = (int)(cus / tiles);
-      const int cap = (int)(K / (20 * pl.cfg));  // partials (splits * bm * 4 B per column) <= K / 5
+      const int cap = (int)(K / (20 * cap_rows));
       if (splits > cap) splits = cap;
       if (splits > 16) splits = 16;
       while (splits > 1 && (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes ||

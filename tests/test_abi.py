@@ -174,6 +174,11 @@ def test_dense_planner_choice(lib):
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 4096, 7168)       # 256 tiles: 1.0
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)  # 144 tiles: 0.56
         assert "kernel=skinny" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 2048)
+        # 64 < M <= 128: a 128 x 128 tile when it still fills the CUs through a K split
+        assert "tile=128x128 tiles=56 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 16384)
+        assert "tile=128x128 tiles=56 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 100, 7168, 5120)
+        assert "tile=64x64" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 4096, 7168)
+        assert "tile=64x64" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 16384)
         assert "tail=16x4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)
         dg.dg_set_num_cus(4)
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 384)          # 4 tiles on 4 CUs

@@ -189,7 +189,8 @@ def test_dense_deterministic_and_nan_rows_contained():
 # block count is not a multiple of the ring depth, and one workspace reused
 # across calls (its split counters must come back to zero after every call)
 SKINNY = [(1, 2112, 7168), (17, 144, 1024), (64, 2112, 7168), (100, 272, 4096), (128, 2112, 7168),
-          (64, 4096, 640), (128, 32768, 512), (33, 24576, 1536), (64, 7168, 2048)]
+          (64, 4096, 640), (128, 32768, 512), (33, 24576, 1536), (64, 7168, 2048),
+          (100, 7168, 5120)]  # the last: one 128-row tile of 128 columns, K split in 4
 
 
 # persistent kernel (M > 128): tile counts that leave a partial last round, so
