@@ -44,7 +44,10 @@ COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte cou
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE counters (calibrated against a plain copy) and recorded together with
 # a hash of the kernel's sources: reported only while those sources are unchanged.
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_dense_sweep.md")
+TRAFFIC_RECORDS = {
+    "sweep": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_dense_sweep.md"),
+    "masked": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_masked_4096x7168.md"),
+}
 KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_matmul_amd/csrc/gemm_wide.hip",
                   "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
                   "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/csrc/api.cpp",
@@ -64,8 +67,10 @@ def kernel_source_hash():
 def recorded_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter record, or None when the
     record is missing, is for another kernel/workload, or predates the sources."""
+    if workload not in TRAFFIC_RECORDS:
+        return None
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(TRAFFIC_RECORDS[workload]) as f:
             fields = dict(l.strip()[2:].split(": ", 1) for l in f if l.startswith("- ") and ": " in l)
     except OSError:
         return None
@@ -109,7 +114,9 @@ def parse():
     ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc",
                                                               "kgrouped", "ue8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--shapes", default="", help="comma-separated indices into the sweep (default: all 18)")
+    ap.add_argument("--shapes", default="",
+                    help="comma-separated indices into the workload's shape list (default: all; the sweep has 18, "
+                         "the grouped workloads 2)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -280,6 +287,8 @@ def run_grouped(args, torch, dg, workloads):
     grouped GEMM calls."""
     dev = torch.device("cuda:0")
     cfgs = workloads.CONFIGS[args.workload]
+    if args.shapes:
+        cfgs = [cfgs[int(i)] for i in args.shapes.split(",")]
     prepared = []
     for c in cfgs:
         G, N, K = c["G"], c["N"], c["K"]
@@ -369,13 +378,15 @@ def run_grouped(args, torch, dg, workloads):
     else:
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
+    big_p = next(p for p in prepared if p["N"] == big["N"] and p["K"] == big["K"])
     if args.workload == "contiguous":
-        big_p = next(p for p in prepared if p["N"] == big["N"] and p["K"] == big["K"])
         plan = dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, big_p["rows"], big_p["N"], big_p["K"], big_p["G"])
         kname = "fp8_gemm_wide_kernel<contiguous>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<contiguous>"
     else:
         kname = "fp8_gemm_persistent_kernel<masked>"
-    roof.update(traffic=None, kernel=f"{kname} ({big['N']}x{big['K']})",
+    label = f"{kname} ({big['N']}x{big['K']})"
+    roof.update(traffic=recorded_traffic(label, args.workload), kernel=label,
+                algorithmic_bytes_per_launch=round(big_p["bytes"]),
                 avg_launch_us=big["gemm_us"])
     name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
     config = dict(workload=name, shapes=[f"G={p['G']} N={p['N']} K={p['K']}" for p in prepared],
