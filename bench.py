@@ -19,7 +19,9 @@ Output: one JSON line with the whole-step FP8 TFLOPS, per-shape GEMM TFLOPS,
 GB/s and fraction of the MI355X roofline, the dominant kernel's roofline, and
 the CPU oracle timed on a bounded sample of the same workload.
 
-Other workloads for profiling: --workload large | contiguous | masked | small.
+Other workloads: --workload large | small (one dense shape), contiguous | masked
+(the M-grouped forms), bf16 | acc | kgrouped | ue8m0 (the BF16, accumulating,
+K-grouped and UE8M0-scale variants).
 """
 
 import argparse
@@ -649,8 +651,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the FP8 GEMM path is a per-GPU kernel and multi-GPU runs are not part of it", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): the FP8 GEMM "
+              "path is a per-GPU kernel, and runs over several GPUs are not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
 
