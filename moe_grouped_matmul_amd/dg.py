@@ -131,6 +131,9 @@ def _bytes_view(t, name):
 def _need(t, name, dtype, ndim):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the library runs on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if t.dim() != ndim:
