@@ -553,13 +553,15 @@ def run_ue8m0(args, torch, dg, workloads):
     nbytes = float(M * K + N * K + 4 * M * KW + 4 * ((N + 127) // 128) * KW + 2 * M * N)
     us = ms_per_step * 1e3
     achieved = flops / us / 1e6
+    plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
+    kname = "fp8_gemm_wide_kernel<ue8m0>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<ue8m0>"
     roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
-                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel="fp8_gemm_persistent_kernel<ue8m0>",
+                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel=kname,
                 launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
                 algorithmic_flops_per_launch=round(flops))
     per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1), gbs=round(nbytes / us / 1e3, 1),
                       bound="mfma", roof_frac=round(roof_time_us(flops, nbytes) / us, 4),
-                      kernel="fp8_gemm_persistent_kernel<ue8m0>")]
+                      kernel=kname)]
     config = dict(workload="dense_fp8_nt_ue8m0_4096x7168x16384", shapes=[f"{M}x{N}x{K}"],
                   scales="UE8M0 1x128 activations, 128x128 weights, four codes per int32", out="bf16",
                   step="dg_fp8_gemm_nt_ue8m0", cold_hbm=True)

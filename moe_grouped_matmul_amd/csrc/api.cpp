@@ -93,6 +93,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Dense split-K plan: enough work items to cover the CUs twice when the
 // output alone has too few tiles.  Splits never exceed the K blocks.
+// 256 x 256 tiles (gemm_wide.hip, no K split) stream a third fewer operand
+// bytes per flop than 256 x 128 ones; taken when they fill whole rounds of
+// the CUs to at least 85%.
+bool wide_fill(int64_t M, int64_t N, int cus) {
+  if (M < 256 || N < 256) return false;
+  const int64_t tw = ceil_div(M, 256) * ceil_div(N, 256);
+  return (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85;
+}
+
 struct DensePlan {
   bool persist;  // persistent kernel (gemm_persist.hip), M > 128
   bool wide;     // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
@@ -229,11 +238,8 @@ DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, 
     return pl;
   }
   if (M > 128 && fits_persistent(1, M, N, K)) {
-    // 256 x 256 tiles stream a third fewer operand bytes per flop than the
-    // 256 x 128 ones; taken when they fill whole rounds of the CUs to at
-    // least 85% (the wide kernel has no K split for a partial round)
     const int64_t tw = ceil_div(M, 256) * ceil_div(N, 256);
-    if (allow_wide && M >= 256 && N >= 256 && (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85) {
+    if (allow_wide && wide_fill(M, N, cus)) {
       pl.persist = true;
       pl.wide = true;
       pl.m_tiles = (int)ceil_div(M, 256);
@@ -433,7 +439,21 @@ int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
   DensePlan pl;
-  plan_persistent(pl, M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  const int ecus = effective_cus(cus);
+  const bool wide = wide_fill(M, N, ecus);
+  if (wide) {
+    pl.m_tiles = (int)ceil_div(M, 256);
+    pl.n_tiles = (int)ceil_div(N, 256);
+    const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
+    pl.grid = (int)(tw < ecus ? tw : ecus);
+    pl.kb_per_split = (int)(K / 128);
+    pl.dp_tiles = (int)tw;
+    pl.sk_tiles = 0;
+    pl.sk_pieces = 1;
+    pl.sk_kb = (int)(K / 128);
+  } else {
+    plan_persistent(pl, M, N, K, ecus, workspace ? workspace_bytes : 0);
+  }
   dg::GemmParams p{};
   p.A = A;
   p.sfa = reinterpret_cast<const float*>(sfa);  // packed UE8M0 words, read as such by the kernel
@@ -454,10 +474,12 @@ int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
   p.sk_pieces = pl.sk_pieces;
   p.sk_kb = pl.sk_kb;
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] gemm_nt_ue8m0 M=%lld N=%lld K=%lld grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
-                 (long long)M, (long long)N, (long long)K, pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
-                 pl.sk_pieces, pl.sk_kb);
-  const hipError_t e = dg::launch_gemm_persistent(dg::kDenseUe8m0, pl.grid, p, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr,
+                 "[dg] gemm_nt_ue8m0 M=%lld N=%lld K=%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                 (long long)M, (long long)N, (long long)K, wide ? "wide" : "persistent", pl.grid, pl.m_tiles * pl.n_tiles,
+                 pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, pl.sk_kb);
+  const hipError_t e = wide ? dg::launch_gemm_wide(dg::kDenseUe8m0, pl.grid, p, static_cast<hipStream_t>(stream))
+                            : dg::launch_gemm_persistent(dg::kDenseUe8m0, pl.grid, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -770,6 +792,7 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   }
   (void)hipGetLastError();
   if (cus <= 0) cus = 256;
+  if (op == DG_OP_GEMM_NT_UE8M0 && wide_fill(rows, N, effective_cus(cus))) return 0;  // 256 x 256 tiles, no split
   if (op == DG_OP_BF16_GEMM_NT || op == DG_OP_GEMM_NT_UE8M0) {
     const int64_t kb = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;  // bytes per operand row
     if (!fits_persistent(1, rows, N, kb)) return 0;
@@ -790,7 +813,8 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   (void)G;
   thread_local std::string text;
   text.clear();
-  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS) || rows <= 0 || N <= 0 || K <= 0 || K % 128 || N % 16)
+  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0) || rows <= 0 || N <= 0 || K <= 0 ||
+      K % 128 || N % 16)
     return text.c_str();
   int cus = 0;
   int dev = -1;
@@ -805,6 +829,23 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
     const ContigPlan cp = plan_contiguous(rows, N, K, G < 1 ? 1 : G, effective_cus(cus));
     std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx256 grid=%d", cp.wide ? "wide" : (cp.persist ? "persistent" : "grid"),
                   cp.wide ? 256 : 128, cp.grid);
+    text = buf;
+    return text.c_str();
+  }
+  if (op == DG_OP_GEMM_NT_UE8M0) {
+    const int ecus = effective_cus(cus);
+    if (wide_fill(rows, N, ecus)) {
+      const int64_t tw = ceil_div(rows, 256) * ceil_div(N, 256);
+      std::snprintf(buf, sizeof(buf), "kernel=wide tile=256x256 grid=%d tiles=%d whole=%d tail=0x1",
+                    (int)(tw < ecus ? tw : ecus), (int)tw, (int)tw);
+    } else if (fits_persistent(1, rows, N, K)) {
+      DensePlan pb;
+      plan_persistent(pb, rows, N, K, ecus, (size_t)-1);
+      std::snprintf(buf, sizeof(buf), "kernel=persistent tile=256x128 grid=%d tiles=%d whole=%d tail=%dx%d", pb.grid,
+                    pb.m_tiles * pb.n_tiles, pb.dp_tiles, pb.sk_tiles, pb.sk_pieces);
+    } else {
+      buf[0] = 0;
+    }
     text = buf;
     return text.c_str();
   }

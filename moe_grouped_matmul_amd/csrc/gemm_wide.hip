@@ -25,6 +25,12 @@
 // contiguous, m-grouped range of tiles.  No K split: used where the tiles
 // fill the CUs in whole or nearly whole rounds.
 //
+// UE8M0 scales (dense): alpha and beta are powers of two given by their
+// exponent bytes, four K blocks per 32-bit word (as in gemm_persist.hip).
+// The matrix cores apply them (v_mfma_scale_f32_16x16x128_f8f6f4: beta's byte
+// for the B operand, each row's alpha byte for the A operand), which is exact,
+// and the promotion is one fp32 add of the scaled block product.
+//
 // M-grouped contiguous form (Lesson 13, Fig. 13-3, contiguous layout): only
 // aligned 128-row blocks are guaranteed to hold one expert, so a 256-row tile
 // may straddle two.  Every workgroup reads m_indices of its own tiles at
@@ -54,7 +60,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint3
 template <int MODE>
 __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0, "modes of the wide kernel");
   constexpr bool CONTIG = MODE == kContiguous;
+  constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
   constexpr int MAXT = kWideMaxContigTiles;  // tiles per workgroup the contiguous pass table holds
   constexpr int WGN = 2;
   constexpr int TM = 4;
@@ -91,6 +99,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const int K = p.K;
   const int N = p.N;
   const int KB = K >> 7;
+  const int KW = (KB + 3) >> 2;  // UE8M0: packed words (four K blocks) per scale row
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;
   const int T = p.m_tiles * p.n_tiles;
@@ -175,7 +184,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 
   const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
   const uint32_t b_bytes = (uint32_t)(CONTIG ? p.G : 1) * (uint32_t)N * (uint32_t)K;
-  const uint32_t s_bytes = (uint32_t)rows * (uint32_t)KB * 4u;
+  const uint32_t s_bytes = (uint32_t)rows * (uint32_t)(UE ? KW : KB) * 4u;
   const __amdgpu_buffer_rsrc_t rd = wide_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
 
   // DMA lanes (as gemm_persist.hip): instruction i of this wave fills LDS rows
@@ -246,7 +255,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
           is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0);                   \
     else                                                                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(WD_SS(st_) + wave * 64), 4, is_soff,    \
-                                               is_kb * rows * 4, 0, 0);                                    \
+                                               (UE ? (is_kb >> 2) : is_kb) * rows * 4, 0, 0);              \
   } while (0)
 #define WD_ISSUE_END()                                                                                     \
   do {                                                                                                     \
@@ -266,7 +275,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     cp_act = !CONTIG || ((cp_hm >> (wm >> 1)) & 1);
     int nblk = (cp_nt * BN + wn * 128) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
-    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_e * NB + nblk) * KB);
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_e * NB + nblk) * (UE ? KW : KB));
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
@@ -323,7 +332,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #define WD_STEP(st_, jj_)                                                                                  \
   do {                                                                                                     \
     const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = live_ ? sfb_w[cp_kb] : 0.f;                                                        \
+    const float beta_ = UE ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                           \
+    /* UE8M0: the iteration's codes sit in byte cp_kb % 4 of their packed words */                        \
+    const int ash_ = 8 * (cp_kb & 3);                                                                      \
+    const int bcode_ = UE && live_ ? __builtin_bit_cast(int, sfb_w[cp_kb >> 2]) >> ash_ : 0;              \
+    (void)ash_;                                                                                            \
+    (void)bcode_;                                                                                          \
     wait_vmcnt<0>();                                                                                       \
     wait_lgkmcnt0();                                                                                       \
     __builtin_amdgcn_s_barrier();                                                                          \
@@ -340,10 +354,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
       WD_ISSUE_END();                                                                                      \
     } else {                                                                                               \
       i32x8 af_[TM], bf_[2];                                                                               \
-      float sc_[TM];                                                                                       \
+      float sc_[TM];  /* alpha * beta of the row tile's rows */                                            \
+      int acode_[TM]; /* UE8M0: the rows' alpha codes in byte 0 */                                         \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         WD_FRAG(af_[i_], sl_ + a_row0, i_ * 2048);                                                         \
-        sc_[i_] = WD_SS(st_)[wm * 64 + i_ * 16 + q16] * beta_;                                             \
+        const float al_ = WD_SS(st_)[wm * 64 + i_ * 16 + q16];                                             \
+        if constexpr (UE) acode_[i_] = __builtin_bit_cast(int, al_) >> ash_;                               \
+        else sc_[i_] = al_ * beta_;                                                                        \
       }                                                                                                    \
       WD_FRAG(bf_[0], sl_ + b_row0, 0);                                                                    \
       WD_ISSUE_BEGIN();                                                                                    \
@@ -352,15 +369,24 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
         if (k_ < TM * TN) {                                                                                \
           const int j_ = k_ / TM;                                                                          \
           if (k_ % TM == 0 && j_ + 1 < TN) WD_FRAG(bf_[(j_ + 1) & 1], sl_ + b_row0, (j_ + 1) * 2048);      \
-          t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],          \
-                                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
+          if constexpr (UE) /* alpha and beta applied by the matrix cores (exact powers of two) */          \
+            t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],        \
+                                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, \
+                                                                         bcode_, 0, acode_[k_ % TM]);      \
+          else                                                                                             \
+            t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],        \
+                                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
           if (k_ < L_BLOCK) WD_ISSUE_LOAD((st_) ^ 1, k_);                                                  \
         }                                                                                                  \
         if (k_ >= 3) {                                                                                     \
           const int kk_ = k_ - 3;                                                                          \
           f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
-          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
-            uk_[v_] = __builtin_fmaf(t_[kk_ & 3][v_], sc_[kk_ % TM], uk_[v_]);                             \
+          if constexpr (UE) {                                                                              \
+            uk_ += t_[kk_ & 3]; /* the promotion: one fp32 add of the scaled block product */             \
+          } else {                                                                                         \
+            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
+              uk_[v_] = __builtin_fmaf(t_[kk_ & 3][v_], sc_[kk_ % TM], uk_[v_]);                           \
+          }                                                                                                \
           asm volatile("" : "+v"(uk_));                                                                    \
         }                                                                                                  \
         __builtin_amdgcn_sched_barrier(0);                                                                 \
@@ -414,6 +440,8 @@ hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t
   if (grid <= 0) return hipSuccess;
   if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kDenseUe8m0)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseUe8m0>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();

@@ -173,6 +173,11 @@ def test_dense_planner_choice(lib):
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)      # 448 tiles: 0.875
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 4096, 7168)       # 256 tiles: 1.0
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)  # 144 tiles: 0.56
+        # UE8M0 scales: the same 256 x 256 rule (no workspace needed there), else 256 x 128 tiles
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 4096, 7168, 16384)
+        assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 7168, 16384) == 0
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 4096, 2112, 7168)
+        assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 2112, 7168) > 0
         assert "kernel=skinny" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 2048)
         # 64 < M <= 128: a 128 x 128 tile when it still fills the CUs through a K split
         assert "tile=128x128 tiles=56 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 16384)

@@ -2,8 +2,9 @@
 (oracle/ue8m0.py): both quantisers bit-exact (bytes and packed code words,
 ragged N, K blocks not a multiple of four, several groups, zero groups,
 amax exactly at and just past the power-of-two boundaries, tiny values), the
-GEMM within the bf16 tolerance over small, ragged and split shapes, bit
-identity with the fp32-scale kernel fed the same powers of two, and the
+GEMM within the bf16 tolerance over small, ragged and split shapes and on
+256 x 256 tiles, bit identity with the fp32-scale kernel fed the same powers
+of two, and the
 4096x7168x16384 shape at full size on sampled rows and column blocks."""
 
 import numpy as np
@@ -107,6 +108,31 @@ def test_gemm_ue8m0_many_tiles_per_workgroup(cus):
         dg.dg_set_num_cus(0)
     assert_close(D.view(torch.int16).cpu().numpy().view(np.uint16), oracle.gemm_nt_ue8m0(qa, pa, qb, pb),
                  f"ue8m0 on {cus} CUs")
+
+
+# (cus, M, N, K): 256 x 256 tiles (the wide kernel) once they fill whole rounds
+# of the (capped) CUs, ragged M and N included, several tiles per workgroup
+WIDE = [(1, 256, 256, 128), (4, 512, 512, 640), (4, 500, 496, 384), (3, 300, 608, 1024), (2, 1024, 272, 256)]
+
+
+@pytest.mark.parametrize("cus,M,N,K", WIDE)
+def test_gemm_ue8m0_wide_tiles(cus, M, N, K):
+    dg.dg_set_num_cus(cus)
+    try:
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
+        qa, pa, qb, pb = _case(M, N, K, seed=cus + M + N)
+        D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        dg.dg_fp8_gemm_nt_ue8m0(_t(qa), _t(pa), _t(qb), _t(pb), D, _ws(M, N, K))
+        # the fp32-scale kernel on the same plan, fed the same powers of two: bit for bit
+        kb = K // 128
+        D2 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        dg.dg_fp8_gemm_nt(_t(qa), _t(ue8m0_value(unpack_k(pa.T, kb).T)), _t(qb), _t(ue8m0_value(unpack_k(pb, kb))), D2)
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_num_cus(0)
+    assert torch.equal(D.view(torch.int16), D2.view(torch.int16))
+    assert_close(D.view(torch.int16).cpu().numpy().view(np.uint16), oracle.gemm_nt_ue8m0(qa, pa, qb, pb),
+                 f"ue8m0 wide {M}x{N}x{K} on {cus} CUs")
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 400, 640), (2048, 1024, 2048)])
