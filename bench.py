@@ -453,14 +453,16 @@ def run_bf16(args, torch, dg, workloads):
     nbytes = 2.0 * (M * K + N * K + M * N)
     us = ms_per_step * 1e3
     achieved = flops / us / 1e6
+    plan = dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, M, N, K, 1)
+    kname = "fp8_gemm_wide_kernel<bf16>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<bf16>"
     roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None, kernel="fp8_gemm_persistent_kernel<bf16>",
+                frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None, kernel=kname,
                 launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
                 algorithmic_flops_per_launch=round(flops))
     per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1),
                       gbs=round(nbytes / us / 1e3, 1), bound="mfma",
                       roof_frac=round(max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6 / us, 4),
-                      kernel="fp8_gemm_persistent_kernel<bf16>")]
+                      kernel=kname)]
     config = dict(workload="dense_bf16_nt_4096x7168x16384", shapes=[f"{M}x{N}x{K}"], out="bf16",
                   step="dg_bf16_gemm_nt", cold_hbm=True)
     return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],

@@ -241,8 +241,8 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
 /* Text description of the launch plan the library would use for `op` at this
  * shape on the current device with a full workspace, e.g. "kernel=wide
  * tile=256x256 grid=256 tiles=448 whole=448 tail=0x1" (DG_OP_GEMM_NT,
- * DG_OP_GEMM_NT_UE8M0 and DG_OP_CONTIGUOUS, rows = M_total and G the expert
- * count there; "" for other ops or invalid shapes).  The pointer stays valid until the next call on the
+ * DG_OP_GEMM_NT_UE8M0, DG_OP_BF16_GEMM_NT and DG_OP_CONTIGUOUS, rows = M_total
+ * and G the expert count there; "" for other ops or invalid shapes).  The pointer stays valid until the next call on the
  * same thread. */
 const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
 

@@ -555,10 +555,24 @@ int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M
   int rc = 0;
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  // the persistent kernel's schedule over K blocks of 128 bytes (64 bf16)
+  // the persistent kernels' schedule over K blocks of 128 bytes (64 bf16)
   if (!fits_persistent(1, M, N, 2 * K)) return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
   DensePlan pl;
-  plan_persistent(pl, M, N, 2 * K, effective_cus(cus), workspace ? workspace_bytes : 0);
+  const int ecus = effective_cus(cus);
+  const bool wide = wide_fill(M, N, ecus);
+  if (wide) {
+    pl.m_tiles = (int)ceil_div(M, 256);
+    pl.n_tiles = (int)ceil_div(N, 256);
+    const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
+    pl.grid = (int)(tw < ecus ? tw : ecus);
+    pl.kb_per_split = (int)(2 * K / 128);
+    pl.dp_tiles = (int)tw;
+    pl.sk_tiles = 0;
+    pl.sk_pieces = 1;
+    pl.sk_kb = pl.kb_per_split;
+  } else {
+    plan_persistent(pl, M, N, 2 * K, ecus, workspace ? workspace_bytes : 0);
+  }
   dg::GemmParams p{};
   p.A = reinterpret_cast<const uint8_t*>(A);
   p.B = reinterpret_cast<const uint8_t*>(B);
@@ -577,10 +591,12 @@ int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M
   p.sk_pieces = pl.sk_pieces;
   p.sk_kb = pl.sk_kb;
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] bf16_gemm_nt M=%lld N=%lld K=%lld grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
-                 (long long)M, (long long)N, (long long)K, pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
-                 pl.sk_pieces, pl.sk_kb);
-  const hipError_t e = dg::launch_gemm_persistent(dg::kDenseBf16, pl.grid, p, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr,
+                 "[dg] bf16_gemm_nt M=%lld N=%lld K=%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                 (long long)M, (long long)N, (long long)K, wide ? "wide" : "persistent", pl.grid, pl.m_tiles * pl.n_tiles,
+                 pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, pl.sk_kb);
+  const hipError_t e = wide ? dg::launch_gemm_wide(dg::kDenseBf16, pl.grid, p, static_cast<hipStream_t>(stream))
+                            : dg::launch_gemm_persistent(dg::kDenseBf16, pl.grid, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -792,7 +808,8 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   }
   (void)hipGetLastError();
   if (cus <= 0) cus = 256;
-  if (op == DG_OP_GEMM_NT_UE8M0 && wide_fill(rows, N, effective_cus(cus))) return 0;  // 256 x 256 tiles, no split
+  if ((op == DG_OP_GEMM_NT_UE8M0 || op == DG_OP_BF16_GEMM_NT) && wide_fill(rows, N, effective_cus(cus)))
+    return 0;  // 256 x 256 tiles, no split
   if (op == DG_OP_BF16_GEMM_NT || op == DG_OP_GEMM_NT_UE8M0) {
     const int64_t kb = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;  // bytes per operand row
     if (!fits_persistent(1, rows, N, kb)) return 0;
@@ -813,8 +830,8 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   (void)G;
   thread_local std::string text;
   text.clear();
-  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0) || rows <= 0 || N <= 0 || K <= 0 ||
-      K % 128 || N % 16)
+  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0 && op != DG_OP_BF16_GEMM_NT) ||
+      rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128) || N % 16)
     return text.c_str();
   int cus = 0;
   int dev = -1;
@@ -832,15 +849,16 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
     text = buf;
     return text.c_str();
   }
-  if (op == DG_OP_GEMM_NT_UE8M0) {
+  if (op == DG_OP_GEMM_NT_UE8M0 || op == DG_OP_BF16_GEMM_NT) {
     const int ecus = effective_cus(cus);
+    const int64_t kbytes = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;  // bytes per operand row
     if (wide_fill(rows, N, ecus)) {
       const int64_t tw = ceil_div(rows, 256) * ceil_div(N, 256);
       std::snprintf(buf, sizeof(buf), "kernel=wide tile=256x256 grid=%d tiles=%d whole=%d tail=0x1",
                     (int)(tw < ecus ? tw : ecus), (int)tw, (int)tw);
-    } else if (fits_persistent(1, rows, N, K)) {
+    } else if (fits_persistent(1, rows, N, kbytes)) {
       DensePlan pb;
-      plan_persistent(pb, rows, N, K, ecus, (size_t)-1);
+      plan_persistent(pb, rows, N, kbytes, ecus, (size_t)-1);
       std::snprintf(buf, sizeof(buf), "kernel=persistent tile=256x128 grid=%d tiles=%d whole=%d tail=%dx%d", pb.grid,
                     pb.m_tiles * pb.n_tiles, pb.dp_tiles, pb.sk_tiles, pb.sk_pieces);
     } else {

@@ -31,6 +31,14 @@
 // for the B operand, each row's alpha byte for the A operand), which is exact,
 // and the promotion is one fp32 add of the scaled block product.
 //
+// BF16 operands (plain GEMM, no scales): a K block is 64 bf16 = 128 bytes
+// per row, so LDS rows, swizzle, DMA and fragment reads are those of the fp8
+// path.  A fragment's chunk q holds K elements 8 q .. 8 q + 7 of the block's
+// first 32, chunk q + 4 the same of its second 32 (both operands map them
+// alike), so each 16 x 16 tile takes two v_mfma_f32_16x16x32_bf16 straight
+// into the accumulator: the 32 first halves (B half fragments streamed one
+// ahead), then the 32 second halves, each 32 MFMAs after its first half.
+//
 // M-grouped contiguous form (Lesson 13, Fig. 13-3, contiguous layout): only
 // aligned 128-row blocks are guaranteed to hold one expert, so a 256-row tile
 // may straddle two.  Every workgroup reads m_indices of its own tiles at
@@ -52,6 +60,8 @@ constexpr int kWideRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
 constexpr uint32_t kWideOOB = 0xFFFFFF00u;  // an offset past every buffer range used here
 
 typedef unsigned int wu32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 wbf16x8 __attribute__((ext_vector_type(8)));
+typedef int wi32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kWideRsrcWord3);
@@ -60,9 +70,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint3
 template <int MODE>
 __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0, "modes of the wide kernel");
+  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0 || MODE == kDenseBf16,
+                "modes of the wide kernel");
   constexpr bool CONTIG = MODE == kContiguous;
   constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
+  constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
   constexpr int MAXT = kWideMaxContigTiles;  // tiles per workgroup the contiguous pass table holds
   constexpr int WGN = 2;
   constexpr int TM = 4;
@@ -72,7 +84,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   constexpr int NWAVES = 8;
   constexpr int A_INS = BM / 8 / NWAVES;      // 1 KB (8-row) loads per wave per K block
   constexpr int B_INS = BN / 8 / NWAVES;
-  constexpr int L_BLOCK = A_INS + B_INS + 1;  // + one alpha load per wave
+  constexpr int L_BLOCK = A_INS + B_INS + (BF16 ? 0 : 1);  // + one alpha load per wave
   constexpr int GM = 4;                       // m-tiles per tile group of the walk
   constexpr int SLOT_S = (BM + BN) * 128;
   constexpr int SLOT_BYTES = SLOT_S + NWAVES * 64 * 4;
@@ -96,7 +108,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const int b = (int)blockIdx.x;
   const int G = (int)gridDim.x;
 
-  const int K = p.K;
+  const int K = BF16 ? 2 * p.K : p.K;  // bytes per operand row
   const int N = p.N;
   const int KB = K >> 7;
   const int KW = (KB + 3) >> 2;  // UE8M0: packed words (four K blocks) per scale row
@@ -332,10 +344,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #define WD_STEP(st_, jj_)                                                                                  \
   do {                                                                                                     \
     const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = UE ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                           \
+    const float beta_ = UE || BF16 ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                   \
     /* UE8M0: the iteration's codes sit in byte cp_kb % 4 of their packed words */                        \
     const int ash_ = 8 * (cp_kb & 3);                                                                      \
     const int bcode_ = UE && live_ ? __builtin_bit_cast(int, sfb_w[cp_kb >> 2]) >> ash_ : 0;              \
+    (void)beta_;                                                                                           \
     (void)ash_;                                                                                            \
     (void)bcode_;                                                                                          \
     wait_vmcnt<0>();                                                                                       \
@@ -351,6 +364,30 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     if (!cp_act) { /* no rows of this wave in the pass: only this wave's share of the loads */             \
       WD_ISSUE_BEGIN();                                                                                    \
       _Pragma("unroll") for (int n_ = 0; n_ < L_BLOCK; ++n_) WD_ISSUE_LOAD((st_) ^ 1, n_);                \
+      WD_ISSUE_END();                                                                                      \
+    } else if constexpr (BF16) {                                                                           \
+      i32x8 af_[TM];                                                                                       \
+      uint4 bh_[2]; /* B half fragments, streamed one ahead */                                             \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) WD_FRAG(af_[i_], sl_ + a_row0, i_ * 2048);         \
+      bh_[0] = *reinterpret_cast<const uint4*>(sl_ + b_row0 + fr_lo);                                      \
+      WD_ISSUE_BEGIN();                                                                                    \
+      _Pragma("unroll") for (int k_ = 0; k_ < 2 * TM * TN; ++k_) {                                         \
+        const int h_ = k_ / (TM * TN);    /* 0: first 32 K elements, 1: second */                          \
+        const int f_ = k_ % (TM * TN);                                                                     \
+        const int j_ = f_ / TM;                                                                            \
+        const int i_ = f_ % TM;                                                                            \
+        const int sq_ = h_ * TN + j_;     /* position in the half-fragment stream */                       \
+        if (i_ == 0 && sq_ + 1 < 2 * TN) {                                                                 \
+          const int hn_ = (sq_ + 1) / TN, jn_ = (sq_ + 1) % TN;                                            \
+          bh_[(sq_ + 1) & 1] = *reinterpret_cast<const uint4*>(sl_ + b_row0 + jn_ * 2048 + (hn_ ? fr_hi : fr_lo)); \
+        }                                                                                                  \
+        const wi32x4 av_ = h_ == 0 ? wi32x4{af_[i_][0], af_[i_][1], af_[i_][2], af_[i_][3]}                \
+                                   : wi32x4{af_[i_][4], af_[i_][5], af_[i_][6], af_[i_][7]};               \
+        u[i_][j_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(wbf16x8, bh_[sq_ & 1]),     \
+                                                           __builtin_bit_cast(wbf16x8, av_), u[i_][j_], 0, 0, 0); \
+        if (k_ < L_BLOCK) WD_ISSUE_LOAD((st_) ^ 1, k_);                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                                 \
+      }                                                                                                    \
       WD_ISSUE_END();                                                                                      \
     } else {                                                                                               \
       i32x8 af_[TM], bf_[2];                                                                               \
@@ -442,6 +479,8 @@ hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseUe8m0)
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseUe8m0>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kDenseBf16)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseBf16>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();

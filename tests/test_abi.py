@@ -178,6 +178,11 @@ def test_dense_planner_choice(lib):
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 7168, 16384) == 0
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 4096, 2112, 7168)
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 2112, 7168) > 0
+        # BF16: the same rule (K counted in bf16 elements, a multiple of 64)
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 4096, 7168, 16384)
+        assert dg.dg_get_workspace_size(dg.DG_OP_BF16_GEMM_NT, 4096, 7168, 16384) == 0
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 300, 400, 576)
+        assert dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 300, 400, 100) == ""
         assert "kernel=skinny" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 2048)
         # 64 < M <= 128: a 128 x 128 tile when it still fills the CUs through a K split
         assert "tile=128x128 tiles=56 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 16384)

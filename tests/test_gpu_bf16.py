@@ -1,7 +1,7 @@
 """BF16 dense GEMM (dg_bf16_gemm_nt) against the oracle (oracle/gemm_bf16.py):
 small and ragged shapes on one or many tiles per workgroup, with and without
-a K-split tail, integer inputs bit-exact, and the full 4096 x 7168 x 16384
-shape on sampled rows."""
+a K-split tail and on 256 x 256 tiles, integer inputs bit-exact, and the full
+4096 x 7168 x 16384 shape on sampled rows."""
 
 import numpy as np
 import pytest
@@ -69,6 +69,29 @@ def test_bf16_many_tiles_per_workgroup_reused_workspace(cus, M, N, K):
     for o in outs[1:]:
         assert np.array_equal(o, outs[0]), "results differ between calls on one workspace"
     assert_close(outs[0], oracle.gemm_bf16_nt(a, b), f"bf16 {M}x{N}x{K} on {cus} CUs")
+
+
+# (cus, M, N, K): 256 x 256 tiles (the wide kernel) once they fill whole rounds
+# of the (capped) CUs: ragged M and N, several tiles per workgroup, one K block
+WIDE = [(1, 256, 256, 64), (4, 512, 512, 640), (4, 500, 496, 384), (3, 300, 608, 1024), (2, 1024, 272, 256),
+        (7, 1000, 1792, 512)]
+
+
+@pytest.mark.parametrize("cus,M,N,K", WIDE)
+def test_bf16_wide_tiles(cus, M, N, K):
+    dg.dg_set_num_cus(cus)
+    try:
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, M, N, K, 1)
+        a, b = workloads.dense_bf16(M, N, K, seed=cus + M + N)
+        got = _run(a, b)
+        rng = np.random.default_rng(M + N)  # integers in [-3, 3]: exact products and sums
+        ai = oracle.bf16_rne_bits(rng.integers(-3, 4, (M, K)).astype(np.float64))
+        bi = oracle.bf16_rne_bits(rng.integers(-3, 4, (N, K)).astype(np.float64))
+        got_i = _run(ai, bi)
+    finally:
+        dg.dg_set_num_cus(0)
+    assert_close(got, oracle.gemm_bf16_nt(a, b), f"bf16 wide {M}x{N}x{K} on {cus} CUs")
+    assert np.array_equal(got_i, oracle.gemm_bf16_nt(ai, bi))
 
 
 def test_bf16_full_size_sampled_rows():
