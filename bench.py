@@ -505,13 +505,16 @@ def run_acc(args, torch, dg, workloads):
     nbytes += 6.0 * M * N  # fp32 C read and fp32 D written instead of bf16 D
     us = ms_per_step * 1e3
     achieved = flops / us / 1e6
+    # the accumulating form takes 256 x 256 tiles by the dense rule
+    plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT, M, N, K, 1)
+    kname = "fp8_gemm_wide_kernel<acc>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<acc>"
     roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
-                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel="fp8_gemm_persistent_kernel<acc>",
+                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel=kname,
                 launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
                 algorithmic_flops_per_launch=round(flops))
     per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1), gbs=round(nbytes / us / 1e3, 1),
                       bound="mfma", roof_frac=round(roof_time_us(flops, nbytes) / us, 4),
-                      kernel="fp8_gemm_persistent_kernel<acc>")]
+                      kernel=kname)]
     config = dict(workload="dense_fp8_nt_acc_4096x7168x16384", shapes=[f"{M}x{N}x{K}"], out="fp32 D = C + A.B^T",
                   step="dg_fp8_gemm_nt_acc (C = D, in place)", cold_hbm=True)
     return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],

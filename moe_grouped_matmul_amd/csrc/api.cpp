@@ -394,10 +394,22 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
     return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0, false);
+  const int ecus = effective_cus(cus);
+  DensePlan pl = plan_dense(M, N, K, ecus, workspace ? workspace_bytes : 0, false);
   if (!pl.persist && !pl.skinny) return fail(DG_ERR_SHAPE, "problem too large for the accumulating form");
   if (pl.persist && M * N * 4 >= (int64_t)0xFFFFFF00 - 4096)
     return fail(DG_ERR_SHAPE, "fp32 output too large for 32-bit buffer offsets");
+  const bool wide = pl.persist && wide_fill(M, N, ecus);  // 256 x 256 tiles, no K split
+  if (wide) {
+    pl.m_tiles = (int)ceil_div(M, 256);
+    pl.n_tiles = (int)ceil_div(N, 256);
+    const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
+    pl.grid = (int)(tw < ecus ? tw : ecus);
+    pl.dp_tiles = (int)tw;
+    pl.sk_tiles = 0;
+    pl.sk_pieces = 1;
+    pl.sk_kb = (int)(K / 128);
+  }
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
@@ -418,8 +430,13 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
   p.sk_tiles = pl.sk_tiles;
   p.sk_pieces = pl.sk_pieces;
   p.sk_kb = pl.sk_kb;
-  const hipError_t e = pl.persist ? dg::launch_gemm_persistent(dg::kDenseAcc, pl.grid, p, static_cast<hipStream_t>(stream))
-                                  : dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream));
+  if (std::getenv("DG_PRINT_CONFIGS"))
+    std::fprintf(stderr, "[dg] gemm_nt_acc M=%lld N=%lld K=%lld kernel=%s\n", (long long)M, (long long)N, (long long)K,
+                 wide ? "wide" : (pl.persist ? "persistent" : "skinny"));
+  const hipError_t e =
+      wide ? dg::launch_gemm_wide(dg::kDenseAcc, pl.grid, p, static_cast<hipStream_t>(stream))
+           : (pl.persist ? dg::launch_gemm_persistent(dg::kDenseAcc, pl.grid, p, static_cast<hipStream_t>(stream))
+                         : dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream)));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -39,6 +39,11 @@
 // into the accumulator: the 32 first halves (B half fragments streamed one
 // ahead), then the 32 second halves, each 32 MFMAs after its first half.
 //
+// Accumulating form (fp32 D = C + A . B^T, C optional and possibly D itself):
+// a finished tile is written row tile by row tile, the C fragments of the
+// next row tile loaded before the current one is stored (two in flight;
+// distinct rows, so C = D in place stays correct).
+//
 // M-grouped contiguous form (Lesson 13, Fig. 13-3, contiguous layout): only
 // aligned 128-row blocks are guaranteed to hold one expert, so a 256-row tile
 // may straddle two.  Every workgroup reads m_indices of its own tiles at
@@ -67,11 +72,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kWideRsrcWord3);
 }
 
-template <int MODE>
+template <int MODE, bool HASC>
 __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0 || MODE == kDenseBf16,
+  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0 || MODE == kDenseBf16 ||
+                    MODE == kDenseAcc,
                 "modes of the wide kernel");
+  constexpr bool ACC = MODE == kDenseAcc;    // fp32 output D = C + A . B^T
   constexpr bool CONTIG = MODE == kContiguous;
   constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
@@ -197,7 +204,9 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
   const uint32_t b_bytes = (uint32_t)(CONTIG ? p.G : 1) * (uint32_t)N * (uint32_t)K;
   const uint32_t s_bytes = (uint32_t)rows * (uint32_t)(UE ? KW : KB) * 4u;
-  const __amdgpu_buffer_rsrc_t rd = wide_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
+  const __amdgpu_buffer_rsrc_t rd = ACC ? wide_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
+                                        : wide_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
+  const __amdgpu_buffer_rsrc_t rc = wide_rsrc(p.Cacc, HASC ? (uint32_t)rows * (uint32_t)N * 4u : 0u);
 
   // DMA lanes (as gemm_persist.hip): instruction i of this wave fills LDS rows
   // 64 i + 8 wave + lane / 8, lane chunk (lane % 8) of row r holding K chunk
@@ -306,8 +315,36 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   bool pend = false;
   int st_row0 = 0, st_col0 = 0;
   uint32_t st_m[8] = {~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u};  // contiguous: rows tagged with the pass's expert
+#define WD_OUT_OFF(i_, h_) /* fp32 byte offset of the lane's run (row tile i_, column half h_), or OOB */ \
+  ((st_row0 + wm * 64 + (i_) * 16 + q16 < rows && st_col0 + wn * 128 + (h_) * 64 + q * 16 < N)             \
+       ? ((uint32_t)(st_row0 + wm * 64 + (i_) * 16 + q16) * (uint32_t)N +                                   \
+          (uint32_t)(st_col0 + wn * 128 + (h_) * 64 + q * 16)) * 4u                                        \
+       : kWideOOB)
+#define WD_LOAD_C(cv_, i_)                                                                                 \
+  _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                                       \
+    const uint32_t o_ = WD_OUT_OFF(i_, h_);                                                                \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                                       \
+      cv_[4 * h_ + j_] = HASC ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(           \
+                                    rc, o_ == kWideOOB ? kWideOOB : o_ + 16u * j_, 0, 0))                  \
+                              : f32x4{0.f, 0.f, 0.f, 0.f};                                                 \
+  }
 #define WD_STORE_U()                                                                                       \
   do {                                                                                                     \
+    if constexpr (ACC) {                                                                                   \
+      f32x4 ca_[TN], cb_[TN];                                                                              \
+      WD_LOAD_C(ca_, 0);                                                                                   \
+      _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
+        f32x4* cur_ = (i_ & 1) ? cb_ : ca_;                                                                \
+        f32x4* nxt_ = (i_ & 1) ? ca_ : cb_;                                                                \
+        if (i_ + 1 < TM) { WD_LOAD_C(nxt_, i_ + 1); }                                                      \
+        _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                                 \
+          const uint32_t o_ = WD_OUT_OFF(i_, h_);                                                          \
+          _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                                 \
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(wu32x4, u[i_][4 * h_ + j_] + cur_[4 * h_ + j_]), \
+                                                   rd, o_ == kWideOOB ? kWideOOB : o_ + 16u * j_, 0, 0);   \
+        }                                                                                                  \
+      }                                                                                                    \
+    } else                                                                                                 \
     _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                    \
       const int rr_ = wm * 64 + i_ * 16 + q16;                                                             \
       const int r_ = st_row0 + rr_;                                                                        \
@@ -463,6 +500,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #undef WD_STEP
 #undef WD_FRAG
 #undef WD_STORE_U
+#undef WD_LOAD_C
+#undef WD_OUT_OFF
 #undef WD_ISSUE_BEGIN
 #undef WD_ISSUE_LOAD
 #undef WD_ISSUE_END
@@ -476,13 +515,17 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (mode == kContiguous)
-    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguous>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguous, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseUe8m0)
-    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseUe8m0>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseUe8m0, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseBf16)
-    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseBf16>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseBf16, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kDenseAcc && p.Cacc)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseAcc, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kDenseAcc)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseAcc, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDense>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDense, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

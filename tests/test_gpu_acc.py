@@ -1,7 +1,9 @@
 """Accumulating FP8 GEMM (dg_fp8_gemm_nt_acc, D = C + A.B^T in fp32) against
-the oracle (oracle.gemm_nt_c): skinny (M <= 128) and persistent (M > 128)
-kernels, with C given, absent and aliased to D, with and without K splits,
-many tiles per workgroup; integer inputs bit-exact."""
+the oracle (oracle.gemm_nt_c): skinny (M <= 128), persistent (M > 128) and
+wide (256 x 256 tiles) kernels, with C given, absent and aliased to D, with
+and without K splits, many tiles per workgroup; integer inputs bit-exact."""
+
+import os
 
 import numpy as np
 import pytest
@@ -70,6 +72,48 @@ def test_acc_many_tiles_per_workgroup(cus, M, N, K):
     finally:
         dg.dg_set_num_cus(0)
     _check(D.cpu().numpy(), qa, sa, qb, sb, c, f"acc {M}x{N}x{K} on {cus} CUs")
+
+
+# (cus, M, N, K): 256 x 256 tiles (the wide kernel, C loaded and D stored
+# row tile by row tile) once they fill whole rounds of the capped CUs
+WIDE = [(1, 256, 256, 128), (4, 512, 512, 640), (4, 500, 496, 384), (3, 300, 608, 1024), (7, 1000, 1792, 512)]
+
+
+@pytest.mark.parametrize("cus,M,N,K", WIDE)
+@pytest.mark.parametrize("mode", ["c", "none", "inplace"])
+def test_acc_wide_tiles(capfd, cus, M, N, K, mode):
+    dg.dg_set_num_cus(cus)
+    os.environ["DG_PRINT_CONFIGS"] = "1"
+    try:
+        qa, sa, qb, sb, c = _case(M, N, K, seed=cus + M + N)
+        C = None if mode == "none" else _t(c)
+        D = C if mode == "inplace" else torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        capfd.readouterr()
+        dg.dg_fp8_gemm_nt_acc(_t(qa), _t(sa), _t(qb), _t(sb), C, D, _ws(M, N, K))
+        torch.cuda.synchronize()
+        assert "kernel=wide" in capfd.readouterr().err
+    finally:
+        del os.environ["DG_PRINT_CONFIGS"]
+        dg.dg_set_num_cus(0)
+    _check(D.cpu().numpy(), qa, sa, qb, sb, None if mode == "none" else c, f"acc wide {M}x{N}x{K} {mode} on {cus} CUs")
+
+
+def test_acc_wide_integer_inputs_bit_exact():
+    M, N, K = 512, 496, 512
+    dg.dg_set_num_cus(4)
+    try:
+        rng = np.random.default_rng(9)
+        qa = oracle.encode_e4m3(rng.integers(-10, 10, (M, K)).astype(np.float32))
+        qb = oracle.encode_e4m3(rng.integers(-10, 10, (N, K)).astype(np.float32))
+        sa = np.ones((K // 128, M), np.float32)
+        sb = np.ones(((N + 127) // 128, K // 128), np.float32)
+        c = rng.integers(-5000, 5000, (M, N)).astype(np.float32)
+        D = _t(c)  # in place
+        dg.dg_fp8_gemm_nt_acc(_t(qa), _t(sa), _t(qb), _t(sb), D, D, None)
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_num_cus(0)
+    assert np.array_equal(D.cpu().numpy(), oracle.gemm_nt_c(qa, sa, qb, sb, c))
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 272, 512), (300, 144, 1024)])
