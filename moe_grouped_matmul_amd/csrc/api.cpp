@@ -834,7 +834,8 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
     plan_persistent(pb, rows, N, kb, effective_cus(cus), (size_t)-1);
     return (dg::persistent_workspace_bytes(pb.sk_tiles, pb.sk_pieces) + 15) / 16 * 16;
   }
-  // sized for the 256 x 128 plan, which the accumulating form also uses
+  // sized for the 256 x 128 plan, which the accumulating form also uses where
+  // 256 x 256 tiles do not apply (those need no workspace; a larger one is unused)
   const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, false);
   if (pl.persist) return (dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces) + 15) / 16 * 16;
   if (pl.splits <= 1) return 0;

@@ -4,8 +4,10 @@
 // forms: an aligned 128-row block of the contiguous form belongs to one
 // expert, and a masked expert's rows fill fewer padded MFMA rows) with one
 // continuous LDS ring, so the next tile's first K blocks load while the
-// current tile finishes and stores.  Used for the dense form with M > 128 and
-// for the two M-grouped forms.
+// current tile finishes and stores.  Used for the dense forms with M > 128
+// where 256 x 256 tiles (gemm_wide.hip) would leave a partial round, for the
+// masked form, for the contiguous form where the wide kernel does not take
+// it (K < 4096, or a partial round) and for the K-grouped form.
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: for every 128-wide K block the fp8 partial product of
