@@ -286,7 +286,9 @@ def test_contiguous_out_of_range_indices_untouched():
 # ---------------------------------------------------------------- masked
 
 @pytest.mark.parametrize("mm,max_m,N,K", [([64, 0, 17, 40], 64, 128, 256), ([256, 1, 129, 0, 200, 255], 256, 272, 512),
-                                          ([3, 99, -4], 8, 16, 128), ([0, 0], 128, 128, 128)])
+                                          ([3, 99, -4], 8, 16, 128), ([0, 0], 128, 128, 128),
+                                          ([200, 128, 129, 73], 200, 528, 384),   # capacity not a multiple of 128
+                                          ([300, 257, 1, 256], 300, 304, 256)])   # three 128-row tiles
 def test_masked_matches_oracle(mm, max_m, N, K):
     G = len(mm)
     w = workloads.masked(G, max_m, N, K, seed=G + max_m, masked_m=mm)
