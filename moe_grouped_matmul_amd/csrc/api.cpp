@@ -536,8 +536,14 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.N = (int)N;
   p.K = (int)K;
   p.G = (int)G;
+  const int ecus = effective_cus(cus);
+  // 256 x 256 tiles of all groups where they fill whole rounds of the CUs to
+  // >= 85% (as the dense rule), else 256 x 128 tiles
+  const int64_t tw = G * ceil_div(M, 256) * ceil_div(N, 256);
+  const bool wide = M >= 256 && N >= 256 && tw <= ((int64_t)1 << 31) - 1 &&
+                    (double)tw / (double)(ceil_div(tw, ecus) * ecus) >= 0.85;
   p.m_tiles = (int)ceil_div(M, 256);
-  p.n_tiles = (int)ceil_div(N, 128);
+  p.n_tiles = (int)ceil_div(N, wide ? 256 : 128);
   p.splits = 1;
   p.kb_per_split = (int)(K / 128);
   p.dp_tiles = 0;
@@ -546,12 +552,12 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.sk_kb = (int)(K / 128);
   const int64_t tiles = G * p.m_tiles * p.n_tiles;
   if (tiles > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "too many tiles");
-  const int ecus = effective_cus(cus);
   const int grid = (int)(tiles < ecus ? tiles : ecus);
   if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] k_grouped G=%lld M=%lld N=%lld K=%lld tiles=%lld grid=%d\n", (long long)G, (long long)M,
-                 (long long)N, (long long)K, (long long)tiles, grid);
-  const hipError_t e = dg::launch_gemm_persistent(dg::kKGrouped, grid, p, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr, "[dg] k_grouped G=%lld M=%lld N=%lld K=%lld kernel=%s tiles=%lld grid=%d\n", (long long)G,
+                 (long long)M, (long long)N, (long long)K, wide ? "wide" : "persistent", (long long)tiles, grid);
+  const hipError_t e = wide ? dg::launch_gemm_wide(dg::kKGrouped, grid, p, static_cast<hipStream_t>(stream))
+                            : dg::launch_gemm_persistent(dg::kKGrouped, grid, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

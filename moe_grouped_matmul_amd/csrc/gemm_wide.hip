@@ -46,6 +46,16 @@
 // next row tile loaded before the current one is stored (two in flight;
 // distinct rows, so C = D in place stays correct).
 //
+// K-grouped form (MoE weight gradient, fp32 D[g] = C[g] + A[:, seg g] .
+// B[:, seg g]^T): every workgroup reads the group lengths on the device and
+// builds the first K block of each group; the tiles of all groups are walked
+// in rounds of one tile per workgroup (XCD-contiguous inside a round), each
+// tile over its group's K blocks only (a group without blocks runs one
+// iteration over zeros, so its tiles still store C).  Waves 4..7 load the
+// per-column beta of the tile's 256 columns where the other forms have no
+// alpha rows, and the promotion scales each product by its columns' beta
+// before the row's alpha.
+//
 // M-grouped contiguous form (Lesson 13, Fig. 13-3, contiguous layout): only
 // aligned 128-row blocks are guaranteed to hold one expert, so a 256-row tile
 // may straddle two.  Every workgroup reads m_indices of its own tiles at
@@ -65,6 +75,7 @@ namespace {
 
 constexpr int kWideRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
 constexpr uint32_t kWideOOB = 0xFFFFFF00u;  // an offset past every buffer range used here
+constexpr int kWideMaxGroups = 1024;        // groups the K-grouped prefix table holds
 
 typedef unsigned int wu32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 wbf16x8 __attribute__((ext_vector_type(8)));
@@ -78,9 +89,10 @@ template <int MODE, bool HASC>
 __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0 || MODE == kDenseBf16 ||
-                    MODE == kDenseAcc,
+                    MODE == kDenseAcc || MODE == kKGrouped,
                 "modes of the wide kernel");
-  constexpr bool ACC = MODE == kDenseAcc;    // fp32 output D = C + A . B^T
+  constexpr bool KG = MODE == kKGrouped;     // groups along K, per-column beta, fp32 D[g] = C[g] + ...
+  constexpr bool ACC = MODE == kDenseAcc || KG;  // fp32 output D = C + A . B^T
   constexpr bool CONTIG = MODE == kContiguous;
   constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
@@ -106,6 +118,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   __shared__ int pass_half[CONTIG ? 2 * MAXT : 1];  // bit h: rows of 128-row half h take part
   __shared__ uint32_t pass_mask[CONTIG ? 2 * MAXT : 1][8];
   __shared__ int tile_np[CONTIG ? MAXT + 1 : 1];
+  __shared__ int kpref[KG ? kWideMaxGroups + 1 : 1];  // K-grouped: first K block of each group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,9 +136,35 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const int KW = (KB + 3) >> 2;  // UE8M0: packed words (four K blocks) per scale row
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;
-  const int T = p.m_tiles * p.n_tiles;
+  const int tpg = p.m_tiles * p.n_tiles;  // tiles per group (K-grouped) or in all
+  const int T = KG ? p.G * tpg : tpg;
   const int n_dp = b < T ? (T - b + G - 1) / G : 0;  // tiles of this workgroup
   if (n_dp == 0) return;  // uniform over the workgroup
+  if constexpr (KG) {
+    // kpref[g] = first K block of group g: prefix of floor(ks / 128), clamped to KB
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < p.G; base += 64) {
+        const int g = base + lane;
+        int v = 0;
+        if (g < p.G) {
+          const int k = p.index[g];
+          v = k > 0 ? (k >> 7) : 0;
+          v = v < KB ? v : KB;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(v, off);
+          if (lane >= off) v += o;
+        }
+        if (g < p.G) kpref[g + 1] = carry + v < KB ? carry + v : KB;
+        carry += __shfl(v, 63);
+        carry = carry < KB ? carry : KB;
+      }
+      if (lane == 0) kpref[0] = 0;
+    }
+    __syncthreads();
+  }
   auto dense_tile = [&](int s, int* mt, int* nt) { grouped_mn(xcd_tile(b + s * G, T), p.m_tiles, p.n_tiles, GM, mt, nt); };
 
   int nseg = n_dp;  // passes (dense: one per tile)
@@ -201,7 +240,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     nseg = __builtin_amdgcn_readfirstlane(tile_np[MAXT]);
     if (nseg == 0) return;  // no row of these tiles is tagged: nothing to store
   }
-  const int J = nseg * KB;
+  int J = nseg * KB;  // iterations of this workgroup (K-grouped: counted below)
 
   const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
   const uint32_t b_bytes = (uint32_t)(CONTIG ? p.G : 1) * (uint32_t)N * (uint32_t)K;
@@ -229,22 +268,58 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
       dense_tile(__builtin_amdgcn_readfirstlane(pass_tile[s]), mt, nt);
       *e = __builtin_amdgcn_readfirstlane(pass_exp[s]);
       *hm = __builtin_amdgcn_readfirstlane(pass_half[s]);
+    } else if constexpr (KG) {
+      // round s of one tile per workgroup, XCD-contiguous inside the round
+      const int left = T - s * G;
+      const int t = s * G + xcd_tile(b, left < G ? left : G);
+      const int g = t / tpg;
+      grouped_mn(t - g * tpg, p.m_tiles, p.n_tiles, GM, mt, nt);
+      *e = g;  // the group (of C and D; A and B are shared)
+      *hm = 3;
     } else {
       dense_tile(s, mt, nt);
       *e = 0;
       *hm = 3;
     }
   };
+  // K blocks [lo, hi) of pass s (K-grouped: its group's; a group without
+  // blocks runs one iteration over zero operands, zero = 1)
+  auto k_range = [&](int e, int* lo, int* hi, int* zero) {
+    *lo = 0;
+    *hi = KB;
+    *zero = 0;
+    if constexpr (KG) {
+      *lo = __builtin_amdgcn_readfirstlane(kpref[e]);
+      *hi = __builtin_amdgcn_readfirstlane(kpref[e + 1]);
+      if (*hi == *lo) {
+        *zero = 1;
+        *hi = *lo + 1;
+      }
+    }
+  };
+
+  if constexpr (KG) {
+    J = 0;
+    for (int s = 0; s < nseg; ++s) {
+      int mt, nt, e, hm, lo, hi, z;
+      tile_of(s, &mt, &nt, &e, &hm);
+      k_range(e, &lo, &hi, &z);
+      J += hi - lo;
+    }
+  }
 
 #define WD_SLOT(st) ((st) == 0 ? slot0 : slot1)
 #define WD_SS(st) (reinterpret_cast<float*>(WD_SLOT(st) + SLOT_S))
 
   // ---- issue pointer: iteration j + 1 of this workgroup's sequence
-  int is_seg = 0, is_kb = 0;
+  int is_seg = 0, is_kb = 0, is_hi = KB, is_zero = 0;
   uint32_t is_aoff[A_INS], is_boff[B_INS], is_soff;
+  const bool bwave = KG && wave >= 4;  // K-grouped: waves 4..7 load beta of the tile's columns
   auto is_setup = [&]() {
     int mt, nt, e, hm;
     tile_of(is_seg, &mt, &nt, &e, &hm);
+    k_range(e, &is_kb, &is_hi, &is_zero);
+    if (KG) e = 0;  // B is shared by the groups
     const int row_limit = rows - mt * BM < BM ? rows - mt * BM : BM;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -258,14 +333,20 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     }
     const int srow = wave * 64 + lane;  // alpha of the tile's rows that exist
     is_soff = srow < BM && srow < row_limit && ((hm >> (srow >> 7)) & 1) ? (uint32_t)((mt * BM + srow) * 4) : kWideOOB;
+    if (bwave) {
+      const int scol = nt * BN + (wave - 4) * 64 + lane;
+      is_soff = scol < N ? (uint32_t)(scol * 4) : kWideOOB;
+    }
   };
   is_setup();
 
 #define WD_ISSUE_BEGIN()                                                                                   \
   const bool in_ = is_seg < nseg;                                                                          \
-  const __amdgpu_buffer_rsrc_t ra_ = wide_rsrc(p.A, in_ ? a_bytes : 0u);                                   \
-  const __amdgpu_buffer_rsrc_t rb_ = wide_rsrc(p.B, in_ ? b_bytes : 0u);                                   \
-  const __amdgpu_buffer_rsrc_t rs_ = wide_rsrc(p.sfa, in_ ? s_bytes : 0u);                                 \
+  const bool ld_ = in_ && !(KG && is_zero);                                                                \
+  const __amdgpu_buffer_rsrc_t ra_ = wide_rsrc(p.A, ld_ ? a_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rb_ = wide_rsrc(p.B, ld_ ? b_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rs_ = bwave ? wide_rsrc(p.sfb, ld_ ? (uint32_t)N * (uint32_t)KB * 4u : 0u)  \
+                                           : wide_rsrc(p.sfa, ld_ ? s_bytes : 0u);                         \
   const int ks_ = is_kb << 7
 #define WD_ISSUE_LOAD(st_, n_)                                                                             \
   do {                                                                                                     \
@@ -278,27 +359,28 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
           is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0);                   \
     else                                                                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(WD_SS(st_) + wave * 64), 4, is_soff,    \
-                                               (UE ? (is_kb >> 2) : is_kb) * rows * 4, 0, 0);              \
+                                               (UE ? (is_kb >> 2) : is_kb) * (bwave ? N : rows) * 4, 0, 0); \
   } while (0)
 #define WD_ISSUE_END()                                                                                     \
   do {                                                                                                     \
-    if (in_ && ++is_kb == KB) {                                                                            \
-      is_kb = 0;                                                                                           \
+    if (in_ && ++is_kb == is_hi) {                                                                         \
       if (++is_seg < nseg) is_setup();                                                                     \
     }                                                                                                      \
   } while (0)
 
   // ---- compute pointer: iteration j
-  int cp_seg = 0, cp_kb = 0;
+  int cp_seg = 0, cp_kb = 0, cp_hi = KB, cp_zero = 0;
   int cp_mt, cp_nt, cp_e, cp_hm;
   tile_of(0, &cp_mt, &cp_nt, &cp_e, &cp_hm);
+  k_range(cp_e, &cp_kb, &cp_hi, &cp_zero);
+  (void)cp_zero;
   const DG_CONST float* sfb_w;
   bool cp_act;  // this wave's rows take part in the pass
   auto cp_setup = [&]() {
     cp_act = !CONTIG || ((cp_hm >> (wm >> 1)) & 1);
     int nblk = (cp_nt * BN + wn * 128) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
-    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)cp_e * NB + nblk) * (UE ? KW : KB));
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + ((int64_t)(KG ? 0 : cp_e) * NB + nblk) * (UE ? KW : KB));
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
@@ -315,7 +397,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   // of row tile i holds row wm*64 + 16 i + l % 16 and, in 64-column half h,
   // columns wn*128 + 64 h + 16 q + [0, 16)
   bool pend = false;
-  int st_row0 = 0, st_col0 = 0;
+  int st_row0 = 0, st_col0 = 0, st_grp = 0;
   uint32_t st_m[8] = {~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u};  // contiguous: rows tagged with the pass's expert
 #define WD_OUT_OFF(i_, h_) /* fp32 byte offset of the lane's run (row tile i_, column half h_), or OOB */ \
   ((st_row0 + wm * 64 + (i_) * 16 + q16 < rows && st_col0 + wn * 128 + (h_) * 64 + q * 16 < N)             \
@@ -327,12 +409,17 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     const uint32_t o_ = WD_OUT_OFF(i_, h_);                                                                \
     _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                                       \
       cv_[4 * h_ + j_] = HASC ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(           \
-                                    rc, o_ == kWideOOB ? kWideOOB : o_ + 16u * j_, 0, 0))                  \
+                                    rcg_, o_ == kWideOOB ? kWideOOB : o_ + 16u * j_, 0, 0))                \
                               : f32x4{0.f, 0.f, 0.f, 0.f};                                                 \
   }
 #define WD_STORE_U()                                                                                       \
   do {                                                                                                     \
     if constexpr (ACC) {                                                                                   \
+      /* K-grouped: C and D of the tile's group */                                                         \
+      const size_t gof_ = KG ? (size_t)st_grp * (size_t)rows * (size_t)N : 0;                              \
+      const __amdgpu_buffer_rsrc_t rdg_ = KG ? wide_rsrc(p.Dacc + gof_, (uint32_t)rows * (uint32_t)N * 4u) : rd; \
+      const __amdgpu_buffer_rsrc_t rcg_ =                                                                  \
+          KG ? wide_rsrc(HASC ? p.Cacc + gof_ : p.Cacc, HASC ? (uint32_t)rows * (uint32_t)N * 4u : 0u) : rc; \
       f32x4 ca_[TN], cb_[TN];                                                                              \
       WD_LOAD_C(ca_, 0);                                                                                   \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
@@ -343,7 +430,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
           const uint32_t o_ = WD_OUT_OFF(i_, h_);                                                          \
           _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                                 \
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(wu32x4, u[i_][4 * h_ + j_] + cur_[4 * h_ + j_]), \
-                                                   rd, o_ == kWideOOB ? kWideOOB : o_ + 16u * j_, 0, 0);   \
+                                                   rdg_, o_ == kWideOOB ? kWideOOB : o_ + 16u * j_, 0, 0); \
         }                                                                                                  \
       }                                                                                                    \
     } else                                                                                                 \
@@ -383,7 +470,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #define WD_STEP(st_, jj_)                                                                                  \
   do {                                                                                                     \
     const bool live_ = (jj_) < J;                                                                          \
-    const float beta_ = UE || BF16 ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                                   \
+    const float beta_ = UE || BF16 || KG ? 1.f : (live_ ? sfb_w[cp_kb] : 0.f);                             \
     /* UE8M0: the iteration's codes sit in byte cp_kb % 4 of their packed words */                        \
     const int ash_ = 8 * (cp_kb & 3);                                                                      \
     const int bcode_ = UE && live_ ? __builtin_bit_cast(int, sfb_w[cp_kb >> 2]) >> ash_ : 0;              \
@@ -441,10 +528,15 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
       WD_FRAG(bf_[0], sl_ + b_row0, 0);                                                                    \
       WD_ISSUE_BEGIN();                                                                                    \
       f32x4 t_[4];                                                                                         \
+      f32x4 bt_[2]; /* K-grouped: beta of fragment j's columns, two j in flight */                         \
+      (void)bt_;                                                                                           \
       _Pragma("unroll") for (int k_ = 0; k_ < TM * TN + 3; ++k_) {                                         \
         if (k_ < TM * TN) {                                                                                \
           const int j_ = k_ / TM;                                                                          \
           if (k_ % TM == 0 && j_ + 1 < TN) WD_FRAG(bf_[(j_ + 1) & 1], sl_ + b_row0, (j_ + 1) * 2048);      \
+          if (KG && k_ % TM == 0) /* beta of the 4 columns of fragment j_ this lane holds */               \
+            bt_[j_ & 1] = *reinterpret_cast<const f32x4*>(                                                 \
+                WD_SS(st_) + 256 + wn * 128 + (j_ >> 2) * 64 + q * 16 + (j_ & 3) * 4);                     \
           if constexpr (UE) /* alpha and beta applied by the matrix cores (exact powers of two) */          \
             t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],        \
                                                                          f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, \
@@ -460,6 +552,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
           if constexpr (UE) {                                                                              \
             uk_ += t_[kk_ & 3]; /* the promotion: one fp32 add of the scaled block product */             \
           } else {                                                                                         \
+            if constexpr (KG) t_[kk_ & 3] *= bt_[(kk_ / TM) & 1];                                          \
             _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
               uk_[v_] = __builtin_fmaf(t_[kk_ & 3][v_], sc_[kk_ % TM], uk_[v_]);                           \
           }                                                                                                \
@@ -469,16 +562,17 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
       }                                                                                                    \
       WD_ISSUE_END();                                                                                      \
     }                                                                                                      \
-    if (live_ && ++cp_kb == KB) { /* a tile is done */                                                    \
+    if (live_ && ++cp_kb == cp_hi) { /* a tile is done */                                                 \
       st_row0 = cp_mt * BM;                                                                                \
       st_col0 = cp_nt * BN;                                                                                \
+      st_grp = cp_e;                                                                                       \
       if (CONTIG) {                                                                                        \
         _Pragma("unroll") for (int w_ = 0; w_ < 8; ++w_) st_m[w_] = __builtin_amdgcn_readfirstlane(pass_mask[cp_seg][w_]); \
       }                                                                                                    \
       pend = true;                                                                                         \
-      cp_kb = 0;                                                                                           \
       if (++cp_seg < nseg) {                                                                               \
         tile_of(cp_seg, &cp_mt, &cp_nt, &cp_e, &cp_hm);                                                    \
+        k_range(cp_e, &cp_kb, &cp_hi, &cp_zero);                                                           \
         cp_setup();                                                                                        \
       }                                                                                                    \
     }                                                                                                      \
@@ -522,6 +616,10 @@ hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseUe8m0, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseBf16)
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseBf16, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kKGrouped && p.Cacc)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kKGrouped, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kKGrouped)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kKGrouped, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseAcc && p.Cacc)
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseAcc, true>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseAcc)

@@ -2,10 +2,12 @@
 D[g] = C[g] + A[:, seg g] . B[:, seg g]^T in fp32) against the oracle
 (oracle.k_grouped_contiguous): ragged M and N, empty groups, one and many
 groups, an unused K tail, C given / absent / in place, many tiles per
-workgroup, the kernel's documented handling of lengths that are negative,
+workgroup on 256 x 128 and 256 x 256 tiles, the kernel's documented handling of lengths that are negative,
 unaligned or run past K, graph replay with device-side length changes,
 integer inputs bit-exact, and the two weight-gradient shapes at full size on
 sampled rows and columns."""
+
+import os
 
 import numpy as np
 import pytest
@@ -66,7 +68,50 @@ def test_k_grouped_matches_oracle(G, M, N, counts, maxt, mode):
     _check(D.cpu().numpy(), qa, sa, qb, sb, ks, None if mode == "none" else c, f"k-grouped G={G} {M}x{N} {mode}")
 
 
-@pytest.mark.parametrize("cus", [1, 7])
+# (cus, G, M, N, counts): 256 x 256 tiles (the wide kernel) once the tiles of
+# all groups fill whole rounds of the capped CUs: ragged M and N, an empty
+# group, several groups and tiles per workgroup
+WIDE = [(1, 1, 256, 256, [384]), (2, 2, 300, 272, None), (3, 3, 513, 400, [1000, 0, 257]), (4, 8, 256, 1040, None)]
+
+
+@pytest.mark.parametrize("cus,G,M,N,counts", WIDE)
+@pytest.mark.parametrize("mode", ["c", "none", "inplace"])
+def test_k_grouped_wide_tiles(capfd, cus, G, M, N, counts, mode):
+    dg.dg_set_num_cus(cus)
+    os.environ["DG_PRINT_CONFIGS"] = "1"
+    try:
+        qa, sa, qb, sb, ks, c = _case(G, M, N, seed=cus * 100 + G + M, counts=counts, max_tokens=700)
+        C = None if mode == "none" else _t(c)
+        D = C if mode == "inplace" else torch.full((G, M, N), float("nan"), dtype=torch.float32, device=DEV)
+        capfd.readouterr()
+        _run(qa, sa, qb, sb, ks, C, D)
+        assert "kernel=wide" in capfd.readouterr().err
+    finally:
+        del os.environ["DG_PRINT_CONFIGS"]
+        dg.dg_set_num_cus(0)
+    _check(D.cpu().numpy(), qa, sa, qb, sb, ks, None if mode == "none" else c,
+           f"k-grouped wide G={G} {M}x{N} {mode} on {cus} CUs")
+
+
+def test_k_grouped_wide_integer_inputs_bit_exact():
+    rng = np.random.default_rng(15)
+    G, M, N, ks = 3, 300, 272, np.array([256, 0, 384], np.int32)
+    K = int(ks.sum())
+    qa = oracle.encode_e4m3(rng.integers(-10, 10, (M, K)).astype(np.float32))
+    qb = oracle.encode_e4m3(rng.integers(-10, 10, (N, K)).astype(np.float32))
+    sa = np.ones((K // 128, M), np.float32)
+    sb = np.ones((K // 128, N), np.float32)
+    c = rng.integers(-5000, 5000, (G, M, N)).astype(np.float32)
+    dg.dg_set_num_cus(2)
+    try:
+        D = _t(c)  # in place
+        _run(qa, sa, qb, sb, ks, D, D)
+    finally:
+        dg.dg_set_num_cus(0)
+    assert np.array_equal(D.cpu().numpy(), oracle.k_grouped_contiguous(qa, sa, qb, sb, ks, c))
+
+
+@pytest.mark.parametrize("cus", [1, 7, 9])  # 1 and 7: 256 x 256 tiles; 9: 256 x 128 tiles
 def test_k_grouped_many_tiles_per_workgroup(cus):
     dg.dg_set_num_cus(cus)
     try:
