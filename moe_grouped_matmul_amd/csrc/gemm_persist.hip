@@ -6,8 +6,9 @@
 // continuous LDS ring, so the next tile's first K blocks load while the
 // current tile finishes and stores.  Used for the dense forms with M > 128
 // where 256 x 256 tiles (gemm_wide.hip) would leave a partial round, for the
-// masked form, for the contiguous form where the wide kernel does not take
-// it (K < 4096, or a partial round) and for the K-grouped form.
+// masked form, and for the contiguous and K-grouped forms where the wide
+// kernel does not take them (the contiguous form with K < 4096, or tiles
+// leaving a partial round).
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: for every 128-wide K block the fp8 partial product of

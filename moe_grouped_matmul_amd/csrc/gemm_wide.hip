@@ -1,7 +1,8 @@
 // Wide-tile persistent block-scaled FP8 GEMM for gfx950: one 512-thread
 // workgroup per CU walks 256 x 256 output tiles.  Modes: the dense form
 // (bf16 output), its UE8M0-scale, BF16-operand and accumulating (fp32
-// D = C + A . B^T) variants, and the M-grouped contiguous form.
+// D = C + A . B^T) variants, the M-grouped contiguous form and the K-grouped
+// form (fp32 per-group output).
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: every 128-wide K block's fp8 partial product of a
