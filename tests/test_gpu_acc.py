@@ -1,7 +1,8 @@
 """Accumulating FP8 GEMM (dg_fp8_gemm_nt_acc, D = C + A.B^T in fp32) against
 the oracle (oracle.gemm_nt_c): skinny (M <= 128), persistent (M > 128) and
 wide (256 x 256 tiles) kernels, with C given, absent and aliased to D, with
-and without K splits, many tiles per workgroup; integer inputs bit-exact."""
+and without K splits, many tiles per workgroup; integer inputs bit-exact; the
+4096 x 7168 x 16384 shape in place at full size on sampled rows and columns."""
 
 import os
 
@@ -132,6 +133,35 @@ def test_acc_integer_inputs_bit_exact(M, N, K):
         dg.dg_fp8_gemm_nt_acc(_t(qa), _t(sa), _t(qb), _t(sb), _t(c), D, _ws(M, N, K) if ws else None)
         torch.cuda.synchronize()
         assert np.array_equal(D.cpu().numpy(), ref)
+
+
+@pytest.mark.timeout(600)
+def test_acc_full_size_in_place():
+    # the accumulate workload's shape and configuration: C = D in place, 256 x 256 tiles
+    M, N, K, seed = 4096, 7168, 16384, 200
+    a32, b32 = workloads.dense(M, N, K, seed)
+    A32, B32 = _t(a32), _t(b32)
+    A = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    SA = torch.empty((K // 128, M), dtype=torch.float32, device=DEV)
+    B = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+    SB = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=DEV)
+    dg.dg_quant_1x128(A32, A, SA)
+    dg.dg_quant_128x128(B32, B, SB)
+    del A32, B32
+    rng = np.random.default_rng(seed + 1)
+    c = (rng.standard_normal((M, N)) * 3.0).astype(np.float32)
+    D = _t(c)
+    dg.dg_fp8_gemm_nt_acc(A, SA, B, SB, D, D, _ws(M, N, K))
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, M // 2, M - 1} | set(int(r) for r in rng.integers(0, M, 9))))
+    ri = torch.from_numpy(rows).to(DEV)
+    qa, sa = oracle.quant_1x128(a32[rows])
+    assert np.array_equal(A.index_select(0, ri).cpu().numpy(), qa)
+    got = D.index_select(0, ri).cpu().numpy()
+    for blk in (0, 27, 55):
+        c0, c1 = 128 * blk, 128 * blk + 128
+        qb, sb = oracle.quant_128x128(b32[c0:c1])
+        _check(got[:, c0:c1], qa, sa, qb, sb, c[rows][:, c0:c1], f"acc full size columns {c0}:{c1}")
 
 
 def test_mfma_dot_product_truncation_bound():
