@@ -643,12 +643,8 @@ def run_kgrouped(args, torch, dg, workloads):
                               algorithmic_flops_per_launch=round(p["flops"]),
                               algorithmic_bytes_per_launch=round(p["bytes"])))
     big = max(per_shape, key=lambda r: r["gemm_us"])
-    # the library's tile rule for this form: 256 x 256 tiles of all groups where
-    # they fill whole rounds of the CUs to >= 85%, else 256 x 128 tiles
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tw = big["G"] * -(-big["M"] // 256) * -(-big["N"] // 256)
-    wide = big["M"] >= 256 and big["N"] >= 256 and tw / (-(-tw // cus) * cus) >= 0.85
-    kname = "fp8_gemm_wide_kernel<k_grouped>" if wide else "fp8_gemm_persistent_kernel<k_grouped>"
+    plan = dg.dg_describe_plan(dg.DG_OP_K_GROUPED, big["M"], big["N"], big["K"], big["G"])
+    kname = "fp8_gemm_wide_kernel<k_grouped>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<k_grouped>"
     roof = dict(bound="mfma", achieved=big["tflops"], peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
                 frac=round(big["tflops"] / PEAK_FP8_TFLOPS, 4), traffic=None,
                 kernel=f"{kname} ({big['M']}x{big['N']})", avg_launch_us=big["gemm_us"])

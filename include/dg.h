@@ -61,7 +61,14 @@ enum {
 };
 
 /* Operation ids for dg_get_workspace_size. */
-enum { DG_OP_GEMM_NT = 0, DG_OP_CONTIGUOUS = 1, DG_OP_MASKED = 2, DG_OP_BF16_GEMM_NT = 3, DG_OP_GEMM_NT_UE8M0 = 4 };
+enum {
+  DG_OP_GEMM_NT = 0,
+  DG_OP_CONTIGUOUS = 1,
+  DG_OP_MASKED = 2,
+  DG_OP_BF16_GEMM_NT = 3,
+  DG_OP_GEMM_NT_UE8M0 = 4,
+  DG_OP_K_GROUPED = 5 /* dg_k_grouped_fp8_gemm_nt_contiguous (plan description only) */
+};
 
 /*
  * Dense GEMM.  Lesson 13, Fig. 13-1; DeepGEMM's "normal" GEMM (the Feb-2025
@@ -241,8 +248,9 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
 /* Text description of the launch plan the library would use for `op` at this
  * shape on the current device with a full workspace, e.g. "kernel=wide
  * tile=256x256 grid=256 tiles=448 whole=448 tail=0x1" (DG_OP_GEMM_NT,
- * DG_OP_GEMM_NT_UE8M0, DG_OP_BF16_GEMM_NT and DG_OP_CONTIGUOUS, rows = M_total
- * and G the expert count there; "" for other ops or invalid shapes).  The pointer stays valid until the next call on the
+ * DG_OP_GEMM_NT_UE8M0, DG_OP_BF16_GEMM_NT, DG_OP_CONTIGUOUS with rows = M_total
+ * and G the expert count, and DG_OP_K_GROUPED with rows = M, G the group
+ * count and K the total K; "" for other ops or invalid shapes).  The pointer stays valid until the next call on the
  * same thread. */
 const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
 

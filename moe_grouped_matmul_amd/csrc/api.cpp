@@ -102,6 +102,14 @@ bool wide_fill(int64_t M, int64_t N, int cus) {
   return (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85;
 }
 
+// K-grouped form: 256 x 256 tiles of all groups where they fill whole rounds
+// of the CUs to >= 85% (the dense rule), else 256 x 128 tiles.
+bool kgrouped_wide(int64_t G, int64_t M, int64_t N, int cus) {
+  const int64_t tw = G * ceil_div(M, 256) * ceil_div(N, 256);
+  return M >= 256 && N >= 256 && tw <= ((int64_t)1 << 31) - 1 &&
+         (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85;
+}
+
 struct DensePlan {
   bool persist;  // persistent kernel (gemm_persist.hip), M > 128
   bool wide;     // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
@@ -537,11 +545,7 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.K = (int)K;
   p.G = (int)G;
   const int ecus = effective_cus(cus);
-  // 256 x 256 tiles of all groups where they fill whole rounds of the CUs to
-  // >= 85% (as the dense rule), else 256 x 128 tiles
-  const int64_t tw = G * ceil_div(M, 256) * ceil_div(N, 256);
-  const bool wide = M >= 256 && N >= 256 && tw <= ((int64_t)1 << 31) - 1 &&
-                    (double)tw / (double)(ceil_div(tw, ecus) * ecus) >= 0.85;
+  const bool wide = kgrouped_wide(G, M, N, ecus);
   p.m_tiles = (int)ceil_div(M, 256);
   p.n_tiles = (int)ceil_div(N, wide ? 256 : 128);
   p.splits = 1;
@@ -854,7 +858,8 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   (void)G;
   thread_local std::string text;
   text.clear();
-  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0 && op != DG_OP_BF16_GEMM_NT) ||
+  if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0 && op != DG_OP_BF16_GEMM_NT &&
+       op != DG_OP_K_GROUPED) ||
       rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128) || N % 16)
     return text.c_str();
   int cus = 0;
@@ -870,6 +875,16 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
     const ContigPlan cp = plan_contiguous(rows, N, K, G < 1 ? 1 : G, effective_cus(cus));
     std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx256 grid=%d", cp.wide ? "wide" : (cp.persist ? "persistent" : "grid"),
                   cp.wide ? 256 : 128, cp.grid);
+    text = buf;
+    return text.c_str();
+  }
+  if (op == DG_OP_K_GROUPED) {
+    const int64_t g = G < 1 ? 1 : G;
+    const int ecus = effective_cus(cus);
+    const bool wide = kgrouped_wide(g, rows, N, ecus);
+    const int64_t tiles = g * ceil_div(rows, 256) * ceil_div(N, wide ? 256 : 128);
+    std::snprintf(buf, sizeof(buf), "kernel=%s tile=256x%d grid=%lld tiles=%lld", wide ? "wide" : "persistent",
+                  wide ? 256 : 128, (long long)(tiles < ecus ? tiles : ecus), (long long)tiles);
     text = buf;
     return text.c_str();
   }

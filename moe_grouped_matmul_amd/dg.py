@@ -30,6 +30,7 @@ DG_OP_CONTIGUOUS = 1
 DG_OP_MASKED = 2
 DG_OP_BF16_GEMM_NT = 3
 DG_OP_GEMM_NT_UE8M0 = 4
+DG_OP_K_GROUPED = 5
 
 EXPORTED = (
     "dg_fp8_gemm_nt",

@@ -178,6 +178,10 @@ def test_dense_planner_choice(lib):
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 7168, 16384) == 0
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 4096, 2112, 7168)
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 2112, 7168) > 0
+        # K-grouped: 256 x 256 tiles of all groups where they fill whole rounds, else 256 x 128
+        assert "kernel=wide tile=256x256 grid=256 tiles=3584" in dg.dg_describe_plan(dg.DG_OP_K_GROUPED, 4096, 7168,
+                                                                                       33536, 8)
+        assert "kernel=persistent tile=256x128" in dg.dg_describe_plan(dg.DG_OP_K_GROUPED, 300, 144, 1024, 3)
         # BF16: the same rule (K counted in bf16 elements, a multiple of 64)
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 4096, 7168, 16384)
         assert dg.dg_get_workspace_size(dg.DG_OP_BF16_GEMM_NT, 4096, 7168, 16384) == 0
