@@ -51,7 +51,10 @@ def _gpu_dense(qa, sa, qb, sb, M, N, K, workspace=True):
 
 # ---------------------------------------------------------------- quantisers
 
-@pytest.mark.parametrize("G,M,K", [(1, 1, 128), (1, 70, 512), (3, 33, 384), (1, 64, 7168)])
+# the last two cases have 65576 and 65688 groups: a grid of over 4096
+# workgroups whose last one is partly filled
+@pytest.mark.parametrize("G,M,K", [(1, 1, 128), (1, 70, 512), (3, 33, 384), (1, 64, 7168), (1, 1171, 7168),
+                                   (3, 391, 7168)])
 def test_quant_1x128_bit_exact(G, M, K):
     rng = np.random.default_rng(G * 100 + M)
     x = rng.standard_normal((G, M, K), dtype=np.float32) * np.exp2(rng.integers(-30, 30, (G, M, 1))).astype(np.float32)

@@ -42,7 +42,10 @@ def _edge_rows(M, K, seed):
     return x
 
 
-@pytest.mark.parametrize("G,M,K", [(1, 64, 128), (1, 37, 640), (3, 20, 1024), (1, 300, 512), (2, 9, 1152)])
+# the last case has 65688 groups: a grid of over 4096 workgroups whose last
+# one is partly filled
+@pytest.mark.parametrize("G,M,K", [(1, 64, 128), (1, 37, 640), (3, 20, 1024), (1, 300, 512), (2, 9, 1152),
+                                   (3, 391, 7168)])
 def test_quant_1x128_ue8m0_bit_exact(G, M, K):
     x = np.stack([_edge_rows(M, K, 10 * g + K) for g in range(G)])
     q = torch.empty((G, M, K), dtype=torch.uint8, device=DEV)
