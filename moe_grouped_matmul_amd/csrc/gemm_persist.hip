@@ -31,8 +31,10 @@
 //     that expert, and only the masked rows are stored;
 //   * masked (Lesson 13, Fig. 13-3, masked layout): every workgroup reads
 //     masked_m on the device and builds the prefix sums of the active tiles
-//     per group, sum_g ceil(masked_m[g] / 128) * ceil(N / 256); task ids are
-//     walked round-robin and located by binary search, so only the 128-row
+//     per group, sum_g ceil(masked_m[g] / 128) * ceil(N / 256); each round
+//     hands every XCD a contiguous run of task ids, ids inside a group walk
+//     column tiles with that tile's row tiles adjacent (they share the B tile
+//     in one L2), and an id is located by binary search, so only the 128-row
 //     tiles holding rows below masked_m are computed, only those rows are
 //     loaded and stored, and the launch shape is fixed (graph-capturable);
 //   * K-grouped (the weight-gradient family of the deep-dive blog, section 3):
@@ -269,6 +271,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       r.kb_hi = r.kb_lo + p.sk_kb < KB ? r.kb_lo + p.sk_kb : KB;
     }
     if (MODE == kMasked) {
+      // round s of one task per workgroup, XCD-contiguous inside the round;
+      // inside a group the row tiles of one column tile are adjacent tasks,
+      // so they run together on one XCD and share that B tile in its L2
+      const int left = T - s * G;
+      d = s * G + xcd_tile(b, left < G ? left : G);
       int lo = 0, hi = ngrp - 1;  // largest g with pref[g] <= d
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -278,9 +285,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       r.grp = __builtin_amdgcn_readfirstlane(lo);
       r.bgrp = r.grp;
       const int local = d - __builtin_amdgcn_readfirstlane(pref[r.grp]);
-      r.mt = local / p.n_tiles;
-      r.nt = local - r.mt * p.n_tiles;
       const int mm = __builtin_amdgcn_readfirstlane(mmv[r.grp]);
+      const int mtg = (mm + BM - 1) / BM;  // >= 1: the group has tasks
+      r.nt = local / mtg;
+      r.mt = local - r.nt * mtg;
       r.row_limit = mm - r.mt * BM < BM ? mm - r.mt * BM : BM;
     } else if constexpr (KG) {
       // round s of one tile per workgroup, XCD-contiguous inside the round
