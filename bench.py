@@ -19,9 +19,16 @@ Output: one JSON line with the whole-step FP8 TFLOPS, per-shape GEMM TFLOPS,
 GB/s and fraction of the MI355X roofline, the dominant kernel's roofline, and
 the CPU oracle timed on a bounded sample of the same workload.
 
+The default run also times the M-grouped calls beside the step (not part of
+`value`): the contiguous form (8 experts, tokens per expert uniform in
+[1, 8192], (N, K) in {(4096, 7168), (7168, 2048)}) and the masked form
+(32 experts x 256 rows, masked_m uniform in [0, 256], same (N, K)), each call
+over rotating buffer sets; their rows join `per_shape` and `roofline_by_form`
+holds one roofline per form (--no-grouped skips them).
+
 Other workloads: --workload large | small (one dense shape), contiguous | masked
-(the M-grouped forms), bf16 | acc | kgrouped | ue8m0 (the BF16, accumulating,
-K-grouped and UE8M0-scale variants).
+(the M-grouped forms as the timed step), bf16 | acc | kgrouped | ue8m0 (the
+BF16, accumulating, K-grouped and UE8M0-scale variants).
 """
 
 import argparse
@@ -116,6 +123,8 @@ def parse():
     ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc",
                                                               "kgrouped", "ue8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="sweep only: skip the per-call timing of the contiguous and masked calls")
     ap.add_argument("--shapes", default="",
                     help="comma-separated indices into the workload's shape list (default: all; the sweep has 18, "
                          "the grouped workloads 2)")
@@ -249,7 +258,7 @@ def run_dense(args, torch, dg, workloads):
         del gq, gg
         t_us = g_ms * 1e3
         rt = roof_time_us(p["flops"], p["bytes"])
-        per_shape.append(dict(M=p["M"], N=p["N"], K=p["K"], gemm_us=round(t_us, 2), quant_us=round(q_ms * 1e3, 2),
+        per_shape.append(dict(form="dense", M=p["M"], N=p["N"], K=p["K"], gemm_us=round(t_us, 2), quant_us=round(q_ms * 1e3, 2),
                               tflops=round(p["flops"] / t_us / 1e6, 1), gbs=round(p["bytes"] / t_us / 1e3, 1),
                               bound="mfma" if p["flops"] / (PEAK_FP8_TFLOPS * 1e12) >= p["bytes"] / (PEAK_HBM_GBS * 1e9)
                               else "hbm", roof_frac=round(rt / t_us, 4), kernel=p["kernel"]))
@@ -281,20 +290,24 @@ def run_dense(args, torch, dg, workloads):
                 shapes=[(p["M"], p["N"], p["K"]) for p in prepared])
 
 
-def run_grouped(args, torch, dg, workloads):
+def run_grouped(args, torch, dg, workloads, form=None, timed=True):
     """M-grouped contiguous (8 experts, tokens per expert uniform in [1, 8192],
     segments padded to 128) or masked (32 experts x 256 capacity, masked_m
     uniform in [0, 256]) GEMMs for both (N, K) pairs.  Activations arrive
     already in e4m3 (as from an expert-parallel dispatch), so a step is the two
-    grouped GEMM calls."""
+    grouped GEMM calls.  form: "contiguous" | "masked" (default: the workload);
+    timed=False measures only the per-call kernel times (graphs of
+    back-to-back launches over the rotating sets), as the default sweep run
+    does for the grouped forms."""
     dev = torch.device("cuda:0")
-    cfgs = workloads.CONFIGS[args.workload]
-    if args.shapes:
+    form = form or args.workload
+    cfgs = workloads.CONFIGS[form]
+    if args.shapes and form == args.workload:
         cfgs = [cfgs[int(i)] for i in args.shapes.split(",")]
     prepared = []
     for c in cfgs:
         G, N, K = c["G"], c["N"], c["K"]
-        if args.workload == "contiguous":
+        if form == "contiguous":
             w = workloads.contiguous(G, N, K, c["seed"])
             rows_total = w["m_total"]
             A32 = torch.from_numpy(w["a"]).to(dev)
@@ -340,14 +353,20 @@ def run_grouped(args, torch, dg, workloads):
         sets = [dict(a8=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(),
                      b8=B8 if i == 0 else B8.clone(), sb=SB if i == 0 else SB.clone(),
                      d=torch.empty(d_shape, dtype=torch.bfloat16, device=dev)) for i in range(nsets)]
+        if form == "contiguous":
+            plan = dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, rows_total, N, K, G)
+            kname = ("fp8_gemm_wide_kernel<contiguous>" if "kernel=wide" in plan
+                     else "fp8_gemm_persistent_kernel<contiguous>")
+        else:
+            kname = "fp8_gemm_persistent_kernel<masked>"
         prepared.append(dict(G=G, N=N, K=K, sets=sets, index=index, flops=flops, bytes=nbytes, counts=counts,
-                             rows=rows_total if args.workload == "contiguous" else G * c["max_m"]))
+                             rows=rows_total if form == "contiguous" else G * c["max_m"], kernel=kname))
     torch.cuda.synchronize()
     timer = Timer(torch)
 
     def gemm(p, i):
         st = p["sets"][i % len(p["sets"])]
-        if args.workload == "contiguous":
+        if form == "contiguous":
             dg.dg_m_grouped_fp8_gemm_nt_contiguous(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"])
         else:
             dg.dg_m_grouped_fp8_gemm_nt_masked(st["a8"], st["sa"], st["b8"], st["sb"], st["d"], p["index"],
@@ -360,7 +379,7 @@ def run_grouped(args, torch, dg, workloads):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ms_per_step, wall = timed_steps(torch, timer, step, args)
+    ms_per_step, wall = timed_steps(torch, timer, step, args) if timed else (None, None)
     per_shape = []
     for p in prepared:
         launches = max(len(p["sets"]), 4)  # every set once per replay: cold HBM
@@ -369,10 +388,11 @@ def run_grouped(args, torch, dg, workloads):
         del gg
         rt = roof_time_us(p["flops"], p["bytes"])
         mf = p["flops"] / (PEAK_FP8_TFLOPS * 1e12) >= p["bytes"] / (PEAK_HBM_GBS * 1e9)
-        per_shape.append(dict(G=p["G"], N=p["N"], K=p["K"], rows=p["rows"], valid_rows=int(sum(max(c, 0) for c in p["counts"])),
+        per_shape.append(dict(form=form, G=p["G"], N=p["N"], K=p["K"], rows=p["rows"],
+                              valid_rows=int(sum(max(c, 0) for c in p["counts"])),
                               gemm_us=round(t_us, 2), tflops=round(p["flops"] / t_us / 1e6, 1),
                               gbs=round(p["bytes"] / t_us / 1e3, 1), bound="mfma" if mf else "hbm",
-                              roof_frac=round(rt / t_us, 4)))
+                              roof_frac=round(rt / t_us, 4), kernel=p["kernel"]))
     big = max(per_shape, key=lambda r: r["gemm_us"])
     if big["bound"] == "mfma":
         roof = dict(bound="mfma", achieved=big["tflops"], peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
@@ -381,16 +401,12 @@ def run_grouped(args, torch, dg, workloads):
         roof = dict(bound="hbm", achieved=big["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(big["gbs"] / PEAK_HBM_GBS, 4))
     big_p = next(p for p in prepared if p["N"] == big["N"] and p["K"] == big["K"])
-    if args.workload == "contiguous":
-        plan = dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, big_p["rows"], big_p["N"], big_p["K"], big_p["G"])
-        kname = "fp8_gemm_wide_kernel<contiguous>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<contiguous>"
-    else:
-        kname = "fp8_gemm_persistent_kernel<masked>"
-    label = f"{kname} ({big['N']}x{big['K']})"
-    roof.update(traffic=recorded_traffic(label, args.workload), kernel=label,
+    label = f"{big_p['kernel']} ({big['N']}x{big['K']})"
+    roof.update(traffic=recorded_traffic(label, form), kernel=label,
                 algorithmic_bytes_per_launch=round(big_p["bytes"]),
+                algorithmic_flops_per_launch=round(big_p["flops"]),
                 avg_launch_us=big["gemm_us"])
-    name = "m_grouped_contiguous_8x_tokens_1to8192" if args.workload == "contiguous" else "m_grouped_masked_32x256"
+    name = "m_grouped_contiguous_8x_tokens_1to8192" if form == "contiguous" else "m_grouped_masked_32x256"
     config = dict(workload=name, shapes=[f"G={p['G']} N={p['N']} K={p['K']}" for p in prepared],
                   step="grouped GEMM per (N,K) pair", cold_hbm=True)
     return dict(ms_per_step=ms_per_step, wall_s=wall, step_flops=sum(p["flops"] for p in prepared),
@@ -398,16 +414,19 @@ def run_grouped(args, torch, dg, workloads):
 
 
 def cpu_baseline(shapes, workloads):
-    """The CPU oracle as it stands, on the first min(M, 1024) rows of each shape:
-    activation quantisation + GEMM timed (weights quantised beforehand, untimed)."""
+    """The CPU oracle as it stands, on the first min(M, CPU_SAMPLE_ROWS) rows of
+    each shape: activation quantisation + GEMM timed (weights quantised
+    beforehand, untimed), with the BLAS thread pool set to the cores this
+    process may run on (os.sched_getaffinity)."""
     import oracle
 
+    threads = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_limits
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        limiter = None
     t_total = 0.0
     flops = 0.0
     for (M, N, K), s in shapes:
@@ -419,6 +438,8 @@ def cpu_baseline(shapes, workloads):
         oracle.gemm_nt(qa, sa, qb, sb)
         t_total += time.perf_counter() - t0
         flops += 2.0 * rows * N * K
+    if limiter is not None:
+        limiter.unregister()
     return dict(value=round(flops / t_total / 1e12, 5), unit="TFLOPS", cores=int(threads), kind="oracle",
                 sample=f"first min(M,{CPU_SAMPLE_ROWS}) rows of each of the {len(shapes)} shapes: fp64 oracle 1x128 quantisation "
                        f"+ promoted GEMM + bf16 rounding ({flops / 1e9:.1f} GFLOP in {t_total:.1f} s); "
@@ -686,6 +707,18 @@ def main():
         config = dict(workload=name, shapes=[f"{m}x{n}x{k}" for m, n, k in r["shapes"]],
                       scales="1x128 activations, 128x128 weights, fp32", out="bf16",
                       step="dg_quant_1x128 + dg_fp8_gemm_nt per shape", cold_hbm=True)
+        if args.workload == "sweep" and not args.no_grouped and not args.shapes:
+            # the two M-grouped forms' calls, timed per call beside the step
+            # (not part of `value`): per-call rows and one roofline per form
+            r["roofline_by_form"] = {"dense": r["roofline"]}
+            grouped_names = []
+            for form in ("contiguous", "masked"):
+                torch.cuda.empty_cache()
+                g = run_grouped(args, torch, dg, workloads, form=form, timed=False)
+                r["per_shape"] = r["per_shape"] + g["per_shape"]
+                r["roofline_by_form"][form] = g["roofline"]
+                grouped_names.append(g["name"])
+            config["per_call_only"] = grouped_names
     elif args.workload in ("bf16", "acc", "kgrouped", "ue8m0"):
         r = {"bf16": run_bf16, "acc": run_acc, "kgrouped": run_kgrouped, "ue8m0": run_ue8m0}[args.workload](
             args, torch, dg, workloads)
@@ -715,6 +748,8 @@ def main():
         "per_shape": r["per_shape"],
         "roofline": r["roofline"],
     }
+    if "roofline_by_form" in r:
+        line["roofline_by_form"] = r["roofline_by_form"]
     if not args.no_cpu_baseline and args.workload in ("sweep", "large", "small"):
         shp = workloads.CONFIGS["dense_sweep"] if args.workload == "sweep" else \
             workloads.CONFIGS["dense_large"] if args.workload == "large" else workloads.CONFIGS["dense_small"]

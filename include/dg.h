@@ -39,6 +39,14 @@
  *     contiguous form, rows past masked_m of the masked form) are never
  *     written.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Sizes: the kernels address one launch's activations, scales and
+ *     outputs, and one expert's weights, with 32-bit byte offsets from 64-bit
+ *     bases.  A call with more rows than that allows runs as several row
+ *     chunks enqueued back to back on `stream` (each planned on its own; the
+ *     results are those of one launch per chunk).  Rejected with DG_ERR_SHAPE:
+ *     one expert's weights of 4 GiB or more ((N + 256) * K bytes, bf16: twice
+ *     that), activation scales of 4 GiB or more, more than 1024 groups, and
+ *     the K-grouped form past 32-bit offsets (see there).
  */
 #ifndef DG_H
 #define DG_H
@@ -53,7 +61,8 @@ extern "C" {
 enum {
   DG_OK = 0,
   DG_ERR_INVALID_ARG = 1, /* null pointer, bad enum value */
-  DG_ERR_SHAPE = 2,       /* K % 128 (K % 64 for bf16), N % 16, negative sizes, G out of range */
+  DG_ERR_SHAPE = 2,       /* K % 128 (K % 64 for bf16), N % 16, negative sizes, G out of [1, 1024],
+                             weights of 4 GiB or more per expert */
   DG_ERR_ALIGN = 3,       /* pointer alignment */
   DG_ERR_WORKSPACE = 4,   /* workspace pointer given with a size that is not a multiple of 4 */
   DG_ERR_DEVICE = 5,      /* no HIP device, or the current device is not gfx950 */
@@ -106,7 +115,8 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
  * Each aligned block of dg_get_m_alignment_for_contiguous_layout() rows must
  * hold rows of at most one expert (segments padded to that alignment); rows
  * of a block whose index differs from the block's expert are not written.
- * workspace: unused, pass NULL/0.
+ * G must be in [1, 1024]; each expert's weights are addressed from the
+ * expert's own base.  workspace: unused, pass NULL/0.
  */
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B,
                                         const float* sfb, uint16_t* D, const int32_t* m_indices,
@@ -123,8 +133,12 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
  *   masked_m [G] int32, device: expert g's rows [0, clamp(masked_m[g],0,max_m))
  *            are computed; all other rows of D are not written
  *   D        [G,max_m,N] bf16
- * expected_m: host hint of the typical masked_m (0 = unknown); it may only
- *   change speed, never results.  workspace: unused, pass NULL/0.
+ * G must be in [1, 1024]; each expert's A, alpha, weights and D are
+ * addressed from the expert's own base, so one expert's rows must fit 32-bit
+ * offsets ((max_m + 256) * K and max_m * N * 2 bytes below 4 GiB).
+ * expected_m: host hint of the typical masked_m (0 = unknown); it is not
+ *   used (the launch shape and the results never depend on it).
+ * workspace: unused, pass NULL/0.
  */
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const uint8_t* B,
                                     const float* sfb, uint16_t* D, const int32_t* masked_m,
@@ -139,9 +153,8 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
  *   C [M,N] fp32, row-major, or NULL (read as zeros); may equal D (in place)
  *   D [M,N] fp32, row-major (written)
  * D = fl32(C + acc): the fp32 accumulator of the promoted GEMM plus C, rounded
- * once.  workspace as for dg_fp8_gemm_nt (same size query, DG_OP_GEMM_NT).
- * Shapes whose fp32 output exceeds 32-bit byte offsets (M > 128) are rejected
- * with DG_ERR_SHAPE.
+ * once.  workspace as for dg_fp8_gemm_nt (same size query, DG_OP_GEMM_NT,
+ * which covers both forms).
  */
 int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                        const float* C, float* D, int64_t M, int64_t N, int64_t K, void* workspace,
@@ -185,8 +198,7 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
  * K must be a multiple of 64, N of 16.  workspace: as for dg_fp8_gemm_nt
  * (optional, lets a partial last round of tiles split along K; size from
  * dg_get_workspace_size(DG_OP_BF16_GEMM_NT, M, N, K, 1); zero-filled before
- * first use, left reusable).  Problems whose byte offsets exceed 32 bits are
- * rejected with DG_ERR_SHAPE.
+ * first use, left reusable).
  */
 int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, void* stream);
@@ -231,8 +243,7 @@ int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t 
  * dg_fp8_gemm_nt_ue8m0: D [M,N] bf16 = A . B^T with those scales; the matrix
  * cores apply the scales and add each K block's product to the fp32
  * accumulator, rounded once.  workspace as for dg_fp8_gemm_nt (size from
- * dg_get_workspace_size(DG_OP_GEMM_NT_UE8M0, M, N, K, 1)); problems whose
- * byte offsets exceed 32 bits are rejected with DG_ERR_SHAPE.
+ * dg_get_workspace_size(DG_OP_GEMM_NT_UE8M0, M, N, K, 1)).
  */
 int dg_quant_1x128_ue8m0(const float* x, uint8_t* q, int32_t* sfa, int64_t G, int64_t M, int64_t K,
                          void* stream);
@@ -242,7 +253,9 @@ int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
                          uint16_t* D, int64_t M, int64_t N, int64_t K, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Workspace bytes that let `op` use its full K split for this shape (0 = none used). */
+/* Workspace bytes that let `op` use its full K split for this shape with the
+ * current CU cap (0 = none used); a call split into row chunks reuses it for
+ * every chunk. */
 size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
 
 /* Text description of the launch plan the library would use for `op` at this
@@ -250,8 +263,17 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
  * tile=256x256 grid=256 tiles=448 whole=448 tail=0x1" (DG_OP_GEMM_NT,
  * DG_OP_GEMM_NT_UE8M0, DG_OP_BF16_GEMM_NT, DG_OP_CONTIGUOUS with rows = M_total
  * and G the expert count, and DG_OP_K_GROUPED with rows = M, G the group
- * count and K the total K; "" for other ops or invalid shapes).  The pointer stays valid until the next call on the
- * same thread. */
+ * count and K the total K; "" for other ops or invalid shapes); for a call
+ * split into row chunks it describes the first chunk and ends in "chunks=n".
+ * The pointer stays valid until the next call on the same thread.
+ * Debugging aids, read from the environment on every call:
+ *   DG_FORCE_CONFIG   comma-separated; "kernel=wide" / "kernel=persistent"
+ *                     force the 256x256 or the 256x128 (128x256 grouped) tile
+ *                     kernel wherever the planner chooses between them, and
+ *                     "chunk_rows=<n>" splits calls into row chunks of at
+ *                     most n rows (rounded down to a multiple of 256, at
+ *                     least 256); results stay within the same bounds
+ *   DG_PRINT_CONFIGS  print every launch's plan on stderr */
 const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
 
 /* Row alignment of expert segments in the contiguous layout (deep-dive blog,

@@ -1,7 +1,28 @@
 // C ABI of the library: argument validation, tile-configuration choice and
 // launch on the caller's stream.  No allocation, no synchronisation, no host
 // reads of device data, so every call can be captured into a hipGraph.
+//
+// The kernels address one launch's activations, scales and outputs, and one
+// expert's weights, with 32-bit byte offsets from 64-bit bases.  A call whose
+// rows would not fit is split into row chunks launched back to back on the
+// same stream (each chunk its own plan; chunks that share a split-K
+// workspace run in stream order, and every launch leaves its counters at
+// zero).  Only weights of 4 GiB or more per expert, more than 1024 groups
+// and the K-grouped form past 32-bit offsets are rejected (DG_ERR_SHAPE).
+//
+// DG_FORCE_CONFIG (debug, read on every call): a comma-separated list of
+//   kernel=wide|persistent  force the 256x256 or the 256x128 / 128x256 tile
+//                           kernel where the planner chooses between them
+//                           (rows > 128, or the contiguous form)
+//   chunk_rows=<n>          at most n rows per launch (rounded down to a
+//                           multiple of 256, at least 256)
+//   skinny=<bm>x<wn>x<s>x<p>  rows <= 128: bm-row tiles (64 | 128) of 4 wn
+//                           columns (wn 16 | 32), K split s ways (bounded by
+//                           the K blocks and the workspace), ring depth p
+//                           among the compiled ones (dg::skinny_depth_ok)
+// DG_PRINT_CONFIGS (debug): print each launch's plan on stderr.
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -21,6 +42,11 @@ constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other; CU count cached alongside
 std::atomic<int> g_dev_kind[kMaxDevices];
 std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Byte offsets a kernel may use inside one buffer range: below the
+// out-of-range marker (0xFFFFFF00) the kernels give lanes outside a tile.
+constexpr int64_t kOffLim = (int64_t)0xFFFFFF00 - 4096;
+constexpr int64_t kMaxGroups = 1024;
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -69,9 +95,71 @@ int check_device(int* cus) {
   return DG_OK;
 }
 
+// CU count of the current device for the planning queries (256, the
+// MI355X's, when no device is visible).
+int query_cus() {
+  int cus = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  }
+  (void)hipGetLastError();
+  return cus > 0 ? cus : 256;
+}
+
 int effective_cus(int device_cus) {
   const int cap = g_cu_cap.load(std::memory_order_relaxed);
   return (cap > 0 && cap < device_cus) ? cap : device_cus;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- DG_FORCE_CONFIG
+enum ForceKernel { kForceNone = 0, kForceWide = 1, kForcePersistent = 2 };
+struct Force {
+  int kernel = kForceNone;
+  int64_t chunk_rows = 0;
+  int sk_bm = 0, sk_wn = 0, sk_splits = 0, sk_depth = 0;  // skinny=<bm>x<wn>x<s>x<p>
+};
+Force forced() {
+  Force f;
+  const char* e = std::getenv("DG_FORCE_CONFIG");
+  if (!e) return f;
+  std::string s(e);
+  size_t pos = 0;
+  while (pos <= s.size()) {
+    size_t end = s.find(',', pos);
+    if (end == std::string::npos) end = s.size();
+    const std::string item = s.substr(pos, end - pos);
+    if (item == "kernel=wide") f.kernel = kForceWide;
+    else if (item == "kernel=persistent") f.kernel = kForcePersistent;
+    else if (item.rfind("chunk_rows=", 0) == 0) f.chunk_rows = std::atoll(item.c_str() + 11);
+    else if (item.rfind("skinny=", 0) == 0) {
+      int bm = 0, wn = 0, sp = 0, d = 0;
+      if (std::sscanf(item.c_str() + 7, "%dx%dx%dx%d", &bm, &wn, &sp, &d) == 4 && (bm == 64 || bm == 128) &&
+          (wn == 16 || wn == 32) && sp >= 1 && dg::skinny_depth_ok(bm, wn, d)) {
+        f.sk_bm = bm;
+        f.sk_wn = wn;
+        f.sk_splits = sp;
+        f.sk_depth = d;
+      }
+    }
+    pos = end + 1;
+  }
+  return f;
+}
+bool print_configs() { return std::getenv("DG_PRINT_CONFIGS") != nullptr; }
+
+// Rows per launch (a multiple of 256): A rows of row_bytes each (plus one
+// tile of overhang) and output rows of out_bytes each stay inside 32-bit
+// offsets; 0 when not even 256 rows fit.
+int64_t launch_rows(int64_t row_bytes, int64_t out_bytes) {
+  int64_t r = std::min(kOffLim / row_bytes - 256, kOffLim / out_bytes);
+  const Force f = forced();
+  if (f.chunk_rows > 0 && f.chunk_rows < r) r = std::max<int64_t>(f.chunk_rows, 256);
+  r = r / 256 * 256;
+  return r >= 256 ? r : 0;
 }
 
 int check_nk(int64_t N, int64_t K) {
@@ -81,7 +169,16 @@ int check_nk(int64_t N, int64_t K) {
   return DG_OK;
 }
 
-int check_operands(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, const uint16_t* D) {
+// One expert's weights (N rows of row_bytes, plus one tile of overhang) must
+// fit 32-bit offsets; the caller's activation scales too (rows x K/128 x 4 B).
+int check_weights_and_scales(int64_t N, int64_t row_bytes, int64_t rows, int64_t KB) {
+  if ((N + 256) * row_bytes >= kOffLim)
+    return fail(DG_ERR_SHAPE, "weights of %lld x %lld bytes per expert exceed 4 GiB", (long long)N, (long long)row_bytes);
+  if (rows * KB * 4 >= kOffLim) return fail(DG_ERR_SHAPE, "activation scales exceed 4 GiB");
+  return DG_OK;
+}
+
+int check_operands(const void* A, const void* sfa, const void* B, const void* sfb, const void* D) {
   if (!A || !sfa || !B || !sfb || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16))
     return fail(DG_ERR_ALIGN, "A, B and D must be 16-byte aligned");
@@ -89,10 +186,12 @@ int check_operands(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   return DG_OK;
 }
 
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int check_workspace(const void* ws, size_t bytes) {
+  if (ws && (!aligned(ws, 16) || bytes % 4))
+    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
+  return DG_OK;
+}
 
-// Dense split-K plan: enough work items to cover the CUs twice when the
-// output alone has too few tiles.  Splits never exceed the K blocks.
 // 256 x 256 tiles (gemm_wide.hip, no K split) stream a third fewer operand
 // bytes per flop than 256 x 128 ones; taken when they fill whole rounds of
 // the CUs to at least 85%.
@@ -111,43 +210,46 @@ bool kgrouped_wide(int64_t G, int64_t M, int64_t N, int cus) {
 }
 
 struct DensePlan {
-  bool persist;  // persistent kernel (gemm_persist.hip), M > 128
-  bool wide;     // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
-  int grid;      // persistent: workgroups
-  int dp_tiles, sk_tiles, sk_pieces, sk_kb;
-  bool lds;     // LDS-ring kernel (gemm_lds.hip)
-  bool skinny;  // skinny kernel (gemm_skinny.hip), M <= 128
-  int cfg;      // lds / v1 tile configuration, or skinny rows per tile (64 | 128)
-  int wn;       // skinny: columns per wave (16 | 32)
-  int m_tiles;
-  int n_tiles;
-  int splits;
-  int kb_per_split;
+  bool wide = false;    // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
+  bool persist = false; // persistent kernel (gemm_persist.hip): 256 x 128 tiles, K-split tail
+  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 128
+  int grid = 0;         // wide / persistent: workgroups
+  int dp_tiles = 0, sk_tiles = 0, sk_pieces = 1, sk_kb = 0;
+  int cfg = 0;          // skinny rows per tile (64 | 128)
+  int wn = 0;           // skinny: columns per wave (16 | 32)
+  int depth = 0;        // skinny: ring depth
+  int m_tiles = 0;
+  int n_tiles = 0;
+  int splits = 1;
+  int kb_per_split = 0;
 };
 
-// The LDS-ring kernel addresses operands with 32-bit buffer offsets.
-bool fits_32bit(int64_t rows, int64_t N, int64_t K) {
-  const int64_t lim = ((int64_t)1 << 32) - 1;
-  return (rows + 256) * K < lim && (N + 256) * K < lim && rows * (K / 128) * 4 < lim;
-}
-
-// The persistent kernel addresses A, B, alpha and D of all groups with 32-bit
-// buffer offsets and uses offsets from 0xFFFFFF00 up for lanes outside a tile.
-bool fits_persistent(int64_t groups, int64_t rows, int64_t N, int64_t K) {
-  const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
-  return groups * (rows + 256) * K < lim && groups * (N + 256) * K < lim &&
-         groups * (rows + 256) * (K / 128) * 4 < lim && groups * rows * N * 2 < lim;
+// Wide plan: every tile whole, one workgroup per CU (K = blocks of 128 bytes).
+void plan_wide(DensePlan& pl, int64_t M, int64_t N, int64_t kbytes, int cus) {
+  pl.wide = true;
+  pl.persist = true;
+  pl.m_tiles = (int)ceil_div(M, 256);
+  pl.n_tiles = (int)ceil_div(N, 256);
+  const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
+  pl.grid = (int)(tw < cus ? tw : cus);
+  pl.splits = 1;
+  pl.kb_per_split = (int)(kbytes / 128);
+  pl.dp_tiles = (int)tw;
+  pl.sk_tiles = 0;
+  pl.sk_pieces = 1;
+  pl.sk_kb = pl.kb_per_split;
 }
 
 // Persistent dense schedule over 256x128 tiles, one workgroup per CU: whole
 // rounds of tiles; a partial last round is split along K into P <= 4 pieces
 // run by the workgroups it would leave idle (when the workspace holds the
-// partials), so every workgroup ends at about the same time.
+// partials), so every workgroup ends at about the same time.  K counts
+// bytes per operand row (128 per block).
 void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   const int KB = (int)(K / 128);
   const int64_t T = ceil_div(M, 256) * ceil_div(N, 128);
+  pl.wide = false;
   pl.persist = true;
-  pl.cfg = dg::kLds256x128;
   pl.m_tiles = (int)ceil_div(M, 256);
   pl.n_tiles = (int)ceil_div(N, 128);
   pl.splits = 1;
@@ -166,7 +268,7 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
   const int kbs = (int)ceil_div(KB, P);
   P = (int)ceil_div(KB, kbs);  // every piece non-empty
   if (P < 2 || dg::persistent_workspace_bytes((int)rem, P) > ws_bytes ||
-      dg::persistent_workspace_bytes((int)rem, P) > (size_t)0xFFFFFF00 - 4096)
+      dg::persistent_workspace_bytes((int)rem, P) > (size_t)kOffLim)
     return;
   pl.dp_tiles = (int)(T - rem);
   pl.sk_tiles = (int)rem;
@@ -182,144 +284,197 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
 // is at most K / (20 bm) (the fp32 partials then stay below a fifth of the
 // weight bytes; more splits lose more in the fix-up than they gain), at most
 // 16, and only as large as the workspace holds.
-DensePlan plan_dense(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, bool allow_wide) {
-  DensePlan pl;
-  pl.persist = false;
-  pl.wide = false;
-  pl.grid = 0;
-  pl.dp_tiles = pl.sk_tiles = 0;
-  pl.sk_pieces = 1;
-  pl.sk_kb = 0;
-  pl.lds = false;
-  pl.skinny = false;
-  pl.wn = 0;
+void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   const int KB = (int)(K / 128);
-  if (M <= 128 && fits_32bit(M, N, K)) {
-    pl.skinny = true;
-    // 64 < M <= 128: one 128-row tile (weights read once) when the columns
-    // alone nearly fill the CUs; otherwise two 64-row tiles, whose split-K
-    // partials are half as large per tile
-    pl.cfg = (M <= 64 || ceil_div(N, 64) < cus / 2) ? 64 : 128;
-    pl.m_tiles = (int)ceil_div(M, pl.cfg);
-    const int64_t t16 = pl.m_tiles * ceil_div(N, 64);
-    const int64_t t32 = pl.m_tiles * ceil_div(N, 128);
-    auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
-    pl.wn = (t16 >= cus && fill(t32) >= fill(t16)) ? 32 : 16;
-    int cap_rows = pl.cfg;  // K split capped at K / (20 * cap_rows): partials (splits * bm * 4 B per column) <= K / 5
-    // 64 < M <= 128 with two 64-row tiles: each streams all of A beside its
-    // columns of B; one 128 x 128 tile halves those A reads, and wins where it
-    // still fills the CUs through a K split (partials then up to K / 2.5 per column)
-    if (M > 64 && pl.cfg == 64) {
-      const int64_t t128 = ceil_div(N, 128);
-      int64_t s128 = t128 < cus ? cus / t128 : 1;
-      if (s128 > K / 1280) s128 = K / 1280;
-      if (s128 > 16) s128 = 16;
-      if (s128 >= 2 && (double)(t128 * s128) >= 0.85 * cus &&
-          dg::skinny_workspace_bytes(128, 1, (int)t128, 32, (int)s128) <= ws_bytes) {
-        pl.cfg = 128;
-        pl.m_tiles = 1;
-        pl.wn = 32;
-        cap_rows = 64;
-      }
+  pl.skinny = true;
+  // 64 < M <= 128: one 128-row tile (weights read once) when the columns
+  // alone nearly fill the CUs; otherwise two 64-row tiles, whose split-K
+  // partials are half as large per tile
+  pl.cfg = (M <= 64 || ceil_div(N, 64) < cus / 2) ? 64 : 128;
+  pl.m_tiles = (int)ceil_div(M, pl.cfg);
+  const int64_t t16 = pl.m_tiles * ceil_div(N, 64);
+  const int64_t t32 = pl.m_tiles * ceil_div(N, 128);
+  auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
+  pl.wn = (t16 >= cus && fill(t32) >= fill(t16)) ? 32 : 16;
+  int cap_rows = pl.cfg;  // K split capped at K / (20 * cap_rows): partials (splits * bm * 4 B per column) <= K / 5
+  // 64 < M <= 128 with two 64-row tiles: each streams all of A beside its
+  // columns of B; one 128 x 128 tile halves those A reads, and wins where it
+  // still fills the CUs through a K split (partials then up to K / 2.5 per column)
+  if (M > 64 && pl.cfg == 64) {
+    const int64_t t128 = ceil_div(N, 128);
+    int64_t s128 = t128 < cus ? cus / t128 : 1;
+    if (s128 > K / 1280) s128 = K / 1280;
+    if (s128 > 16) s128 = 16;
+    if (s128 >= 2 && (double)(t128 * s128) >= 0.85 * cus &&
+        dg::skinny_workspace_bytes(128, 1, (int)t128, 32, (int)s128) <= ws_bytes) {
+      pl.cfg = 128;
+      pl.m_tiles = 1;
+      pl.wn = 32;
+      cap_rows = 64;
     }
-    pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
-    const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
-    int splits = 1;
-    if (tiles < cus) {
-      splits = (int)(cus / tiles);
-      const int cap = (int)(K / (20 * cap_rows));
-      if (splits > cap) splits = cap;
-      if (splits > 16) splits = 16;
-      while (splits > 1 && (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes ||
-                            dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) >
-                                ((size_t)1 << 31)))
-        --splits;
-      if (splits < 2) splits = 1;
-    }
-    // whole ring cycles per split where that does not cost a split
-    const int depth = dg::skinny_depth(pl.cfg, pl.wn);
-    int kbs = (int)ceil_div(KB, splits);
-    const int kbs_r = (int)ceil_div(kbs, depth) * depth;
-    if (ceil_div(KB, kbs_r) == splits || kbs_r - kbs < depth / 2) kbs = kbs_r;
-    pl.kb_per_split = kbs;
-    pl.splits = (int)ceil_div(KB, pl.kb_per_split);
-    return pl;
   }
-  if (M > 128 && fits_persistent(1, M, N, K)) {
-    const int64_t tw = ceil_div(M, 256) * ceil_div(N, 256);
-    if (allow_wide && wide_fill(M, N, cus)) {
-      pl.persist = true;
-      pl.wide = true;
-      pl.m_tiles = (int)ceil_div(M, 256);
-      pl.n_tiles = (int)ceil_div(N, 256);
-      pl.grid = (int)(tw < cus ? tw : cus);
-      pl.splits = 1;
-      pl.kb_per_split = KB;
-      pl.dp_tiles = (int)tw;
-      pl.sk_tiles = 0;
-      pl.sk_pieces = 1;
-      pl.sk_kb = KB;
-      return pl;
-    }
-    plan_persistent(pl, M, N, K, cus, ws_bytes);
-    return pl;
-  }
-  if (M > 128 && fits_32bit(M, N, K)) {
-    pl.lds = true;
-    pl.cfg = dg::kLds256x128;
-    pl.m_tiles = (int)ceil_div(M, 256);
-    pl.n_tiles = (int)ceil_div(N, 128);
-    pl.splits = 1;
-    pl.kb_per_split = (int)(K / 128);
-    return pl;
-  }
-  pl.cfg = M <= 128 ? dg::kTile64x64 : dg::kTile128x128;
-  const dg::TileShape ts = dg::tile_shape(pl.cfg);
-  pl.m_tiles = (int)ceil_div(M, ts.bm);
-  pl.n_tiles = (int)ceil_div(N, ts.bn);
+  pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
   const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
   int splits = 1;
   if (tiles < cus) {
-    splits = (int)ceil_div(2 * (int64_t)cus, tiles);
-    if (splits > KB) splits = KB;
+    splits = (int)(cus / tiles);
+    const int cap = (int)(K / (20 * cap_rows));
+    if (splits > cap) splits = cap;
     if (splits > 16) splits = 16;
-    const size_t per_split = (size_t)M * (size_t)N * sizeof(float);
-    const size_t fit = per_split ? ws_bytes / per_split : 0;
-    if ((size_t)splits > fit) splits = (int)fit;
+    while (splits > 1 && (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes ||
+                          dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) >
+                              ((size_t)1 << 31)))
+      --splits;
     if (splits < 2) splits = 1;
   }
-  pl.kb_per_split = (int)ceil_div(KB, splits);
+  const Force f = forced();
+  if (f.sk_bm) {  // DG_FORCE_CONFIG=skinny=...
+    pl.cfg = f.sk_bm;
+    pl.wn = f.sk_wn;
+    pl.m_tiles = (int)ceil_div(M, pl.cfg);
+    pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
+    splits = f.sk_splits < KB ? f.sk_splits : KB;
+    while (splits > 1 && dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes) --splits;
+  }
+  // whole ring cycles per split where that does not cost a split
+  const int depth = f.sk_bm ? f.sk_depth : dg::skinny_depth(pl.cfg, pl.wn);
+  pl.depth = depth;
+  int kbs = (int)ceil_div(KB, splits);
+  const int kbs_r = (int)ceil_div(kbs, depth) * depth;
+  if (ceil_div(KB, kbs_r) == splits || kbs_r - kbs < depth / 2) kbs = kbs_r;
+  pl.kb_per_split = kbs;
   pl.splits = (int)ceil_div(KB, pl.kb_per_split);
+}
+
+// The dense forms.  kFp8 / kAcc: skinny for M <= 128, else 256 x 256 tiles
+// where they fill whole rounds, else 256 x 128 tiles with a K-split tail.
+// kUe8m0 / kBf16: 256 x 256 tiles where they fill whole rounds, else
+// 256 x 128 tiles.  DG_FORCE_CONFIG=kernel=... overrides the wide / 256 x 128
+// choice for M > 128 (and for the UE8M0 / BF16 forms at any M >= 1).
+enum DenseKind { kFp8 = 0, kAcc = 1, kUe8m0 = 2, kBf16 = 3 };
+
+DensePlan plan_dense(DenseKind kind, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
+  DensePlan pl;
+  const int64_t kbytes = kind == kBf16 ? 2 * K : K;  // bytes per operand row
+  const Force f = forced();
+  if ((kind == kFp8 || kind == kAcc) && M <= 128) {
+    plan_skinny(pl, M, N, K, cus, ws_bytes);
+    return pl;
+  }
+  const bool wide = f.kernel == kForceWide ? true : f.kernel == kForcePersistent ? false : wide_fill(M, N, cus);
+  if (wide)
+    plan_wide(pl, M, N, kbytes, cus);
+  else
+    plan_persistent(pl, M, N, kbytes, cus, ws_bytes);
   return pl;
 }
 
-// Contiguous-form plan: the wide kernel (256 x 256 tiles) when K >= 4096,
-// its tiles fill whole rounds of the CUs to >= 85% and each workgroup's tiles
-// fit its pass table; else the persistent kernel over 128 x 256 tiles when
-// that fits.
-struct ContigPlan {
-  bool wide;
-  bool persist;
-  int grid;
-};
-ContigPlan plan_contiguous(int64_t M_total, int64_t N, int64_t K, int64_t G, int cus) {
-  ContigPlan cp{false, false, 0};
-  const bool fits = fits_persistent(1, M_total, N, K) && fits_persistent(G, 0, N, K);
-  const int64_t tw = ceil_div(M_total, 256) * ceil_div(N, 256);
-  const int64_t gw = tw < cus ? tw : cus;
-  // K >= 4096: with fewer K blocks per tile the second passes of tiles at
-  // expert boundaries and the per-tile overheads outweigh the wider tile
-  if (fits && M_total >= 256 && N >= 256 && K >= 4096 && ceil_div(tw, gw) <= dg::kWideMaxContigTiles &&
-      (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85) {
-    cp.wide = true;
-    cp.persist = true;
-    cp.grid = (int)gw;
-    return cp;
+const char* kind_name(DenseKind k) {
+  return k == kFp8 ? "gemm_nt" : k == kAcc ? "gemm_nt_acc" : k == kUe8m0 ? "gemm_nt_ue8m0" : "bf16_gemm_nt";
+}
+
+// Validation shared by the dense forms past their pointer checks, then one
+// launch per row chunk.
+int run_dense(DenseKind kind, const uint8_t* A, const void* sfa, const uint8_t* B, const void* sfb, const float* C,
+              void* D, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t kbytes = kind == kBf16 ? 2 * K : K;
+  const int64_t out_bytes = (kind == kAcc ? 4 : 2) * N;
+  int rc = check_weights_and_scales(N, kbytes, kind == kBf16 ? 0 : M, kind == kUe8m0 ? ceil_div(K / 128, 4) : K / 128);
+  if (rc) return rc;
+  const int64_t chunk = launch_rows(kbytes, out_bytes);
+  if (chunk == 0) return fail(DG_ERR_SHAPE, "rows of %lld bytes do not fit 32-bit offsets", (long long)kbytes);
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  const int ecus = effective_cus(cus);
+  const size_t ws = workspace ? workspace_bytes : 0;
+  for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+    const int64_t rows = std::min(chunk, M - r0);
+    const DensePlan pl = plan_dense(kind, rows, N, K, ecus, ws);
+    dg::GemmParams p{};
+    p.A = A + r0 * kbytes;
+    p.sfa = kind == kBf16 ? nullptr : static_cast<const float*>(sfa) + r0;  // [K/128][M]: a chunk starts r0 floats in
+    p.sfa_ld = (int)M;
+    p.B = B;
+    p.sfb = static_cast<const float*>(sfb);
+    if (kind == kAcc) {
+      p.Cacc = C ? C + r0 * N : nullptr;
+      p.Dacc = static_cast<float*>(D) + r0 * N;
+    } else {
+      p.D = static_cast<uint16_t*>(D) + r0 * N;
+    }
+    p.ws = static_cast<float*>(workspace);
+    p.index = nullptr;
+    p.rows = rows;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.G = 1;
+    p.m_tiles = pl.m_tiles;
+    p.n_tiles = pl.n_tiles;
+    p.splits = pl.splits;
+    p.kb_per_split = pl.kb_per_split;
+    p.dp_tiles = pl.dp_tiles;
+    p.sk_tiles = pl.sk_tiles;
+    p.sk_pieces = pl.sk_pieces;
+    p.sk_kb = pl.sk_kb;
+    if (print_configs()) {
+      if (pl.skinny)
+        std::fprintf(stderr,
+                     "[dg] %s M=%lld N=%lld K=%lld rows=%lld+%lld kernel=skinny tile=%dx%d m_tiles=%d n_tiles=%d splits=%d "
+                     "depth=%d\n",
+                     kind_name(kind), (long long)M, (long long)N, (long long)K, (long long)r0, (long long)rows, pl.cfg,
+                     4 * pl.wn, pl.m_tiles, pl.n_tiles, pl.splits, pl.depth);
+      else
+        std::fprintf(stderr,
+                     "[dg] %s M=%lld N=%lld K=%lld rows=%lld+%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
+                     kind_name(kind), (long long)M, (long long)N, (long long)K, (long long)r0, (long long)rows,
+                     pl.wide ? "wide" : "persistent", pl.grid, pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles,
+                     pl.sk_pieces, pl.sk_kb);
+    }
+    const int mode = kind == kFp8 ? dg::kDense : kind == kAcc ? dg::kDenseAcc : kind == kUe8m0 ? dg::kDenseUe8m0
+                                                                                                 : dg::kDenseBf16;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = pl.skinny ? dg::launch_gemm_skinny(pl.cfg, pl.wn, pl.depth, p, st)
+                         : pl.wide ? dg::launch_gemm_wide(mode, pl.grid, p, st)
+                                   : dg::launch_gemm_persistent(mode, pl.grid, p, st);
+    if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   }
-  const int64_t ptiles = ceil_div(M_total, 128) * ceil_div(N, 256);
-  const int pgrid = (int)(ptiles < cus ? ptiles : cus);
-  cp.persist = fits && ceil_div(ptiles, pgrid) <= dg::kPersistentMaxContigTiles;
-  cp.grid = pgrid;
+  return ok();
+}
+
+int check_rows(int64_t M, const char* name) {
+  if (M < 0) return fail(DG_ERR_SHAPE, "%s must be >= 0 (got %lld)", name, (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "%s too large", name);
+  return DG_OK;
+}
+
+// Contiguous-form plan for one launch of `rows` rows: the wide kernel
+// (256 x 256 tiles, passes at expert boundaries) when K >= 4096 and its
+// tiles fill whole rounds of the CUs to >= 85%; else the persistent kernel
+// over 128 x 256 tiles.  Each workgroup lists its tiles in an LDS table of
+// 64 entries, so the grid grows past the CU count when a launch has more
+// than 64 tiles per CU.
+struct ContigPlan {
+  bool wide = false;
+  int grid = 0;
+  int64_t tiles = 0;
+};
+ContigPlan plan_contiguous(int64_t rows, int64_t N, int64_t K, int cus) {
+  ContigPlan cp;
+  const Force f = forced();
+  const int64_t tw = ceil_div(rows, 256) * ceil_div(N, 256);
+  const bool wide_ok = rows >= 256 && N >= 256;
+  const bool wide = f.kernel == kForceWide ? wide_ok
+                    : f.kernel == kForcePersistent
+                        ? false
+                        // K >= 4096: with fewer K blocks per tile the second passes of tiles at
+                        // expert boundaries and the per-tile overheads outweigh the wider tile
+                        : wide_ok && K >= 4096 && (double)tw / (double)(ceil_div(tw, cus) * cus) >= 0.85;
+  const int64_t tiles = wide ? tw : ceil_div(rows, 128) * ceil_div(N, 256);
+  const int64_t maxt = wide ? dg::kWideMaxContigTiles : dg::kPersistentMaxContigTiles;
+  const int64_t g = std::max<int64_t>(cus, ceil_div(tiles, maxt));
+  cp.wide = wide;
+  cp.tiles = tiles;
+  cp.grid = (int)std::min(tiles, g);
   return cp;
 }
 
@@ -331,59 +486,11 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
                    int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_nk(N, K);
   if (rc) return rc;
-  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
-  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if ((rc = check_rows(M, "M"))) return rc;
   if (M == 0) return ok();
   if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
-  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
-    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
-  int cus = 0;
-  if ((rc = check_device(&cus))) return rc;
-  const DensePlan pl = plan_dense(M, N, K, effective_cus(cus), workspace ? workspace_bytes : 0, true);
-  dg::GemmParams p{};
-  p.A = A;
-  p.sfa = sfa;
-  p.B = B;
-  p.sfb = sfb;
-  p.D = D;
-  p.ws = static_cast<float*>(workspace);
-  p.index = nullptr;
-  p.rows = M;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.G = 1;
-  p.m_tiles = pl.m_tiles;
-  p.n_tiles = pl.n_tiles;
-  p.splits = pl.splits;
-  p.kb_per_split = pl.kb_per_split;
-  p.dp_tiles = pl.dp_tiles;
-  p.sk_tiles = pl.sk_tiles;
-  p.sk_pieces = pl.sk_pieces;
-  p.sk_kb = pl.sk_kb;
-  if (std::getenv("DG_PRINT_CONFIGS") && pl.persist)
-    std::fprintf(stderr,
-                 "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
-                 (long long)M, (long long)N, (long long)K, pl.wide ? "wide" : "persistent", pl.grid,
-                 pl.m_tiles * pl.n_tiles, pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, pl.sk_kb);
-  else if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] gemm_nt M=%lld N=%lld K=%lld kernel=%s tile=%dx%d m_tiles=%d n_tiles=%d splits=%d\n",
-                 (long long)M, (long long)N, (long long)K, pl.skinny ? "skinny" : (pl.lds ? "lds" : "v1"),
-                 pl.skinny ? pl.cfg : (pl.lds ? dg::lds_tile_shape(pl.cfg).bm : dg::tile_shape(pl.cfg).bm),
-                 pl.skinny ? 4 * pl.wn : (pl.lds ? dg::lds_tile_shape(pl.cfg).bn : dg::tile_shape(pl.cfg).bn),
-                 pl.m_tiles, pl.n_tiles, pl.splits);
-  hipError_t e;
-  if (pl.wide)
-    e = dg::launch_gemm_wide(dg::kDense, pl.grid, p, static_cast<hipStream_t>(stream));
-  else if (pl.persist)
-    e = dg::launch_gemm_persistent(dg::kDense, pl.grid, p, static_cast<hipStream_t>(stream));
-  else if (pl.skinny)
-    e = dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream));
-  else if (pl.lds)
-    e = dg::launch_gemm_lds(dg::kDense, pl.cfg, p, static_cast<hipStream_t>(stream));
-  else
-    e = dg::launch_gemm(dg::kDense, pl.cfg, p, 1, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return ok();
+  if ((rc = check_workspace(workspace, workspace_bytes))) return rc;
+  return run_dense(kFp8, A, sfa, B, sfb, nullptr, D, M, N, K, workspace, workspace_bytes, stream);
 }
 
 int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, const float* C,
@@ -391,122 +498,39 @@ int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, con
                        void* stream) {
   int rc = check_nk(N, K);
   if (rc) return rc;
-  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
-  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if ((rc = check_rows(M, "M"))) return rc;
   if (M == 0) return ok();
-  if (!A || !sfa || !B || !sfb || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
-    return fail(DG_ERR_ALIGN, "A, B, C and D must be 16-byte aligned");
-  if (!aligned(sfa, 4) || !aligned(sfb, 4)) return fail(DG_ERR_ALIGN, "scale arrays must be 4-byte aligned");
-  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
-    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
-  int cus = 0;
-  if ((rc = check_device(&cus))) return rc;
-  const int ecus = effective_cus(cus);
-  DensePlan pl = plan_dense(M, N, K, ecus, workspace ? workspace_bytes : 0, false);
-  if (!pl.persist && !pl.skinny) return fail(DG_ERR_SHAPE, "problem too large for the accumulating form");
-  if (pl.persist && M * N * 4 >= (int64_t)0xFFFFFF00 - 4096)
-    return fail(DG_ERR_SHAPE, "fp32 output too large for 32-bit buffer offsets");
-  const bool wide = pl.persist && wide_fill(M, N, ecus);  // 256 x 256 tiles, no K split
-  if (wide) {
-    pl.m_tiles = (int)ceil_div(M, 256);
-    pl.n_tiles = (int)ceil_div(N, 256);
-    const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
-    pl.grid = (int)(tw < ecus ? tw : ecus);
-    pl.dp_tiles = (int)tw;
-    pl.sk_tiles = 0;
-    pl.sk_pieces = 1;
-    pl.sk_kb = (int)(K / 128);
-  }
-  dg::GemmParams p{};
-  p.A = A;
-  p.sfa = sfa;
-  p.B = B;
-  p.sfb = sfb;
-  p.Cacc = C;
-  p.Dacc = D;
-  p.ws = static_cast<float*>(workspace);
-  p.rows = M;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.G = 1;
-  p.m_tiles = pl.m_tiles;
-  p.n_tiles = pl.n_tiles;
-  p.splits = pl.splits;
-  p.kb_per_split = pl.kb_per_split;
-  p.dp_tiles = pl.dp_tiles;
-  p.sk_tiles = pl.sk_tiles;
-  p.sk_pieces = pl.sk_pieces;
-  p.sk_kb = pl.sk_kb;
-  if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] gemm_nt_acc M=%lld N=%lld K=%lld kernel=%s\n", (long long)M, (long long)N, (long long)K,
-                 wide ? "wide" : (pl.persist ? "persistent" : "skinny"));
-  const hipError_t e =
-      wide ? dg::launch_gemm_wide(dg::kDenseAcc, pl.grid, p, static_cast<hipStream_t>(stream))
-           : (pl.persist ? dg::launch_gemm_persistent(dg::kDenseAcc, pl.grid, p, static_cast<hipStream_t>(stream))
-                         : dg::launch_gemm_skinny(pl.cfg, pl.wn, p, static_cast<hipStream_t>(stream)));
-  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if (C && !aligned(C, 16)) return fail(DG_ERR_ALIGN, "A, B, C and D must be 16-byte aligned");
+  if ((rc = check_workspace(workspace, workspace_bytes))) return rc;
+  return run_dense(kAcc, A, sfa, B, sfb, C, D, M, N, K, workspace, workspace_bytes, stream);
 }
 
 int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B, const int32_t* sfb, uint16_t* D,
                          int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_nk(N, K);
   if (rc) return rc;
-  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
-  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if ((rc = check_rows(M, "M"))) return rc;
   if (M == 0) return ok();
-  if ((rc = check_operands(A, reinterpret_cast<const float*>(sfa), B, reinterpret_cast<const float*>(sfb), D)))
-    return rc;
-  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
-    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
-  if (!fits_persistent(1, M, N, K)) return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
-  int cus = 0;
-  if ((rc = check_device(&cus))) return rc;
-  DensePlan pl;
-  const int ecus = effective_cus(cus);
-  const bool wide = wide_fill(M, N, ecus);
-  if (wide) {
-    pl.m_tiles = (int)ceil_div(M, 256);
-    pl.n_tiles = (int)ceil_div(N, 256);
-    const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
-    pl.grid = (int)(tw < ecus ? tw : ecus);
-    pl.kb_per_split = (int)(K / 128);
-    pl.dp_tiles = (int)tw;
-    pl.sk_tiles = 0;
-    pl.sk_pieces = 1;
-    pl.sk_kb = (int)(K / 128);
-  } else {
-    plan_persistent(pl, M, N, K, ecus, workspace ? workspace_bytes : 0);
-  }
-  dg::GemmParams p{};
-  p.A = A;
-  p.sfa = reinterpret_cast<const float*>(sfa);  // packed UE8M0 words, read as such by the kernel
-  p.B = B;
-  p.sfb = reinterpret_cast<const float*>(sfb);
-  p.D = D;
-  p.ws = static_cast<float*>(workspace);
-  p.rows = M;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.G = 1;
-  p.m_tiles = pl.m_tiles;
-  p.n_tiles = pl.n_tiles;
-  p.splits = 1;
-  p.kb_per_split = pl.kb_per_split;
-  p.dp_tiles = pl.dp_tiles;
-  p.sk_tiles = pl.sk_tiles;
-  p.sk_pieces = pl.sk_pieces;
-  p.sk_kb = pl.sk_kb;
-  if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr,
-                 "[dg] gemm_nt_ue8m0 M=%lld N=%lld K=%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
-                 (long long)M, (long long)N, (long long)K, wide ? "wide" : "persistent", pl.grid, pl.m_tiles * pl.n_tiles,
-                 pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, pl.sk_kb);
-  const hipError_t e = wide ? dg::launch_gemm_wide(dg::kDenseUe8m0, pl.grid, p, static_cast<hipStream_t>(stream))
-                            : dg::launch_gemm_persistent(dg::kDenseUe8m0, pl.grid, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if ((rc = check_workspace(workspace, workspace_bytes))) return rc;
+  return run_dense(kUe8m0, A, sfa, B, sfb, nullptr, D, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (K <= 0 || K % 64 != 0) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 64 (got %lld)", (long long)K);
+  if (N <= 0 || N % 16 != 0) return fail(DG_ERR_SHAPE, "N must be a positive multiple of 16 (got %lld)", (long long)N);
+  if (K > (int64_t)1 << 29 || N > (int64_t)1 << 30) return fail(DG_ERR_SHAPE, "N or K too large");
+  int rc = check_rows(M, "M");
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if (!A || !B || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16))
+    return fail(DG_ERR_ALIGN, "A, B and D must be 16-byte aligned");
+  if ((rc = check_workspace(workspace, workspace_bytes))) return rc;
+  return run_dense(kBf16, reinterpret_cast<const uint8_t*>(A), nullptr, reinterpret_cast<const uint8_t*>(B), nullptr,
+                   nullptr, D, M, N, K, workspace, workspace_bytes, stream);
 }
 
 int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
@@ -517,24 +541,25 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   (void)workspace_bytes;
   int rc = check_nk(N, K);
   if (rc) return rc;
-  if (G < 1 || G > 1024) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
-  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
-  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
+  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
+  if ((rc = check_rows(M, "M"))) return rc;
   if (M == 0) return ok();
   if (!A || !sfa || !B || !sfb || !D || !ks) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || (C && !aligned(C, 16)))
     return fail(DG_ERR_ALIGN, "A, B, C and D must be 16-byte aligned");
   if (!aligned(sfa, 4) || !aligned(sfb, 4) || !aligned(ks, 4))
     return fail(DG_ERR_ALIGN, "scale arrays and ks must be 4-byte aligned");
-  // one 256 x 128 tile grid per group over the shared operands; fp32 C and D
-  // are addressed per group
-  if (!fits_persistent(1, M, N, K) || (M + 256) * N * 4 >= (int64_t)0xFFFFFF00 - 4096)
+  // one tile grid per group over the shared operands, addressed with 32-bit
+  // offsets; fp32 C and D are addressed per group
+  if ((M + 256) * K >= kOffLim || (N + 256) * K >= kOffLim || (M + 256) * N * 4 >= kOffLim ||
+      std::max(M, N) * (K / 128) * 4 >= kOffLim)
     return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
+  p.sfa_ld = (int)M;
   p.B = B;
   p.sfb = sfb;
   p.Cacc = C;
@@ -545,7 +570,10 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   p.K = (int)K;
   p.G = (int)G;
   const int ecus = effective_cus(cus);
-  const bool wide = kgrouped_wide(G, M, N, ecus);
+  const Force f = forced();
+  const bool wide = f.kernel == kForceWide         ? (M >= 256 && N >= 256)
+                    : f.kernel == kForcePersistent ? false
+                                                   : kgrouped_wide(G, M, N, ecus);
   p.m_tiles = (int)ceil_div(M, 256);
   p.n_tiles = (int)ceil_div(N, wide ? 256 : 128);
   p.splits = 1;
@@ -557,73 +585,11 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   const int64_t tiles = G * p.m_tiles * p.n_tiles;
   if (tiles > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "too many tiles");
   const int grid = (int)(tiles < ecus ? tiles : ecus);
-  if (std::getenv("DG_PRINT_CONFIGS"))
+  if (print_configs())
     std::fprintf(stderr, "[dg] k_grouped G=%lld M=%lld N=%lld K=%lld kernel=%s tiles=%lld grid=%d\n", (long long)G,
                  (long long)M, (long long)N, (long long)K, wide ? "wide" : "persistent", (long long)tiles, grid);
   const hipError_t e = wide ? dg::launch_gemm_wide(dg::kKGrouped, grid, p, static_cast<hipStream_t>(stream))
                             : dg::launch_gemm_persistent(dg::kKGrouped, grid, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
-
-int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M, int64_t N, int64_t K,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (K <= 0 || K % 64 != 0) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 64 (got %lld)", (long long)K);
-  if (N <= 0 || N % 16 != 0) return fail(DG_ERR_SHAPE, "N must be a positive multiple of 16 (got %lld)", (long long)N);
-  if (K > (int64_t)1 << 29 || N > (int64_t)1 << 30) return fail(DG_ERR_SHAPE, "N or K too large");
-  if (M < 0) return fail(DG_ERR_SHAPE, "M must be >= 0 (got %lld)", (long long)M);
-  if (M > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M too large");
-  if (M == 0) return ok();
-  if (!A || !B || !D) return fail(DG_ERR_INVALID_ARG, "null operand pointer");
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16))
-    return fail(DG_ERR_ALIGN, "A, B and D must be 16-byte aligned");
-  if (workspace && (!aligned(workspace, 16) || workspace_bytes % 4))
-    return fail(DG_ERR_WORKSPACE, "workspace must be 16-byte aligned with a size that is a multiple of 4");
-  int rc = 0;
-  int cus = 0;
-  if ((rc = check_device(&cus))) return rc;
-  // the persistent kernels' schedule over K blocks of 128 bytes (64 bf16)
-  if (!fits_persistent(1, M, N, 2 * K)) return fail(DG_ERR_SHAPE, "problem too large for 32-bit buffer offsets");
-  DensePlan pl;
-  const int ecus = effective_cus(cus);
-  const bool wide = wide_fill(M, N, ecus);
-  if (wide) {
-    pl.m_tiles = (int)ceil_div(M, 256);
-    pl.n_tiles = (int)ceil_div(N, 256);
-    const int64_t tw = (int64_t)pl.m_tiles * pl.n_tiles;
-    pl.grid = (int)(tw < ecus ? tw : ecus);
-    pl.kb_per_split = (int)(2 * K / 128);
-    pl.dp_tiles = (int)tw;
-    pl.sk_tiles = 0;
-    pl.sk_pieces = 1;
-    pl.sk_kb = pl.kb_per_split;
-  } else {
-    plan_persistent(pl, M, N, 2 * K, ecus, workspace ? workspace_bytes : 0);
-  }
-  dg::GemmParams p{};
-  p.A = reinterpret_cast<const uint8_t*>(A);
-  p.B = reinterpret_cast<const uint8_t*>(B);
-  p.D = D;
-  p.ws = static_cast<float*>(workspace);
-  p.rows = M;
-  p.N = (int)N;
-  p.K = (int)K;  // elements; the kernel addresses rows of 2 K bytes
-  p.G = 1;
-  p.m_tiles = pl.m_tiles;
-  p.n_tiles = pl.n_tiles;
-  p.splits = 1;
-  p.kb_per_split = pl.kb_per_split;
-  p.dp_tiles = pl.dp_tiles;
-  p.sk_tiles = pl.sk_tiles;
-  p.sk_pieces = pl.sk_pieces;
-  p.sk_kb = pl.sk_kb;
-  if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr,
-                 "[dg] bf16_gemm_nt M=%lld N=%lld K=%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
-                 (long long)M, (long long)N, (long long)K, wide ? "wide" : "persistent", pl.grid, pl.m_tiles * pl.n_tiles,
-                 pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, pl.sk_kb);
-  const hipError_t e = wide ? dg::launch_gemm_wide(dg::kDenseBf16, pl.grid, p, static_cast<hipStream_t>(stream))
-                            : dg::launch_gemm_persistent(dg::kDenseBf16, pl.grid, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -636,64 +602,52 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   (void)workspace_bytes;
   int rc = check_nk(N, K);
   if (rc) return rc;
-  if (M_total < 0) return fail(DG_ERR_SHAPE, "M_total must be >= 0");
-  if (M_total > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "M_total too large");
-  if (G < 1 || G > 65536) return fail(DG_ERR_SHAPE, "G must be in [1, 65536] (got %lld)", (long long)G);
+  if ((rc = check_rows(M_total, "M_total"))) return rc;
+  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
   if (M_total == 0) return ok();
   if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
   if (!m_indices) return fail(DG_ERR_INVALID_ARG, "null m_indices");
   if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
+  if ((rc = check_weights_and_scales(N, K, M_total, K / 128))) return rc;
+  // row chunks are multiples of 256 rows, so every aligned 128-row block
+  // stays inside one chunk
+  const int64_t chunk = launch_rows(K, 2 * N);
+  if (chunk == 0) return fail(DG_ERR_SHAPE, "rows do not fit 32-bit offsets");
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  // 256 x 256 tiles (wide kernel, two passes where a tile straddles two
-  // experts) when they fill whole rounds of the CUs to >= 85%; otherwise
-  // 128 x 256 tiles, each inside one 128-row aligned expert segment.  Both
-  // need their 32-bit offsets to fit and each workgroup's tiles to fit its
-  // table.
   const int ecus = effective_cus(cus);
-  const ContigPlan cp = plan_contiguous(M_total, N, K, G, ecus);
-  const int64_t ptiles = ceil_div(M_total, 128) * ceil_div(N, 256);
-  const int pgrid = (int)(ptiles < ecus ? ptiles : ecus);
-  const bool persist = cp.persist;
-  const bool lds = persist || fits_32bit(M_total, N, K);
-  const int bm = 128;
-  const int bn = lds ? 256 : 128;
-  dg::GemmParams p{};
-  p.A = A;
-  p.sfa = sfa;
-  p.B = B;
-  p.sfb = sfb;
-  p.D = D;
-  p.index = m_indices;
-  p.rows = M_total;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.G = (int)G;
-  p.m_tiles = (int)ceil_div(M_total, bm);
-  p.n_tiles = (int)ceil_div(N, bn);
-  p.splits = 1;
-  p.kb_per_split = (int)(K / 128);
-  if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld tile=%dx%d kernel=%s\n", (long long)M_total,
-                 (long long)N, (long long)K, (long long)G, cp.wide ? 256 : bm, bn,
-                 cp.wide ? "wide" : (persist ? "persistent" : "grid"));
-  hipError_t e;
-  if (cp.wide) {
-    p.m_tiles = (int)ceil_div(M_total, 256);
+  for (int64_t r0 = 0; r0 < M_total; r0 += chunk) {
+    const int64_t rows = std::min(chunk, M_total - r0);
+    const ContigPlan cp = plan_contiguous(rows, N, K, ecus);
+    dg::GemmParams p{};
+    p.A = A + r0 * K;
+    p.sfa = sfa + r0;
+    p.sfa_ld = (int)M_total;
+    p.B = B;
+    p.sfb = sfb;
+    p.D = D + r0 * N;
+    p.index = m_indices + r0;
+    p.rows = rows;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.G = (int)G;
+    p.m_tiles = (int)ceil_div(rows, cp.wide ? 256 : 128);
     p.n_tiles = (int)ceil_div(N, 256);
-    e = dg::launch_gemm_wide(dg::kContiguous, cp.grid, p, static_cast<hipStream_t>(stream));
-  } else if (persist) {
-    p.dp_tiles = (int)ptiles;  // every tile whole: no K-split tail, no workspace
+    p.splits = 1;
+    p.kb_per_split = (int)(K / 128);
+    p.dp_tiles = (int)cp.tiles;  // every tile whole: no K-split tail, no workspace
     p.sk_tiles = 0;
     p.sk_pieces = 1;
     p.sk_kb = (int)(K / 128);
-    e = dg::launch_gemm_persistent(dg::kContiguous, pgrid, p, static_cast<hipStream_t>(stream));
-  } else if (lds) {
-    e = dg::launch_gemm_lds(dg::kContiguous, dg::kLds128x256, p, static_cast<hipStream_t>(stream));
-  } else {
-    e = dg::launch_gemm(dg::kContiguous, dg::kTile128x128, p, 1, static_cast<hipStream_t>(stream));
+    if (print_configs())
+      std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld rows=%lld+%lld tile=%dx256 kernel=%s grid=%d\n",
+                   (long long)M_total, (long long)N, (long long)K, (long long)G, (long long)r0, (long long)rows,
+                   cp.wide ? 256 : 128, cp.wide ? "wide" : "persistent", cp.grid);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = cp.wide ? dg::launch_gemm_wide(dg::kContiguous, cp.grid, p, st)
+                                 : dg::launch_gemm_persistent(dg::kContiguous, cp.grid, p, st);
+    if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   }
-  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -703,26 +657,26 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
                                     void* stream) {
   (void)workspace;
   (void)workspace_bytes;
+  (void)expected_m;  // launch shape and results never depend on it
   int rc = check_nk(N, K);
   if (rc) return rc;
-  if (G < 1 || G > 65536) return fail(DG_ERR_SHAPE, "G must be in [1, 65536] (got %lld)", (long long)G);
+  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
   if (max_m < 0) return fail(DG_ERR_SHAPE, "max_m must be >= 0");
-  if (G * max_m > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "G * max_m too large");
+  if (max_m > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "max_m too large");
   if (max_m == 0) return ok();
   if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
   if (!masked_m) return fail(DG_ERR_INVALID_ARG, "null masked_m");
   if (!aligned(masked_m, 4)) return fail(DG_ERR_ALIGN, "masked_m must be 4-byte aligned");
+  // each expert's A, alpha, B and D are addressed from the expert's own base
+  if ((rc = check_weights_and_scales(N, K, max_m, K / 128))) return rc;
+  if ((max_m + 256) * K >= kOffLim || max_m * N * 2 >= kOffLim)
+    return fail(DG_ERR_SHAPE, "one expert's rows exceed 32-bit offsets (max_m = %lld)", (long long)max_m);
   int cus = 0;
   if ((rc = check_device(&cus))) return rc;
-  (void)expected_m;
-  // persistent kernel with a device-side task list over the active tiles
-  const bool persist = G <= 1024 && fits_persistent(G, max_m, N, K);
-  const bool lds = persist || fits_32bit(max_m, N, K);
-  const int cfg = lds ? (int)dg::kLds256x128 : (max_m <= 64 ? dg::kTile64x128 : dg::kTile128x128);
-  const dg::TileShape ts = lds ? dg::lds_tile_shape(cfg) : dg::tile_shape(cfg);
   dg::GemmParams p{};
   p.A = A;
   p.sfa = sfa;
+  p.sfa_ld = (int)max_m;
   p.B = B;
   p.sfb = sfb;
   p.D = D;
@@ -731,26 +685,18 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   p.N = (int)N;
   p.K = (int)K;
   p.G = (int)G;
-  // the persistent kernel runs 128 x 256 tiles
-  p.m_tiles = (int)ceil_div(max_m, persist ? 128 : ts.bm);
-  p.n_tiles = (int)ceil_div(N, persist ? 256 : ts.bn);
+  // 128 x 256 tiles over a device-side task list
+  p.m_tiles = (int)ceil_div(max_m, 128);
+  p.n_tiles = (int)ceil_div(N, 256);
   p.splits = 1;
   p.kb_per_split = (int)(K / 128);
-  if (std::getenv("DG_PRINT_CONFIGS"))
-    std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=%dx%d kernel=%s\n", (long long)G,
-                 (long long)max_m, (long long)N, (long long)K, persist ? 128 : ts.bm, persist ? 256 : ts.bn,
-                 persist ? "persistent" : "grid");
-  hipError_t e;
-  if (persist) {
-    const int64_t tiles = G * p.m_tiles * p.n_tiles;
-    const int ecus = effective_cus(cus);
-    e = dg::launch_gemm_persistent(dg::kMasked, (int)(tiles < ecus ? tiles : ecus), p,
-                                   static_cast<hipStream_t>(stream));
-  } else if (lds) {
-    e = dg::launch_gemm_lds(dg::kMasked, cfg, p, static_cast<hipStream_t>(stream));
-  } else {
-    e = dg::launch_gemm(dg::kMasked, cfg, p, (int)G, static_cast<hipStream_t>(stream));
-  }
+  const int64_t tiles = G * p.m_tiles * p.n_tiles;
+  const int ecus = effective_cus(cus);
+  const int grid = (int)(tiles < ecus ? tiles : ecus);
+  if (print_configs())
+    std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=128x256 kernel=persistent grid=%d\n",
+                 (long long)G, (long long)max_m, (long long)N, (long long)K, grid);
+  const hipError_t e = dg::launch_gemm_persistent(dg::kMasked, grid, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -827,96 +773,71 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
   (void)G;
   if (op != DG_OP_GEMM_NT && op != DG_OP_BF16_GEMM_NT && op != DG_OP_GEMM_NT_UE8M0) return 0;
   if (rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128)) return 0;
-  int cus = 0;
-  int dev = -1;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+  const int ecus = effective_cus(query_cus());
+  const int64_t kbytes = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;
+  // the largest row chunk's plan; chunks reuse the workspace one after another
+  const int64_t chunk = launch_rows(kbytes, 2 * N);
+  if (chunk == 0) return 0;
+  const int64_t r = std::min(rows, chunk);
+  const DenseKind kind = op == DG_OP_BF16_GEMM_NT ? kBf16 : op == DG_OP_GEMM_NT_UE8M0 ? kUe8m0 : kFp8;
+  size_t need = 0;
+  // the fp8 forms: the accumulating one shares this workspace and plans the same
+  // way, except that it has 256 x 128 tiles where the bf16-output form has 256 x 256
+  const DenseKind kinds[2] = {kind, kAcc};
+  for (int i = 0; i < (kind == kFp8 ? 2 : 1); ++i) {
+    const DensePlan pl = plan_dense(kinds[i], r, N, K, ecus, (size_t)-1);
+    size_t b = 0;
+    if (pl.skinny && pl.splits > 1) b = dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, pl.splits);
+    if (pl.persist && !pl.wide) b = dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces);
+    need = std::max(need, b);
   }
-  (void)hipGetLastError();
-  if (cus <= 0) cus = 256;
-  if ((op == DG_OP_GEMM_NT_UE8M0 || op == DG_OP_BF16_GEMM_NT) && wide_fill(rows, N, effective_cus(cus)))
-    return 0;  // 256 x 256 tiles, no split
-  if (op == DG_OP_BF16_GEMM_NT || op == DG_OP_GEMM_NT_UE8M0) {
-    const int64_t kb = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;  // bytes per operand row
-    if (!fits_persistent(1, rows, N, kb)) return 0;
-    DensePlan pb;
-    plan_persistent(pb, rows, N, kb, effective_cus(cus), (size_t)-1);
-    return (dg::persistent_workspace_bytes(pb.sk_tiles, pb.sk_pieces) + 15) / 16 * 16;
-  }
-  // sized for the 256 x 128 plan, which the accumulating form also uses where
-  // 256 x 256 tiles do not apply (those need no workspace; a larger one is unused)
-  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, false);
-  if (pl.persist) return (dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces) + 15) / 16 * 16;
-  if (pl.splits <= 1) return 0;
-  if (pl.skinny)
-    return (dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, pl.splits) + 15) / 16 * 16;
-  return (size_t)pl.splits * (size_t)rows * (size_t)N * sizeof(float);
+  return (need + 15) / 16 * 16;
 }
 
 const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G) {
-  (void)G;
   thread_local std::string text;
   text.clear();
   if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0 && op != DG_OP_BF16_GEMM_NT &&
        op != DG_OP_K_GROUPED) ||
       rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128) || N % 16)
     return text.c_str();
-  int cus = 0;
-  int dev = -1;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
-  }
-  (void)hipGetLastError();
-  if (cus <= 0) cus = 256;
-  char buf[256];
+  const int ecus = effective_cus(query_cus());
+  char buf[320];
   if (op == DG_OP_CONTIGUOUS) {
-    const ContigPlan cp = plan_contiguous(rows, N, K, G < 1 ? 1 : G, effective_cus(cus));
-    std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx256 grid=%d", cp.wide ? "wide" : (cp.persist ? "persistent" : "grid"),
-                  cp.wide ? 256 : 128, cp.grid);
+    const int64_t chunk = launch_rows(K, 2 * N);
+    if (chunk == 0) return text.c_str();
+    const int64_t r = std::min(rows, chunk);
+    const ContigPlan cp = plan_contiguous(r, N, K, ecus);
+    std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx256 grid=%d tiles=%lld chunks=%lld", cp.wide ? "wide" : "persistent",
+                  cp.wide ? 256 : 128, cp.grid, (long long)cp.tiles, (long long)ceil_div(rows, chunk));
     text = buf;
     return text.c_str();
   }
   if (op == DG_OP_K_GROUPED) {
     const int64_t g = G < 1 ? 1 : G;
-    const int ecus = effective_cus(cus);
-    const bool wide = kgrouped_wide(g, rows, N, ecus);
+    const Force f = forced();
+    const bool wide = f.kernel == kForceWide         ? (rows >= 256 && N >= 256)
+                      : f.kernel == kForcePersistent ? false
+                                                     : kgrouped_wide(g, rows, N, ecus);
     const int64_t tiles = g * ceil_div(rows, 256) * ceil_div(N, wide ? 256 : 128);
     std::snprintf(buf, sizeof(buf), "kernel=%s tile=256x%d grid=%lld tiles=%lld", wide ? "wide" : "persistent",
                   wide ? 256 : 128, (long long)(tiles < ecus ? tiles : ecus), (long long)tiles);
     text = buf;
     return text.c_str();
   }
-  if (op == DG_OP_GEMM_NT_UE8M0 || op == DG_OP_BF16_GEMM_NT) {
-    const int ecus = effective_cus(cus);
-    const int64_t kbytes = op == DG_OP_BF16_GEMM_NT ? 2 * K : K;  // bytes per operand row
-    if (wide_fill(rows, N, ecus)) {
-      const int64_t tw = ceil_div(rows, 256) * ceil_div(N, 256);
-      std::snprintf(buf, sizeof(buf), "kernel=wide tile=256x256 grid=%d tiles=%d whole=%d tail=0x1",
-                    (int)(tw < ecus ? tw : ecus), (int)tw, (int)tw);
-    } else if (fits_persistent(1, rows, N, kbytes)) {
-      DensePlan pb;
-      plan_persistent(pb, rows, N, kbytes, ecus, (size_t)-1);
-      std::snprintf(buf, sizeof(buf), "kernel=persistent tile=256x128 grid=%d tiles=%d whole=%d tail=%dx%d", pb.grid,
-                    pb.m_tiles * pb.n_tiles, pb.dp_tiles, pb.sk_tiles, pb.sk_pieces);
-    } else {
-      buf[0] = 0;
-    }
-    text = buf;
-    return text.c_str();
-  }
-  const DensePlan pl = plan_dense(rows, N, K, effective_cus(cus), (size_t)-1, true);
-  if (pl.wide || pl.persist)
-    std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx%d grid=%d tiles=%d whole=%d tail=%dx%d",
-                  pl.wide ? "wide" : "persistent", 256, pl.wide ? 256 : 128, pl.grid, pl.m_tiles * pl.n_tiles,
-                  pl.dp_tiles, pl.sk_tiles, pl.sk_pieces);
-  else if (pl.skinny)
-    std::snprintf(buf, sizeof(buf), "kernel=skinny tile=%dx%d tiles=%d splits=%d", pl.cfg, 4 * pl.wn,
-                  pl.m_tiles * pl.n_tiles, pl.splits);
+  const DenseKind kind = op == DG_OP_BF16_GEMM_NT ? kBf16 : op == DG_OP_GEMM_NT_UE8M0 ? kUe8m0 : kFp8;
+  const int64_t kbytes = kind == kBf16 ? 2 * K : K;
+  const int64_t chunk = launch_rows(kbytes, 2 * N);
+  if (chunk == 0 || (N + 256) * kbytes >= kOffLim) return text.c_str();
+  const int64_t r = std::min(rows, chunk);
+  const DensePlan pl = plan_dense(kind, r, N, K, ecus, (size_t)-1);
+  if (pl.skinny)
+    std::snprintf(buf, sizeof(buf), "kernel=skinny tile=%dx%d tiles=%d splits=%d chunks=%lld", pl.cfg, 4 * pl.wn,
+                  pl.m_tiles * pl.n_tiles, pl.splits, (long long)ceil_div(rows, chunk));
   else
-    std::snprintf(buf, sizeof(buf), "kernel=%s tiles=%d splits=%d", pl.lds ? "lds" : "v1", pl.m_tiles * pl.n_tiles,
-                  pl.splits);
+    std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx%d grid=%d tiles=%d whole=%d tail=%dx%d chunks=%lld",
+                  pl.wide ? "wide" : "persistent", 256, pl.wide ? 256 : 128, pl.grid, pl.m_tiles * pl.n_tiles,
+                  pl.dp_tiles, pl.sk_tiles, pl.sk_pieces, (long long)ceil_div(rows, chunk));
   text = buf;
   return text.c_str();
 }
@@ -942,6 +863,6 @@ int dg_get_num_cus(void) {
 
 const char* dg_get_last_error(void) { return g_last_error.c_str(); }
 
-const char* dg_version(void) { return "dg-mi355x 0.1.0 (gfx950)"; }
+const char* dg_version(void) { return "dg-mi355x 0.2.0 (gfx950)"; }
 
 }  // extern "C"

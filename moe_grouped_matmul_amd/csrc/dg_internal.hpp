@@ -18,6 +18,8 @@ struct GemmParams {
   float* ws;             // split-K partials [splits][rows][N] (dense only)
   const int32_t* index;  // m_indices (contiguous), masked_m (masked) or ks (K-grouped); unused when dense
   int64_t rows;          // dense: M; contiguous: M_total; masked: max_m (rows per group)
+  int sfa_ld;            // row stride of the MN-major activation scales (elements): the caller's row
+                         // count, which exceeds `rows` when a call is split into row chunks
   int N;
   int K;
   int G;
@@ -47,24 +49,6 @@ struct GemmParams {
 // by the matrix cores' block scaling.
 enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4, kKGrouped = 5, kDenseUe8m0 = 6 };
 
-// Tile configurations compiled for gfx950 (workgroup tile BM x BN, K step 128).
-enum TileCfg { kTile128x128 = 0, kTile64x128 = 1, kTile64x64 = 2, kNumTileCfgs = 3 };
-
-struct TileShape {
-  int bm;
-  int bn;
-};
-TileShape tile_shape(int cfg);
-
-// LDS-ring kernel configurations (gemm_lds.hip): 512-thread workgroups.
-enum LdsCfg { kLds256x128 = 0, kLds128x256 = 1 };
-TileShape lds_tile_shape(int cfg);
-
-// Enqueue the LDS-ring kernel (dense, contiguous or masked; no split-K); operands are
-// addressed with 32-bit offsets, so (rows + 256) * K, (N + 256) * K and
-// rows * K / 32 must stay below 2^32.
-hipError_t launch_gemm_lds(int mode, int cfg, const GemmParams& p, hipStream_t stream);
-
 // Enqueue the skinny dense kernel (gemm_skinny.hip, M <= 128, bm-row tiles
 // with bm in {64, 128}, wn in {16, 32} columns per wave, 4 waves):
 // p.m_tiles = ceil(M / bm), p.n_tiles = ceil(N / (4 wn)), p.splits K splits of
@@ -72,22 +56,28 @@ hipError_t launch_gemm_lds(int mode, int cfg, const GemmParams& p, hipStream_t s
 // skinny_workspace_bytes(...) bytes: fp32 partials followed by one uint32
 // counter per tile that must be zero on entry (each call leaves them zero).
 size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int splits);
-hipError_t launch_gemm_skinny(int bm, int wn, const GemmParams& p, hipStream_t stream);
+hipError_t launch_gemm_skinny(int bm, int wn, int depth, const GemmParams& p, hipStream_t stream);
 // K blocks in flight per wave (ring depth; LDS per slot is (bm + 4 wn) * 128 B
 // plus 1 KB); a split's block count is padded to a multiple of it (padding
 // blocks read as zeros), so splits should be multiples.  Four slots for 64-row
 // tiles of 16-column waves (about 70 KB, two workgroups per CU) measured
 // faster than eight (one per CU) on every decode shape tried.
 constexpr int skinny_depth(int bm, int wn) { return bm == 64 ? 4 : (wn == 16 ? 6 : 4); }
+// Ring depths compiled for each tile shape (the default above, and deeper
+// rings that fit the LDS for measurement through DG_FORCE_CONFIG).
+constexpr bool skinny_depth_ok(int bm, int wn, int d) {
+  return d == skinny_depth(bm, wn) || (bm == 64 && wn == 16 && d == 8) || (bm == 64 && wn == 32 && d == 6);
+}
 
 // Enqueue the persistent kernel (gemm_persist.hip) with `grid` workgroups (one
 // per CU): mode kDense over 256x128 tiles (tail tiles split along K when
 // p.sk_tiles > 0, p.ws then holds persistent_workspace_bytes(...) bytes whose
 // counters must be zero on entry and are left zero), kContiguous over 128x256
 // tiles (p.dp_tiles = all tiles, no split; at most kPersistentMaxContigTiles
-// tiles per workgroup), kMasked over 256x128 tiles (G <= 1024) or kKGrouped
-// over 256x128 tiles of every group (G <= 1024, no split).  A, B, sfa and D of
-// all groups are addressed with 32-bit offsets (K-grouped: D and C per group).
+// tiles per workgroup), kMasked over 128x256 tiles (G <= 1024) or kKGrouped
+// over 256x128 tiles of every group (G <= 1024, no split).  One launch's A,
+// alpha and D (masked: one group's, from the group's base) and one expert's
+// B are addressed with 32-bit offsets; alpha rows are p.sfa_ld apart.
 constexpr int kPersistentMaxContigTiles = 64;
 size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces);
 hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream);
@@ -95,13 +85,10 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
 // Enqueue the wide-tile persistent kernel (gemm_wide.hip): mode kDense or
 // kContiguous over 256 x 256 tiles (p.m_tiles = ceil(rows/256), p.n_tiles =
 // ceil(N/256)), no K split, `grid` workgroups; contiguous: at most
-// kWideMaxContigTiles tiles per workgroup; 32-bit offsets as for the
-// persistent kernel.
+// kWideMaxContigTiles tiles per workgroup; offsets as for the persistent
+// kernel.
 constexpr int kWideMaxContigTiles = 64;
 hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t stream);
-
-// Enqueue the GEMM kernel (and the split-K reduction when p.splits > 1).
-hipError_t launch_gemm(int mode, int cfg, const GemmParams& p, int groups, hipStream_t stream);
 
 // ue8m0: scales as packed UE8M0 codes (int32 words of four K blocks) instead of fp32
 hipError_t launch_quant_1x128(const float* x, uint8_t* q, void* sfa, int64_t G, int64_t M, int64_t K, bool ue8m0,

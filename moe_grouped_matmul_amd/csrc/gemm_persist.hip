@@ -317,13 +317,18 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     return r;
   };
 
-  // ---- buffer resources over whole arrays (all groups); offsets are 32-bit
-  const uint32_t a_bytes = (uint32_t)(ngrp * rows) * (uint32_t)K;
-  const uint32_t b_bytes = (uint32_t)(nbgrp * N) * (uint32_t)K;
-  const uint32_t s_bytes = (uint32_t)(ngrp * rows) * (uint32_t)(UE ? KW : KB) * 4u;
+  // ---- buffer resources: one group's A, alpha and D (masked: from the
+  // group's 64-bit base) and one expert's B, each addressed with 32-bit
+  // offsets; alpha rows are sfa_ld apart
+  (void)nbgrp;
+  const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K;
+  // (the last scale row ends after this launch's rows: a row chunk's scales
+  // never reach past the caller's array)
+  const uint32_t s_bytes = ((uint32_t)p.sfa_ld * (uint32_t)((UE ? KW : KB) - 1) + (uint32_t)rows) * 4u;
   const uint32_t sb_bytes = KG ? (uint32_t)N * (uint32_t)KB * 4u : 0u;  // K-grouped beta [KB][N]
   const __amdgpu_buffer_rsrc_t rd = F32OUT ? make_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
-                                        : make_rsrc(p.D, (uint32_t)(ngrp * rows) * (uint32_t)N * 2u);
+                                        : make_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
   // accumulating form: C (a null C reads as zeros through a zero-length range)
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.Cacc, ACC && p.Cacc ? (uint32_t)rows * (uint32_t)N * 4u : 0u);
 
@@ -358,10 +363,16 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   uint32_t is_aoff[A_INS];
   uint32_t is_boff[B_INS];
   uint32_t is_soff;
+  const uint8_t* is_aptr = p.A;    // the segment's group of A rows (masked)
+  const uint8_t* is_bptr = p.B;    // the segment's expert's weights
+  const float* is_sptr = p.sfa;    // the segment's group of alpha (masked)
   auto is_setup = [&]() {
     const int agrp = KG ? 0 : is_t.grp;  // K-grouped: A and alpha are shared by all groups
-    const int arow = agrp * rows + is_t.mt * BM;
-    const int brow = is_t.bgrp * N + is_t.nt * BN;
+    is_aptr = p.A + (size_t)agrp * (size_t)rows * (size_t)K;
+    is_sptr = p.sfa + (size_t)agrp * (size_t)KB * (size_t)rows;
+    is_bptr = p.B + (size_t)is_t.bgrp * (size_t)N * (size_t)K;
+    const int arow = is_t.mt * BM;
+    const int brow = is_t.nt * BN;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int r = 64 * i + a_loc;
@@ -375,9 +386,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     // scale lanes: alpha of the tile's rows that exist; beta (K-grouped) of
     // its columns below N; every other lane addresses past the range
     const int srow = wave * 64 + lane;
-    is_soff = srow < BM && srow < is_t.row_limit
-                  ? (uint32_t)((agrp * KB * rows + is_t.mt * BM + srow) * 4)
-                  : kOOB;
+    is_soff = srow < BM && srow < is_t.row_limit ? (uint32_t)((is_t.mt * BM + srow) * 4) : kOOB;
     if (KG && bwave) {
       const int scol = is_t.nt * BN + (wave - 4) * 64 + lane;
       is_soff = scol < N ? (uint32_t)(scol * 4) : kOOB;
@@ -393,10 +402,10 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 #define PS_ISSUE_BEGIN()                                                                                   \
   const bool in_ = is_seg < nseg;                                                                          \
   const bool ld_ = in_ && !(KG && is_t.zero);                                                              \
-  const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(p.A, ld_ ? a_bytes : 0u);                                   \
-  const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(p.B, ld_ ? b_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t ra_ = make_rsrc(is_aptr, ld_ ? a_bytes : 0u);                               \
+  const __amdgpu_buffer_rsrc_t rb_ = make_rsrc(is_bptr, ld_ ? b_bytes : 0u);                               \
   const __amdgpu_buffer_rsrc_t rs_ = bwave ? make_rsrc(p.sfb, ld_ ? sb_bytes : 0u)                         \
-                                           : make_rsrc(p.sfa, ld_ ? s_bytes : 0u);                         \
+                                           : make_rsrc(is_sptr, ld_ ? s_bytes : 0u);                       \
   const int ks_ = is_kb << 7
 #define PS_ISSUE_LOAD(st_, bs_, n_)                                                                        \
   do {                                                                                                     \
@@ -410,7 +419,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     else                                                                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                            \
           rs_, (DG_LDS void*)(bwave ? &bring[KG ? (bs_) : 0][(wave - 4) * 64] : PS_SS(st_) + wave * 64), 4,     \
-          is_soff, (UE ? (is_kb >> 2) : is_kb) * (bwave ? N : rows) * 4, 0, 0);                             \
+          is_soff, (UE ? (is_kb >> 2) : is_kb) * (bwave ? N : p.sfa_ld) * 4, 0, 0);                         \
   } while (0)
 #define PS_ISSUE_END()                                                                                     \
   do {                                                                                                     \
@@ -476,7 +485,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   uint32_t st_m[4] = {~0u, ~0u, ~0u, ~0u};  // contiguous: rows tagged with the tile's expert
 #define PS_MARK_TILE()                                                                                     \
   do {                                                                                                     \
-    st_row0 = (KG ? 0 : cp_t.grp * rows) + cp_t.mt * BM;                                                  \
+    st_row0 = cp_t.mt * BM; /* masked: D of group st_grp from its own base */                            \
     st_col0 = cp_t.nt * BN;                                                                                \
     st_rows = cp_t.row_limit;                                                                              \
     st_grp = cp_t.grp;                                                                                     \
@@ -517,6 +526,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, u[i_][j_] + c_[i_][j_]), rd_,   \
                                                  o_[i_] + 16u * j_, 0, 0);                                 \
     } else {                                                                                               \
+      const __amdgpu_buffer_rsrc_t rdm_ =                                                                  \
+          MODE == kMasked ? make_rsrc(p.D + (size_t)st_grp * (size_t)rows * (size_t)N, (uint32_t)rows * (uint32_t)N * 2u) : rd; \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         const uint32_t off_ = PS_OUT_OFF(i_);                                                              \
         uint32_t w_[8];                                                                                    \
@@ -524,8 +535,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
           w_[2 * j_] = pack_bf16x2(u[i_][j_][0], u[i_][j_][1]);                                            \
           w_[2 * j_ + 1] = pack_bf16x2(u[i_][j_][2], u[i_][j_][3]);                                        \
         }                                                                                                  \
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[0], w_[1], w_[2], w_[3]}, rd, off_, 0, 0);         \
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rd,                      \
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[0], w_[1], w_[2], w_[3]}, rdm_, off_, 0, 0);       \
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w_[4], w_[5], w_[6], w_[7]}, rdm_,                    \
                                                off_ == kOOB ? kOOB : off_ + 16u, 0, 0);                    \
       }                                                                                                    \
     }                                                                                                      \

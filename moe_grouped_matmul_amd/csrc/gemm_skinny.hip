@@ -123,7 +123,10 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * K, (uint32_t)(M - m0 < BM ? M - m0 : BM) * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, (uint32_t)N * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.sfa + m0, ((uint32_t)M * (uint32_t)KB - (uint32_t)m0) * 4u);
+  // alpha rows are sfa_ld apart (the row stride of the caller's [K/128][rows]
+  // array); the range ends after this launch's last row of the last K block
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.sfa + m0, ((uint32_t)p.sfa_ld * (uint32_t)(KB - 1) + (uint32_t)(M - m0)) * 4u);
   // zero-length ranges: loads for the padding steps past the split's last
   // block read zeros and touch no memory
   const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(p.A, 0);
@@ -196,7 +199,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(SK_SLOT(sA, st_) + (i_ * NW + wave) * 1024), \
                                                  16, a_src + i_ * a_stride, (kb_) << 7, 0, 0);             \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(SK_SLOT(sS, st_) + wave * 64), 4, s_src,  \
-                                             (kb_) * M * 4, 0, 0);                                         \
+                                             (kb_) * p.sfa_ld * 4, 0, 0);                                  \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                      \
       _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                                     \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                          \
@@ -387,17 +390,15 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int BM, int WN>
+template <int BM, int WN, int P>
 hipError_t launch_skinny_cfg(const GemmParams& p, hipStream_t stream) {
   const int64_t units = (int64_t)p.n_tiles * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.m_tiles;
   if (grid <= 0) return hipSuccess;
   if (p.Dacc)
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, skinny_depth(BM, WN), true>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, skinny_depth(BM, WN), false>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -409,9 +410,10 @@ size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int spli
   return (size_t)splits * m_tiles * n_tiles * bm * 4 * wn * 4 + (size_t)m_tiles * n_tiles * 4;
 }
 
-hipError_t launch_gemm_skinny(int bm, int wn, const GemmParams& p, hipStream_t stream) {
-  if (bm == 64) return wn == 16 ? launch_skinny_cfg<64, 16>(p, stream) : launch_skinny_cfg<64, 32>(p, stream);
-  return wn == 16 ? launch_skinny_cfg<128, 16>(p, stream) : launch_skinny_cfg<128, 32>(p, stream);
+hipError_t launch_gemm_skinny(int bm, int wn, int depth, const GemmParams& p, hipStream_t stream) {
+  if (bm == 64 && wn == 16) return depth == 8 ? launch_skinny_cfg<64, 16, 8>(p, stream) : launch_skinny_cfg<64, 16, 4>(p, stream);
+  if (bm == 64) return depth == 6 ? launch_skinny_cfg<64, 32, 6>(p, stream) : launch_skinny_cfg<64, 32, 4>(p, stream);
+  return wn == 16 ? launch_skinny_cfg<128, 16, 6>(p, stream) : launch_skinny_cfg<128, 32, 4>(p, stream);
 }
 
 }  // namespace dg

@@ -243,9 +243,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   }
   int J = nseg * KB;  // iterations of this workgroup (K-grouped: counted below)
 
+  // A, alpha and D of this launch and one expert's B are addressed with
+  // 32-bit offsets from their bases (the expert's weights from its own
+  // 64-bit base); alpha rows are sfa_ld apart
   const uint32_t a_bytes = (uint32_t)rows * (uint32_t)K;
-  const uint32_t b_bytes = (uint32_t)(CONTIG ? p.G : 1) * (uint32_t)N * (uint32_t)K;
-  const uint32_t s_bytes = (uint32_t)rows * (uint32_t)(UE ? KW : KB) * 4u;
+  const uint32_t b_bytes = (uint32_t)N * (uint32_t)K;
+  // (the last scale row ends after this launch's rows: a row chunk's scales
+  // never reach past the caller's array)
+  const uint32_t s_bytes = ((uint32_t)p.sfa_ld * (uint32_t)((UE ? KW : KB) - 1) + (uint32_t)rows) * 4u;
   const __amdgpu_buffer_rsrc_t rd = ACC ? wide_rsrc(p.Dacc, (uint32_t)rows * (uint32_t)N * 4u)
                                         : wide_rsrc(p.D, (uint32_t)rows * (uint32_t)N * 2u);
   const __amdgpu_buffer_rsrc_t rc = wide_rsrc(p.Cacc, HASC ? (uint32_t)rows * (uint32_t)N * 4u : 0u);
@@ -315,12 +320,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   // ---- issue pointer: iteration j + 1 of this workgroup's sequence
   int is_seg = 0, is_kb = 0, is_hi = KB, is_zero = 0;
   uint32_t is_aoff[A_INS], is_boff[B_INS], is_soff;
+  const uint8_t* is_bptr = p.B;  // weights of the pass's expert
   const bool bwave = KG && wave >= 4;  // K-grouped: waves 4..7 load beta of the tile's columns
   auto is_setup = [&]() {
     int mt, nt, e, hm;
     tile_of(is_seg, &mt, &nt, &e, &hm);
     k_range(e, &is_kb, &is_hi, &is_zero);
     if (KG) e = 0;  // B is shared by the groups
+    is_bptr = p.B + (size_t)e * (size_t)N * (size_t)K;
     const int row_limit = rows - mt * BM < BM ? rows - mt * BM : BM;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -330,7 +337,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const int c = nt * BN + 64 * i + b_perm;
-      is_boff[i] = c < N ? (uint32_t)(e * N + c) * (uint32_t)K + dma_chunk : kWideOOB;
+      is_boff[i] = c < N ? (uint32_t)c * (uint32_t)K + dma_chunk : kWideOOB;
     }
     const int srow = wave * 64 + lane;  // alpha of the tile's rows that exist
     is_soff = srow < BM && srow < row_limit && ((hm >> (srow >> 7)) & 1) ? (uint32_t)((mt * BM + srow) * 4) : kWideOOB;
@@ -345,7 +352,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
   const bool in_ = is_seg < nseg;                                                                          \
   const bool ld_ = in_ && !(KG && is_zero);                                                                \
   const __amdgpu_buffer_rsrc_t ra_ = wide_rsrc(p.A, ld_ ? a_bytes : 0u);                                   \
-  const __amdgpu_buffer_rsrc_t rb_ = wide_rsrc(p.B, ld_ ? b_bytes : 0u);                                   \
+  const __amdgpu_buffer_rsrc_t rb_ = wide_rsrc(is_bptr, ld_ ? b_bytes : 0u);                               \
   const __amdgpu_buffer_rsrc_t rs_ = bwave ? wide_rsrc(p.sfb, ld_ ? (uint32_t)N * (uint32_t)KB * 4u : 0u)  \
                                            : wide_rsrc(p.sfa, ld_ ? s_bytes : 0u);                         \
   const int ks_ = is_kb << 7
@@ -360,7 +367,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
           is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0);                   \
     else                                                                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(WD_SS(st_) + wave * 64), 4, is_soff,    \
-                                               (UE ? (is_kb >> 2) : is_kb) * (bwave ? N : rows) * 4, 0, 0); \
+                                               (UE ? (is_kb >> 2) : is_kb) * (bwave ? N : p.sfa_ld) * 4, 0, 0); \
   } while (0)
 #define WD_ISSUE_END()                                                                                     \
   do {                                                                                                     \

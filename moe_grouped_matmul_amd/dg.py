@@ -14,8 +14,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# DG_LIBRARY may point at another build of the same library (tuning experiments)
-LIB_PATH = os.environ.get("DG_LIBRARY", os.path.join(_HERE, "libdg_mi355x.so"))
+LIB_PATH = os.path.join(_HERE, "libdg_mi355x.so")
 
 DG_OK = 0
 DG_ERR_INVALID_ARG = 1
@@ -63,12 +62,13 @@ class DGError(RuntimeError):
 _lib = None
 
 
-def load_library(path=None):
-    """Load (once) and return the ctypes handle; raises if the library is missing."""
+def load_library():
+    """Load (once) and return the ctypes handle of the in-tree library; raises
+    if it is missing."""
     global _lib
-    if _lib is not None and path is None:
+    if _lib is not None:
         return _lib
-    p = path or LIB_PATH
+    p = LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(
             f"{p} not found: build it first (python -m moe_grouped_matmul_amd.build); "
@@ -100,8 +100,7 @@ def load_library(path=None):
                  "dg_quant_128x128_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
                  "dg_get_m_alignment_for_contiguous_layout"):
         getattr(lib, name).restype = I
-    if path is None:
-        _lib = lib
+    _lib = lib
     return lib
 
 

@@ -34,6 +34,31 @@ def assert_close(got_bits, ref_bits, what=""):
         raise AssertionError(f"{what}: {n} elements outside tolerance, e.g. {detail}")
 
 
+def f32_rule_violations(got, ref):
+    """Elements of an fp32 result outside the per-element acceptance rule
+    |got - ref| <= 2^-7 |ref| + 1e-3 rms(ref), rms over the finite reference
+    elements of the call in fp64; NaN positions must coincide.  Returns the
+    boolean mask of violating elements."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    gn, rn = np.isnan(got), np.isnan(ref)
+    fin = ~gn & ~rn
+    r = ref[fin]
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    bad = gn != rn
+    with np.errstate(invalid="ignore"):
+        bad |= fin & ~(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-3 * rms)
+    return bad
+
+
+def assert_f32_rule(got, ref, what=""):
+    bad = f32_rule_violations(got, ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:3]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements outside 2^-7|ref| + 1e-3 rms(ref), e.g. "
+                             f"{[(tuple(i), float(np.asarray(got)[tuple(i)]), float(np.asarray(ref)[tuple(i)])) for i in idx]}")
+
+
 def masked_layout(codes, scales, rows, G, max_m):
     """Place valid rows (expert-major) into [G, max_m, K] / [G, K/128, max_m] with traps elsewhere."""
     from moe_grouped_matmul_amd.workloads import place_rows

@@ -87,7 +87,16 @@ def test_status_codes_from_host(lib):
     assert contig(P16, P16, P16, P16, P16, P16, 256, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
     assert contig(P16, P16, P16, P16, P16, None, 256, 128, 256, 2, None, 0, s) == dg.DG_ERR_INVALID_ARG
     assert contig(P16, P16, P16, P16, P16, P16 + 2, 256, 128, 256, 2, None, 0, s) == dg.DG_ERR_ALIGN
+    # G beyond 1024 groups, and one expert's weights of 4 GiB or more
+    assert contig(P16, P16, P16, P16, P16, P16, 256, 128, 256, 1025, None, 0, s) == dg.DG_ERR_SHAPE and "G" in _err(lib)
+    assert contig(P16, P16, P16, P16, P16, P16, 256, 1 << 19, 8192, 2, None, 0, s) == dg.DG_ERR_SHAPE
+    assert "4 GiB" in _err(lib)
     masked = lib.dg_m_grouped_fp8_gemm_nt_masked
+    assert masked(P16, P16, P16, P16, P16, P16, 1025, 256, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
+    assert masked(P16, P16, P16, P16, P16, P16, 2, 256, 1 << 19, 8192, 0, None, 0, s) == dg.DG_ERR_SHAPE
+    assert "4 GiB" in _err(lib)
+    # one expert's rows past 32-bit offsets (max_m * K or max_m * N * 2 bytes)
+    assert masked(P16, P16, P16, P16, P16, P16, 2, 1 << 20, 4096, 8192, 0, None, 0, s) == dg.DG_ERR_SHAPE
     assert masked(P16, P16, P16, P16, P16, P16, 0, 256, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
     assert masked(P16, P16, P16, P16, P16, P16, 4, -1, 128, 256, 0, None, 0, s) == dg.DG_ERR_SHAPE
     assert masked(None, None, None, None, None, None, 4, 0, 128, 256, 0, None, 0, s) == dg.DG_OK
@@ -103,6 +112,13 @@ def test_status_codes_from_host(lib):
     assert kg(P16, P16, P16, P16, P16 + 4, P16, P16, 2, 256, 128, 256, None, 0, s) == dg.DG_ERR_ALIGN
     assert kg(P16, P16, P16, P16, None, P16, P16 + 2, 2, 256, 128, 256, None, 0, s) == dg.DG_ERR_ALIGN
     assert kg(P16, P16, P16, P16, None, P16, P16, 2, 1 << 20, 4096, 4096, None, 0, s) == dg.DG_ERR_SHAPE
+    # dense forms: weights of 4 GiB or more; rows too long for one tile of
+    # 32-bit offsets; K split into row chunks otherwise (no status code)
+    assert gemm(P16, P16, P16, P16, P16, 64, 1 << 19, 8192, None, 0, s) == dg.DG_ERR_SHAPE and "4 GiB" in _err(lib)
+    assert lib.dg_fp8_gemm_nt_acc(P16, P16, P16, P16, None, P16, 64, 1 << 19, 8192, None, 0, s) == dg.DG_ERR_SHAPE
+    assert lib.dg_fp8_gemm_nt_ue8m0(P16, P16, P16, P16, P16, 64, 1 << 19, 8192, None, 0, s) == dg.DG_ERR_SHAPE
+    assert lib.dg_bf16_gemm_nt(P16, P16, P16, 64, 1 << 18, 8192, None, 0, s) == dg.DG_ERR_SHAPE
+    assert gemm(P16, P16, P16, P16, P16, 64, 16, 1 << 24, None, 0, s) == dg.DG_ERR_SHAPE
     q1 = lib.dg_quant_1x128
     assert q1(P16, P16, P16, 1, 4, 100, s) == dg.DG_ERR_SHAPE
     assert q1(None, P16, P16, 1, 4, 128, s) == dg.DG_ERR_INVALID_ARG
@@ -131,13 +147,15 @@ def test_utilities(lib):
     assert lib.dg_set_num_cus(64) == 0
     assert lib.dg_set_num_cus(0) == 0
     # dense small-M shapes ask for split-K scratch; large ones only when the
-    # tile count leaves a partial last round on the (default 256) CUs, whose
-    # tail tiles are then split along K: 4096x7168 -> 16 x 56 = 896 tiles,
-    # 128 tail tiles in 2 pieces of 256x128 fp32 partials + one counter each
+    # 256 x 128 tiles they run leave a partial last round on the (default 256)
+    # CUs, whose tail tiles are then split along K: 4096x2112 -> 16 x 17 = 272
+    # tiles, 16 tail tiles in 4 pieces of 256x128 fp32 partials + one counter
+    # each; 256 x 256 tiles (4096x7168, 4096x4096) need none
     assert lib.dg_get_workspace_size(0, 64, 2112, 7168, 1) > 0
     assert lib.dg_set_num_cus(256) == 0  # the MI355X count, also when no device is visible
-    assert lib.dg_get_workspace_size(0, 4096, 7168, 16384, 1) == 128 * 2 * 256 * 128 * 4 + 128 * 4
-    assert lib.dg_get_workspace_size(0, 4096, 4096, 7168, 1) == 0  # 512 tiles: whole rounds
+    assert lib.dg_get_workspace_size(0, 4096, 2112, 7168, 1) == 16 * 4 * 256 * 128 * 4 + 16 * 4
+    assert lib.dg_get_workspace_size(0, 4096, 7168, 16384, 1) == 0
+    assert lib.dg_get_workspace_size(0, 4096, 4096, 7168, 1) == 0  # 256 x 256 tiles: whole rounds
     assert lib.dg_set_num_cus(0) == 0
     assert lib.dg_get_workspace_size(2, 256, 4096, 7168, 32) == 0
 

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from moe_grouped_matmul_amd import dg, workloads
-from tests.helpers import acc_tolerance
+from tests.helpers import acc_tolerance, assert_f32_rule
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -42,6 +42,8 @@ def _check(got, qa, sa, qb, sb, c, what):
     bad = ~(np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= tol)
     assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bound, e.g. " \
                           f"{[(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in np.argwhere(bad)[:3]]}"
+    # the per-element acceptance rule on top of the arithmetic ceiling above
+    assert_f32_rule(got, ref, what)
 
 
 SHAPES = [(1, 16, 128), (64, 2112, 1024), (100, 272, 4096), (128, 528, 512), (130, 144, 640), (257, 400, 384),

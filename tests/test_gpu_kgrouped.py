@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from moe_grouped_matmul_amd import dg, workloads
-from tests.helpers import kg_tolerance
+from tests.helpers import assert_f32_rule, kg_tolerance
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,6 +40,8 @@ def _check(got, qa, sa, qb, sb, ks, c, what):
     bad = ~(np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= tol)
     assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bound, e.g. " \
                           f"{[(tuple(i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in np.argwhere(bad)[:3]]}"
+    # the per-element acceptance rule on top of the arithmetic ceiling above
+    assert_f32_rule(got, ref, what)
 
 
 def _run(qa, sa, qb, sb, ks, C, D):

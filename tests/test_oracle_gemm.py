@@ -69,22 +69,20 @@ def test_pages_worked_exercise_promoted_equals_dequantise_first():
     B = rs.randint(g["int_low"], g["int_high_exclusive"], size=(N, K)).astype(np.float32)
     S_A = rs.uniform(g["scale_low"], g["scale_high"], size=(M, K // bk)).astype(np.float32)
     S_B = rs.uniform(g["scale_low"], g["scale_high"], size=(N // bn, K // bk)).astype(np.float32)
-    # dequantise-first formulation the page uses as its reference: scale each
-    # K block of A by its row scale and of B by its block scale, then multiply
-    deq = np.zeros((M, N), np.float64)
-    for kb in range(K // bk):
-        a_sub = A[:, kb * bk:(kb + 1) * bk].astype(np.float64) * S_A[:, kb:kb + 1]
-        b_sub = B[:, kb * bk:(kb + 1) * bk].astype(np.float64) * S_B[np.arange(N) // bn, kb][:, None]
-        deq += a_sub @ b_sub.T
+    # the dequantise-first reading of the closed form: expand every scale to
+    # the elements it covers (alpha over its row's 128-wide K group, beta over
+    # its 128 x 128 block), dequantise both operands once, and take one
+    # ordinary product of the real-valued matrices
+    alpha_full = np.repeat(S_A.astype(np.float64), bk, axis=1)                  # [M, K]
+    beta_full = np.repeat(np.repeat(S_B.astype(np.float64), bn, axis=0), bk, axis=1)  # [N, K]
+    a_real = A.astype(np.float64) * alpha_full
+    b_real = B.astype(np.float64) * beta_full
+    deq = a_real @ b_real.T
     acc = gemm_nt_acc(encode_e4m3(A), np.ascontiguousarray(S_A.T), encode_e4m3(B), S_B)
     assert np.allclose(acc, deq, atol=g["atol"], rtol=0)
-    # both forms are fp64 evaluations of the same sum: they differ by rounding
-    # only, bounded by a few ulps of the sum of absolute terms
-    mag = np.zeros((M, N), np.float64)
-    for kb in range(K // bk):
-        a_abs = np.abs(A[:, kb * bk:(kb + 1) * bk]).astype(np.float64) * S_A[:, kb:kb + 1]
-        b_abs = np.abs(B[:, kb * bk:(kb + 1) * bk]).astype(np.float64) * S_B[np.arange(N) // bn, kb][:, None]
-        mag += a_abs @ b_abs.T
+    # both are fp64 evaluations of the same sum: they differ by rounding only,
+    # bounded by a few ulps of the sum of the absolute terms
+    mag = np.abs(a_real) @ np.abs(b_real).T
     assert np.all(np.abs(acc - deq) <= 4 * (K // bk + 1) * 2.0 ** -53 * mag * 8)
 
 
