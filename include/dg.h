@@ -253,6 +253,26 @@ int dg_fp8_gemm_nt_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
                          uint16_t* D, int64_t M, int64_t N, int64_t K, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * M-grouped contiguous and masked GEMMs with UE8M0 scales (the grouped forms
+ * of dg_fp8_gemm_nt_ue8m0; deep-dive blog, section 3: the grouped GEMMs take
+ * the scale formats of the plain ones).  Operands, index arrays, outputs and
+ * rules as for dg_m_grouped_fp8_gemm_nt_contiguous / _masked, with packed
+ * int32 scales (four K blocks per word, block 4w + j in byte j):
+ *   contiguous: sfa [ceil(K/512)][M_total], sfb [G][ceil(N/128)][ceil(K/512)]
+ *   masked:     sfa [G][ceil(K/512)][max_m], sfb [G][ceil(N/128)][ceil(K/512)]
+ * (dg_quant_1x128_ue8m0 with G groups writes the masked activation layout,
+ * dg_quant_128x128_ue8m0 with G experts the weight layout).
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
+                                              const int32_t* sfb, uint16_t* D, const int32_t* m_indices,
+                                              int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                              void* workspace, size_t workspace_bytes, void* stream);
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
+                                          const int32_t* sfb, uint16_t* D, const int32_t* masked_m,
+                                          int64_t G, int64_t max_m, int64_t N, int64_t K, int64_t expected_m,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes that let `op` use its full K split for this shape with the
  * current CU cap (0 = none used); a call split into row chunks reuses it for
  * every chunk. */

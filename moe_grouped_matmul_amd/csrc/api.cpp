@@ -21,9 +21,14 @@
 //                           the K blocks and the workspace), ring depth p
 //                           among the compiled ones (dg::skinny_depth_ok)
 // DG_PRINT_CONFIGS (debug): print each launch's plan on stderr.
+// DG_CHECK_LAYOUT (debug): the contiguous forms copy m_indices to the host
+// (synchronising the stream; skipped while the stream is being captured) and
+// reject a layout in which an aligned 128-row block holds rows of two
+// experts (DG_ERR_INVALID_ARG).
 
 #include <algorithm>
 #include <atomic>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -267,7 +272,7 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
   if (P < 2) return;
   const int kbs = (int)ceil_div(KB, P);
   P = (int)ceil_div(KB, kbs);  // every piece non-empty
-  if (P < 2 || dg::persistent_workspace_bytes((int)rem, P) > ws_bytes ||
+  if (P < 2 || rem > dg::kWsMaxCounters || dg::persistent_workspace_bytes((int)rem, P) > ws_bytes ||
       dg::persistent_workspace_bytes((int)rem, P) > (size_t)kOffLim)
     return;
   pl.dp_tiles = (int)(T - rem);
@@ -283,7 +288,10 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
 // tile wins ties; with one, 16-column waves give the most tiles, and the split
 // is at most K / (20 bm) (the fp32 partials then stay below a fifth of the
 // weight bytes; more splits lose more in the fix-up than they gain), at most
-// 16, and only as large as the workspace holds.
+// 16, and only as large as the workspace holds.  (Re-measured against a sweep
+// of tile shape, split and ring depth on the decode shapes of the dense sweep,
+// each configuration with a freshly zeroed workspace: no configuration beat
+// this rule by more than the run-to-run spread.)
 void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   const int KB = (int)(K / 128);
   pl.skinny = true;
@@ -316,7 +324,7 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
   pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
   const int64_t tiles = (int64_t)pl.m_tiles * pl.n_tiles;
   int splits = 1;
-  if (tiles < cus) {
+  if (tiles < cus && tiles <= dg::kWsMaxCounters) {
     splits = (int)(cus / tiles);
     const int cap = (int)(K / (20 * cap_rows));
     if (splits > cap) splits = cap;
@@ -327,6 +335,7 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
       --splits;
     if (splits < 2) splits = 1;
   }
+  int depth = dg::skinny_depth(pl.cfg, pl.wn);
   const Force f = forced();
   if (f.sk_bm) {  // DG_FORCE_CONFIG=skinny=...
     pl.cfg = f.sk_bm;
@@ -334,11 +343,12 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
     pl.m_tiles = (int)ceil_div(M, pl.cfg);
     pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
     splits = f.sk_splits < KB ? f.sk_splits : KB;
+    if ((int64_t)pl.m_tiles * pl.n_tiles > dg::kWsMaxCounters) splits = 1;
     while (splits > 1 && dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, splits) > ws_bytes) --splits;
+    depth = f.sk_depth;
   }
-  // whole ring cycles per split where that does not cost a split
-  const int depth = f.sk_bm ? f.sk_depth : dg::skinny_depth(pl.cfg, pl.wn);
   pl.depth = depth;
+  // whole ring cycles per split where that does not cost a split
   int kbs = (int)ceil_div(KB, splits);
   const int kbs_r = (int)ceil_div(kbs, depth) * depth;
   if (ceil_div(KB, kbs_r) == splits || kbs_r - kbs < depth / 2) kbs = kbs_r;
@@ -478,6 +488,144 @@ ContigPlan plan_contiguous(int64_t rows, int64_t N, int64_t K, int cus) {
   return cp;
 }
 
+// DG_CHECK_LAYOUT: every aligned 128-row block holds rows of at most one
+// expert (indices outside [0, G) are padding and free).  Reads m_indices on
+// the host, so it synchronises the stream; a stream under capture is not
+// checked.
+int check_contiguous_layout(const int32_t* m_indices, int64_t M_total, int64_t G, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DG_ERR_DEVICE, "DG_CHECK_LAYOUT: cannot query the stream");
+  }
+  if (cap != hipStreamCaptureStatusNone) return DG_OK;
+  std::vector<int32_t> idx((size_t)M_total);
+  if (hipMemcpyAsync(idx.data(), m_indices, (size_t)M_total * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DG_ERR_DEVICE, "DG_CHECK_LAYOUT: reading m_indices failed");
+  }
+  for (int64_t b = 0; b < M_total; b += 128) {
+    int32_t e = -1;
+    for (int64_t r = b; r < std::min(M_total, b + 128); ++r) {
+      const int32_t x = idx[(size_t)r];
+      if (x < 0 || x >= G) continue;
+      if (e >= 0 && x != e)
+        return fail(DG_ERR_INVALID_ARG,
+                    "DG_CHECK_LAYOUT: rows %lld..%lld hold experts %d and %d (segments must be padded to 128 rows)",
+                    (long long)b, (long long)std::min(M_total, b + 128) - 1, e, x);
+      e = x;
+    }
+  }
+  return DG_OK;
+}
+
+// The M-grouped contiguous form with fp32 (ue = false) or packed UE8M0 scales.
+int run_contiguous(bool ue, const uint8_t* A, const void* sfa, const uint8_t* B, const void* sfb, uint16_t* D,
+                   const int32_t* m_indices, int64_t M_total, int64_t N, int64_t K, int64_t G, void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if ((rc = check_rows(M_total, "M_total"))) return rc;
+  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
+  if (M_total == 0) return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if (!m_indices) return fail(DG_ERR_INVALID_ARG, "null m_indices");
+  if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
+  const int64_t srow = ue ? ceil_div(K / 128, 4) : K / 128;  // scale words per row
+  if ((rc = check_weights_and_scales(N, K, M_total, srow))) return rc;
+  // row chunks are multiples of 256 rows, so every aligned 128-row block
+  // stays inside one chunk
+  const int64_t chunk = launch_rows(K, 2 * N);
+  if (chunk == 0) return fail(DG_ERR_SHAPE, "rows do not fit 32-bit offsets");
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  if (std::getenv("DG_CHECK_LAYOUT") && (rc = check_contiguous_layout(m_indices, M_total, G, stream))) return rc;
+  const int ecus = effective_cus(cus);
+  for (int64_t r0 = 0; r0 < M_total; r0 += chunk) {
+    const int64_t rows = std::min(chunk, M_total - r0);
+    const ContigPlan cp = plan_contiguous(rows, N, K, ecus);
+    dg::GemmParams p{};
+    p.A = A + r0 * K;
+    p.sfa = static_cast<const float*>(sfa) + r0;  // [K/128 or ceil(K/512)][M_total]: a chunk starts r0 words in
+    p.sfa_ld = (int)M_total;
+    p.B = B;
+    p.sfb = static_cast<const float*>(sfb);
+    p.D = D + r0 * N;
+    p.index = m_indices + r0;
+    p.rows = rows;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.G = (int)G;
+    p.m_tiles = (int)ceil_div(rows, cp.wide ? 256 : 128);
+    p.n_tiles = (int)ceil_div(N, 256);
+    p.splits = 1;
+    p.kb_per_split = (int)(K / 128);
+    p.dp_tiles = (int)cp.tiles;  // every tile whole: no K-split tail, no workspace
+    p.sk_tiles = 0;
+    p.sk_pieces = 1;
+    p.sk_kb = (int)(K / 128);
+    if (print_configs())
+      std::fprintf(stderr,
+                   "[dg] contiguous%s M_total=%lld N=%lld K=%lld G=%lld rows=%lld+%lld tile=%dx256 kernel=%s grid=%d\n",
+                   ue ? "_ue8m0" : "", (long long)M_total, (long long)N, (long long)K, (long long)G, (long long)r0,
+                   (long long)rows, cp.wide ? 256 : 128, cp.wide ? "wide" : "persistent", cp.grid);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int mode = ue ? dg::kContiguousUe8m0 : dg::kContiguous;
+    const hipError_t e =
+        cp.wide ? dg::launch_gemm_wide(mode, cp.grid, p, st) : dg::launch_gemm_persistent(mode, cp.grid, p, st);
+    if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+// The M-grouped masked form with fp32 (ue = false) or packed UE8M0 scales.
+int run_masked(bool ue, const uint8_t* A, const void* sfa, const uint8_t* B, const void* sfb, uint16_t* D,
+               const int32_t* masked_m, int64_t G, int64_t max_m, int64_t N, int64_t K, void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
+  if (max_m < 0) return fail(DG_ERR_SHAPE, "max_m must be >= 0");
+  if (max_m > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "max_m too large");
+  if (max_m == 0) return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if (!masked_m) return fail(DG_ERR_INVALID_ARG, "null masked_m");
+  if (!aligned(masked_m, 4)) return fail(DG_ERR_ALIGN, "masked_m must be 4-byte aligned");
+  // each expert's A, alpha, B and D are addressed from the expert's own base
+  if ((rc = check_weights_and_scales(N, K, max_m, ue ? ceil_div(K / 128, 4) : K / 128))) return rc;
+  if ((max_m + 256) * K >= kOffLim || max_m * N * 2 >= kOffLim)
+    return fail(DG_ERR_SHAPE, "one expert's rows exceed 32-bit offsets (max_m = %lld)", (long long)max_m);
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  dg::GemmParams p{};
+  p.A = A;
+  p.sfa = static_cast<const float*>(sfa);
+  p.sfa_ld = (int)max_m;
+  p.B = B;
+  p.sfb = static_cast<const float*>(sfb);
+  p.D = D;
+  p.index = masked_m;
+  p.rows = max_m;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.G = (int)G;
+  // 128 x 256 tiles over a device-side task list
+  p.m_tiles = (int)ceil_div(max_m, 128);
+  p.n_tiles = (int)ceil_div(N, 256);
+  p.splits = 1;
+  p.kb_per_split = (int)(K / 128);
+  const int64_t tiles = G * p.m_tiles * p.n_tiles;
+  const int ecus = effective_cus(cus);
+  const int grid = (int)(tiles < ecus ? tiles : ecus);
+  if (print_configs())
+    std::fprintf(stderr, "[dg] masked%s G=%lld max_m=%lld N=%lld K=%lld tile=128x256 kernel=persistent grid=%d\n",
+                 ue ? "_ue8m0" : "", (long long)G, (long long)max_m, (long long)N, (long long)K, grid);
+  const hipError_t e = dg::launch_gemm_persistent(ue ? dg::kMaskedUe8m0 : dg::kMasked, grid, p,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -594,62 +742,25 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, cons
   return ok();
 }
 
+
 int dg_m_grouped_fp8_gemm_nt_contiguous(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                                         uint16_t* D, const int32_t* m_indices, int64_t M_total, int64_t N,
                                         int64_t K, int64_t G, void* workspace, size_t workspace_bytes,
                                         void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  int rc = check_nk(N, K);
-  if (rc) return rc;
-  if ((rc = check_rows(M_total, "M_total"))) return rc;
-  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
-  if (M_total == 0) return ok();
-  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
-  if (!m_indices) return fail(DG_ERR_INVALID_ARG, "null m_indices");
-  if (!aligned(m_indices, 4)) return fail(DG_ERR_ALIGN, "m_indices must be 4-byte aligned");
-  if ((rc = check_weights_and_scales(N, K, M_total, K / 128))) return rc;
-  // row chunks are multiples of 256 rows, so every aligned 128-row block
-  // stays inside one chunk
-  const int64_t chunk = launch_rows(K, 2 * N);
-  if (chunk == 0) return fail(DG_ERR_SHAPE, "rows do not fit 32-bit offsets");
-  int cus = 0;
-  if ((rc = check_device(&cus))) return rc;
-  const int ecus = effective_cus(cus);
-  for (int64_t r0 = 0; r0 < M_total; r0 += chunk) {
-    const int64_t rows = std::min(chunk, M_total - r0);
-    const ContigPlan cp = plan_contiguous(rows, N, K, ecus);
-    dg::GemmParams p{};
-    p.A = A + r0 * K;
-    p.sfa = sfa + r0;
-    p.sfa_ld = (int)M_total;
-    p.B = B;
-    p.sfb = sfb;
-    p.D = D + r0 * N;
-    p.index = m_indices + r0;
-    p.rows = rows;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.G = (int)G;
-    p.m_tiles = (int)ceil_div(rows, cp.wide ? 256 : 128);
-    p.n_tiles = (int)ceil_div(N, 256);
-    p.splits = 1;
-    p.kb_per_split = (int)(K / 128);
-    p.dp_tiles = (int)cp.tiles;  // every tile whole: no K-split tail, no workspace
-    p.sk_tiles = 0;
-    p.sk_pieces = 1;
-    p.sk_kb = (int)(K / 128);
-    if (print_configs())
-      std::fprintf(stderr, "[dg] contiguous M_total=%lld N=%lld K=%lld G=%lld rows=%lld+%lld tile=%dx256 kernel=%s grid=%d\n",
-                   (long long)M_total, (long long)N, (long long)K, (long long)G, (long long)r0, (long long)rows,
-                   cp.wide ? 256 : 128, cp.wide ? "wide" : "persistent", cp.grid);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = cp.wide ? dg::launch_gemm_wide(dg::kContiguous, cp.grid, p, st)
-                                 : dg::launch_gemm_persistent(dg::kContiguous, cp.grid, p, st);
-    if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  }
-  return ok();
+  return run_contiguous(false, A, sfa, B, sfb, D, m_indices, M_total, N, K, G, stream);
 }
+
+int dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B,
+                                              const int32_t* sfb, uint16_t* D, const int32_t* m_indices,
+                                              int64_t M_total, int64_t N, int64_t K, int64_t G, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return run_contiguous(true, A, sfa, B, sfb, D, m_indices, M_total, N, K, G, stream);
+}
+
 
 int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                                     uint16_t* D, const int32_t* masked_m, int64_t G, int64_t max_m, int64_t N,
@@ -658,47 +769,17 @@ int dg_m_grouped_fp8_gemm_nt_masked(const uint8_t* A, const float* sfa, const ui
   (void)workspace;
   (void)workspace_bytes;
   (void)expected_m;  // launch shape and results never depend on it
-  int rc = check_nk(N, K);
-  if (rc) return rc;
-  if (G < 1 || G > kMaxGroups) return fail(DG_ERR_SHAPE, "G must be in [1, 1024] (got %lld)", (long long)G);
-  if (max_m < 0) return fail(DG_ERR_SHAPE, "max_m must be >= 0");
-  if (max_m > ((int64_t)1 << 31) - 1) return fail(DG_ERR_SHAPE, "max_m too large");
-  if (max_m == 0) return ok();
-  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
-  if (!masked_m) return fail(DG_ERR_INVALID_ARG, "null masked_m");
-  if (!aligned(masked_m, 4)) return fail(DG_ERR_ALIGN, "masked_m must be 4-byte aligned");
-  // each expert's A, alpha, B and D are addressed from the expert's own base
-  if ((rc = check_weights_and_scales(N, K, max_m, K / 128))) return rc;
-  if ((max_m + 256) * K >= kOffLim || max_m * N * 2 >= kOffLim)
-    return fail(DG_ERR_SHAPE, "one expert's rows exceed 32-bit offsets (max_m = %lld)", (long long)max_m);
-  int cus = 0;
-  if ((rc = check_device(&cus))) return rc;
-  dg::GemmParams p{};
-  p.A = A;
-  p.sfa = sfa;
-  p.sfa_ld = (int)max_m;
-  p.B = B;
-  p.sfb = sfb;
-  p.D = D;
-  p.index = masked_m;
-  p.rows = max_m;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.G = (int)G;
-  // 128 x 256 tiles over a device-side task list
-  p.m_tiles = (int)ceil_div(max_m, 128);
-  p.n_tiles = (int)ceil_div(N, 256);
-  p.splits = 1;
-  p.kb_per_split = (int)(K / 128);
-  const int64_t tiles = G * p.m_tiles * p.n_tiles;
-  const int ecus = effective_cus(cus);
-  const int grid = (int)(tiles < ecus ? tiles : ecus);
-  if (print_configs())
-    std::fprintf(stderr, "[dg] masked G=%lld max_m=%lld N=%lld K=%lld tile=128x256 kernel=persistent grid=%d\n",
-                 (long long)G, (long long)max_m, (long long)N, (long long)K, grid);
-  const hipError_t e = dg::launch_gemm_persistent(dg::kMasked, grid, p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return run_masked(false, A, sfa, B, sfb, D, masked_m, G, max_m, N, K, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* A, const int32_t* sfa, const uint8_t* B, const int32_t* sfb,
+                                          uint16_t* D, const int32_t* masked_m, int64_t G, int64_t max_m, int64_t N,
+                                          int64_t K, int64_t expected_m, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)expected_m;
+  return run_masked(true, A, sfa, B, sfb, D, masked_m, G, max_m, N, K, stream);
 }
 
 int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K, void* stream) {

@@ -46,15 +46,35 @@ struct GemmParams {
 // D[g] = C[g] + A[:, seg g] . B[:, seg g]^T per group.
 // kDenseUe8m0: the dense schedule with UE8M0 scales packed four per int32
 // along K (sfa [ceil(KB/4)][rows], sfb [ceil(N/128)][ceil(KB/4)]), applied
-// by the matrix cores' block scaling.
-enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2, kDenseBf16 = 3, kDenseAcc = 4, kKGrouped = 5, kDenseUe8m0 = 6 };
+// by the matrix cores' block scaling; kContiguousUe8m0 / kMaskedUe8m0: the
+// M-grouped forms with those scales (sfb per expert; masked sfa
+// [G][ceil(KB/4)][max_m]).
+enum GemmMode {
+  kDense = 0,
+  kContiguous = 1,
+  kMasked = 2,
+  kDenseBf16 = 3,
+  kDenseAcc = 4,
+  kKGrouped = 5,
+  kDenseUe8m0 = 6,
+  kContiguousUe8m0 = 7,
+  kMaskedUe8m0 = 8
+};
+
+// Split-K workspace layout shared by the skinny and persistent kernels: the
+// first kWsCounterBytes hold one uint32 completion counter per split tile
+// (at most kWsMaxCounters), the fp32 partials follow.  The counters sit at a
+// fixed place, zero on entry and left zero by every launch, so one workspace
+// serves any sequence of shapes (partials of one call never land where
+// another call keeps its counters).
+constexpr int kWsMaxCounters = 1024;
+constexpr size_t kWsCounterBytes = 4 * kWsMaxCounters;
 
 // Enqueue the skinny dense kernel (gemm_skinny.hip, M <= 128, bm-row tiles
 // with bm in {64, 128}, wn in {16, 32} columns per wave, 4 waves):
 // p.m_tiles = ceil(M / bm), p.n_tiles = ceil(N / (4 wn)), p.splits K splits of
-// p.kb_per_split blocks.  With p.splits > 1, p.ws must hold
-// skinny_workspace_bytes(...) bytes: fp32 partials followed by one uint32
-// counter per tile that must be zero on entry (each call leaves them zero).
+// p.kb_per_split blocks.  With p.splits > 1 (then at most kWsMaxCounters
+// tiles), p.ws must hold skinny_workspace_bytes(...) bytes laid out as above.
 size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int splits);
 hipError_t launch_gemm_skinny(int bm, int wn, int depth, const GemmParams& p, hipStream_t stream);
 // K blocks in flight per wave (ring depth; LDS per slot is (bm + 4 wn) * 128 B
@@ -71,8 +91,8 @@ constexpr bool skinny_depth_ok(int bm, int wn, int d) {
 
 // Enqueue the persistent kernel (gemm_persist.hip) with `grid` workgroups (one
 // per CU): mode kDense over 256x128 tiles (tail tiles split along K when
-// p.sk_tiles > 0, p.ws then holds persistent_workspace_bytes(...) bytes whose
-// counters must be zero on entry and are left zero), kContiguous over 128x256
+// p.sk_tiles > 0, at most kWsMaxCounters of them; p.ws then holds
+// persistent_workspace_bytes(...) bytes laid out as above), kContiguous over 128x256
 // tiles (p.dp_tiles = all tiles, no split; at most kPersistentMaxContigTiles
 // tiles per workgroup), kMasked over 128x256 tiles (G <= 1024) or kKGrouped
 // over 256x128 tiles of every group (G <= 1024, no split).  One launch's A,

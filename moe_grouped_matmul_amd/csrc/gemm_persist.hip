@@ -47,8 +47,8 @@
 //     operands carry per-row scales: alpha as in the other forms, beta of the
 //     tile's 128 columns through a 6-slot LDS ring of its own.
 //
-// UE8M0 scales (dense): alpha and beta are powers of two given by their
-// exponent bytes, four K blocks per 32-bit word.  The matrix cores apply
+// UE8M0 scales (dense, contiguous and masked): alpha and beta are powers of
+// two given by their exponent bytes, four K blocks per 32-bit word.  The matrix cores apply
 // them (v_mfma_scale_f32_16x16x128_f8f6f4, every 32-K sub-block of a row
 // given the row's byte), which is exact, and the promotion is one fp32 add of
 // the scaled block product per element.  Letting the MFMA accumulate into
@@ -106,11 +106,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   constexpr bool ACC = MODE == kDenseAcc;    // fp32 output D = C + A . B^T
   constexpr bool KG = MODE == kKGrouped;     // groups along K, per-column beta, fp32 D[g] = C[g] + ...
   constexpr bool F32OUT = ACC || KG;
-  constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
+  // UE8M0 codes, applied by the matrix cores' block scaling (dense and the M-grouped forms)
+  constexpr bool UE = MODE == kDenseUe8m0 || MODE == kContiguousUe8m0 || MODE == kMaskedUe8m0;
+  // the schedule: dense, contiguous or masked (the UE8M0 grouped modes take those of their form)
+  constexpr int FORM = MODE == kContiguousUe8m0 ? kContiguous : (MODE == kMaskedUe8m0 ? kMasked : MODE);
   // 128-row tiles for the grouped forms: a contiguous 128-row block belongs to
   // one expert, and a masked expert's rows fill fewer padded MFMA rows
-  constexpr int WGM = MODE == kContiguous || MODE == kMasked ? 2 : 4;
-  constexpr int WGN = MODE == kContiguous || MODE == kMasked ? 4 : 2;
+  constexpr int WGM = FORM == kContiguous || FORM == kMasked ? 2 : 4;
+  constexpr int WGN = FORM == kContiguous || FORM == kMasked ? 4 : 2;
   constexpr int TM = 4;
   constexpr int TN = 4;
   constexpr int BM = WGM * 64;
@@ -131,12 +134,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[SLOT_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[SLOT_BYTES];
   // masked: active tiles before each group; K-grouped: first K block of each group
-  __shared__ int pref[MODE == kMasked || KG ? kMaxMaskedGroups + 1 : 1];
-  __shared__ int mmv[MODE == kMasked ? kMaxMaskedGroups : 1];       // masked_m clamped to [0, max_m]
+  __shared__ int pref[FORM == kMasked || KG ? kMaxMaskedGroups + 1 : 1];
+  __shared__ int mmv[FORM == kMasked ? kMaxMaskedGroups : 1];       // masked_m clamped to [0, max_m]
   // contiguous: expert of each of this workgroup's tiles (-1: none) and the
   // mask of its rows tagged with that expert
-  __shared__ int seg_exp[MODE == kContiguous ? kMaxContigSegs : 1];
-  __shared__ uint32_t seg_mask[MODE == kContiguous ? kMaxContigSegs : 1][4];
+  __shared__ int seg_exp[FORM == kContiguous ? kMaxContigSegs : 1];
+  __shared__ uint32_t seg_mask[FORM == kContiguous ? kMaxContigSegs : 1][4];
   __shared__ int last_piece;
   // K-grouped: beta of the tile's BN columns, slot j % 6 for iteration j (the
   // loads of iteration j + 3 go to another slot than the reads of iteration j)
@@ -157,12 +160,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   const int KW = (KB + 3) >> 2;  // UE8M0: packed words (four K blocks) per scale row
   const int NB = (N + 127) >> 7;
   const int rows = (int)p.rows;  // dense: M; masked: max_m
-  const int ngrp = MODE == kMasked ? p.G : 1;         // groups of A, alpha and D rows
-  const int nbgrp = MODE == kContiguous || MODE == kMasked ? p.G : 1;  // groups of B and beta
+  const int ngrp = FORM == kMasked ? p.G : 1;         // groups of A, alpha and D rows
+  const int nbgrp = FORM == kContiguous || FORM == kMasked ? p.G : 1;  // groups of B and beta
 
   // ---- task list
   int T;  // tasks: dense tiles / active masked tiles
-  if (MODE == kMasked) {
+  if (FORM == kMasked) {
     if (wave == 0) {
       int carry = 0;
       for (int base = 0; base < ngrp; base += 64) {
@@ -214,14 +217,14 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   } else {
     T = p.m_tiles * p.n_tiles;
   }
-  const int dp_tiles = MODE == kMasked || KG ? T : p.dp_tiles;  // tasks run as whole tiles
+  const int dp_tiles = FORM == kMasked || KG ? T : p.dp_tiles;  // tasks run as whole tiles
   const int P = p.sk_pieces;                               // pieces per tail tile (dense)
   const int n_dp = b < dp_tiles ? (dp_tiles - b + G - 1) / G : 0;
-  const bool has_tail = (MODE == kDense || BF16 || ACC || UE) && b < p.sk_tiles * P;
+  const bool has_tail = (MODE == kDense || BF16 || ACC || MODE == kDenseUe8m0) && b < p.sk_tiles * P;
   const int nseg = n_dp + (has_tail ? 1 : 0);
   if (nseg == 0) return;  // uniform over the workgroup
 
-  if constexpr (MODE == kContiguous) {
+  if constexpr (FORM == kContiguous) {
     // expert and tagged-row mask of each of this workgroup's tiles (the host
     // keeps nseg <= kMaxContigSegs); one wave per tile, two rows per lane
     for (int s = wave; s < nseg; s += NWAVES) {
@@ -270,7 +273,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
       r.kb_lo = r.piece * p.sk_kb;
       r.kb_hi = r.kb_lo + p.sk_kb < KB ? r.kb_lo + p.sk_kb : KB;
     }
-    if (MODE == kMasked) {
+    if (FORM == kMasked) {
       // round s of one task per workgroup, XCD-contiguous inside the round;
       // inside a group the row tiles of one column tile are adjacent tasks,
       // so they run together on one XCD and share that B tile in its L2
@@ -308,7 +311,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     } else {
       grouped_mn(xcd_tile(d, T), p.m_tiles, p.n_tiles, GM, &r.mt, &r.nt);
       r.row_limit = rows - r.mt * BM < BM ? rows - r.mt * BM : BM;
-      if (MODE == kContiguous) {
+      if (FORM == kContiguous) {
         const int e = __builtin_amdgcn_readfirstlane(seg_exp[s]);
         r.bgrp = e < 0 ? 0 : e;
         if (e < 0) r.row_limit = 0;  // no row tagged with an expert: nothing loaded or stored
@@ -369,7 +372,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   auto is_setup = [&]() {
     const int agrp = KG ? 0 : is_t.grp;  // K-grouped: A and alpha are shared by all groups
     is_aptr = p.A + (size_t)agrp * (size_t)rows * (size_t)K;
-    is_sptr = p.sfa + (size_t)agrp * (size_t)KB * (size_t)rows;
+    is_sptr = p.sfa + (size_t)agrp * (size_t)(UE ? KW : KB) * (size_t)rows;
     is_bptr = p.B + (size_t)is_t.bgrp * (size_t)N * (size_t)K;
     const int arow = is_t.mt * BM;
     const int brow = is_t.nt * BN;
@@ -489,7 +492,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     st_col0 = cp_t.nt * BN;                                                                                \
     st_rows = cp_t.row_limit;                                                                              \
     st_grp = cp_t.grp;                                                                                     \
-    if (MODE == kContiguous) {                                                                             \
+    if (FORM == kContiguous) {                                                                             \
       _Pragma("unroll") for (int w_ = 0; w_ < 4; ++w_) st_m[w_] = __builtin_amdgcn_readfirstlane(seg_mask[cp_seg][w_]); \
     }                                                                                                      \
   } while (0)
@@ -497,7 +500,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   ([&]() -> uint32_t {                                                                                     \
     const int gc0_ = st_col0 + wn * 64 + q * 16;                                                           \
     const int r_ = wm * 64 + (i_) * 16 + q16;                                                              \
-    const bool tag_ = MODE != kContiguous || ((st_m[r_ >> 5] >> (r_ & 31)) & 1u);                          \
+    const bool tag_ = FORM != kContiguous || ((st_m[r_ >> 5] >> (r_ & 31)) & 1u);                          \
     return (r_ < st_rows && gc0_ < N && tag_) ? ((uint32_t)(st_row0 + r_) * (uint32_t)N + gc0_) * 2u : kOOB; \
   }())
   // Accumulating forms: fp32 outputs, 64 bytes per lane and row tile (byte
@@ -527,7 +530,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
                                                  o_[i_] + 16u * j_, 0, 0);                                 \
     } else {                                                                                               \
       const __amdgpu_buffer_rsrc_t rdm_ =                                                                  \
-          MODE == kMasked ? make_rsrc(p.D + (size_t)st_grp * (size_t)rows * (size_t)N, (uint32_t)rows * (uint32_t)N * 2u) : rd; \
+          FORM == kMasked ? make_rsrc(p.D + (size_t)st_grp * (size_t)rows * (size_t)N, (uint32_t)rows * (uint32_t)N * 2u) : rd; \
       _Pragma("unroll") for (int i_ = 0; i_ < TM; ++i_) {                                                  \
         const uint32_t off_ = PS_OUT_OFF(i_);                                                              \
         uint32_t w_[8];                                                                                    \
@@ -748,11 +751,23 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
   if (has_tail) {
     // K-split tail tile: fp32 partial in fragment order (piece pc of tail
     // tile s, wave w, fragment (i, j), lane l at byte
-    // (((s * P + pc) * 8 + w) * 16 + i * 4 + j) * 1024 + 16 l), coherent stores;
-    // the last piece sums all pieces' partials in piece order
+    // (((s * P + pc) * 8 + w) * 16 + i * 4 + j) * 1024 + 16 l after the
+    // counter area); the last piece sums all pieces' partials in piece order.
+    // Ordering: the partial stores and loads carry sc1 -- the compiler's
+    // lowering of relaxed agent-scope atomic stores and loads on gfx950 -- so
+    // they are coherent across the XCDs' L2 caches.  Every wave waits
+    // (vmcnt(0)) until its stores are acknowledged at that coherence point,
+    // the barrier then orders all of them before the relaxed counter
+    // increment, and the last piece issues its loads only after its own
+    // increment has returned (so after every other piece's increment, which
+    // followed that piece's acknowledged stores).  An agent-scope release /
+    // acquire would add an L2 write-back / invalidate, needed only for data
+    // cached non-coherently, which these accesses never are.
     const uint32_t frag_bytes = (uint32_t)TM * TN * 1024u;
     const uint32_t tile_bytes = (uint32_t)NWAVES * frag_bytes;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws, (uint32_t)p.sk_tiles * (uint32_t)P * tile_bytes);
+    // counters at the workspace start, partials after them
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(reinterpret_cast<uint8_t*>(p.ws) + kWsCounterBytes, (uint32_t)p.sk_tiles * (uint32_t)P * tile_bytes);
     const uint32_t w_off = (uint32_t)(cp_t.tail * P) * tile_bytes + (uint32_t)wave * frag_bytes + (uint32_t)lane * 16u;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -763,8 +778,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
                                                (uint32_t)cp_t.piece * tile_bytes, kCoherent);
     wait_vmcnt<0>();
     __syncthreads();
-    unsigned int* counters = reinterpret_cast<unsigned int*>(reinterpret_cast<uint8_t*>(p.ws) +
-                                                             (size_t)p.sk_tiles * P * tile_bytes);
+    unsigned int* counters = reinterpret_cast<unsigned int*>(p.ws);
     if (tid == 0)
       last_piece = __hip_atomic_fetch_add(&counters[cp_t.tail], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned int)(P - 1);
@@ -807,8 +821,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
 
 size_t persistent_workspace_bytes(int sk_tiles, int sk_pieces) {
   if (sk_tiles <= 0 || sk_pieces <= 1) return 0;
-  // fp32 partials of 256 x 128 tiles, then one uint32 counter per tail tile
-  return (size_t)sk_tiles * sk_pieces * 256 * 128 * 4 + (size_t)sk_tiles * 4;
+  // the counter area, then fp32 partials of 256 x 128 tiles
+  return kWsCounterBytes + (size_t)sk_tiles * sk_pieces * 256 * 128 * 4;
 }
 
 hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipStream_t stream) {
@@ -831,6 +845,10 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous, false>), g, t, 0, stream, p);
   else if (mode == kDenseUe8m0)
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseUe8m0, false>), g, t, 0, stream, p);
+  else if (mode == kContiguousUe8m0)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguousUe8m0, false>), g, t, 0, stream, p);
+  else if (mode == kMaskedUe8m0)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMaskedUe8m0, false>), g, t, 0, stream, p);
   else
     hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense, false>), g, t, 0, stream, p);
   return hipGetLastError();

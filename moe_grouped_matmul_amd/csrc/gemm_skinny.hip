@@ -278,14 +278,21 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
     // Split K.  Partial of this split in fragment order: for split s, tile
     // (mt, nt) and wave w, fragment (i, j) of lane l sits at float offset
     // ((((s * m_tiles + mt) * n_tiles + nt) * 4 + w) * TM * TN + i * TN + j) * 256 + 4 l.
-    // Stores and loads are coherent across XCDs (sc1); each wave waits for its
-    // stores before the barrier that precedes the counter increment, and the
-    // last split reads the partials only after its increment has returned.
+    // Ordering (the same argument as the persistent kernel's tail pieces):
+    // the partial stores and loads carry sc1, which is how the compiler lowers
+    // relaxed agent-scope atomic stores and loads on gfx950, so each access
+    // is coherent across the XCDs' L2 caches.  Each wave waits (vmcnt(0))
+    // until its sc1 stores are acknowledged at that coherence point before
+    // the barrier that precedes the relaxed counter increment; the last split
+    // issues its sc1 loads only after its increment has returned.  The
+    // write-back / invalidate of the L2 that an agent-scope release / acquire
+    // adds concern data cached non-coherently, which these accesses never are.
     const int tiles = p.m_tiles * p.n_tiles;
     const int tile = mt * p.n_tiles + nt;
     const uint32_t frag_bytes = (uint32_t)TM * TN * 1024u;  // one wave's fragments
     const uint32_t split_bytes = (uint32_t)tiles * NW * frag_bytes;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.ws, (uint32_t)S * split_bytes);
+    // counters at the workspace start, partials after them
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<uint8_t*>(p.ws) + kWsCounterBytes, (uint32_t)S * split_bytes);
     const uint32_t w_off = ((uint32_t)tile * NW + wave) * frag_bytes + (uint32_t)lane * 16u;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -296,8 +303,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
                                                kCoherent);
     wait_vmcnt<0>();
     __syncthreads();
-    unsigned int* counters = reinterpret_cast<unsigned int*>(reinterpret_cast<uint8_t*>(p.ws) +
-                                                             (size_t)S * split_bytes);
+    unsigned int* counters = reinterpret_cast<unsigned int*>(p.ws);
     if (tid == 0)
       last_split = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned int)(S - 1);
@@ -406,8 +412,8 @@ hipError_t launch_skinny_cfg(const GemmParams& p, hipStream_t stream) {
 
 size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int splits) {
   if (splits <= 1) return 0;
-  // fp32 partials of bm x 4wn tiles, then one uint32 counter per tile
-  return (size_t)splits * m_tiles * n_tiles * bm * 4 * wn * 4 + (size_t)m_tiles * n_tiles * 4;
+  // the counter area, then fp32 partials of bm x 4wn tiles
+  return kWsCounterBytes + (size_t)splits * m_tiles * n_tiles * bm * 4 * wn * 4;
 }
 
 hipError_t launch_gemm_skinny(int bm, int wn, int depth, const GemmParams& p, hipStream_t stream) {

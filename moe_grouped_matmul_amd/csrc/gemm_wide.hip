@@ -28,8 +28,9 @@
 // contiguous, m-grouped range of tiles.  No K split: used where the tiles
 // fill the CUs in whole or nearly whole rounds.
 //
-// UE8M0 scales (dense): alpha and beta are powers of two given by their
-// exponent bytes, four K blocks per 32-bit word (as in gemm_persist.hip).
+// UE8M0 scales (dense and contiguous): alpha and beta are powers of two given
+// by their exponent bytes, four K blocks per 32-bit word (as in
+// gemm_persist.hip).
 // The matrix cores apply them (v_mfma_scale_f32_16x16x128_f8f6f4: beta's byte
 // for the B operand, each row's alpha byte for the A operand), which is exact,
 // and the promotion is one fp32 add of the scaled block product.
@@ -89,13 +90,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void* p, uint3
 template <int MODE, bool HASC>
 __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0 || MODE == kDenseBf16 ||
-                    MODE == kDenseAcc || MODE == kKGrouped,
+  static_assert(MODE == kDense || MODE == kContiguous || MODE == kDenseUe8m0 || MODE == kContiguousUe8m0 ||
+                    MODE == kDenseBf16 || MODE == kDenseAcc || MODE == kKGrouped,
                 "modes of the wide kernel");
   constexpr bool KG = MODE == kKGrouped;     // groups along K, per-column beta, fp32 D[g] = C[g] + ...
   constexpr bool ACC = MODE == kDenseAcc || KG;  // fp32 output D = C + A . B^T
-  constexpr bool CONTIG = MODE == kContiguous;
-  constexpr bool UE = MODE == kDenseUe8m0;   // UE8M0 codes, applied by the matrix cores' block scaling
+  constexpr bool CONTIG = MODE == kContiguous || MODE == kContiguousUe8m0;
+  // UE8M0 codes, applied by the matrix cores' block scaling (dense and contiguous)
+  constexpr bool UE = MODE == kDenseUe8m0 || MODE == kContiguousUe8m0;
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
   constexpr int MAXT = kWideMaxContigTiles;  // tiles per workgroup the contiguous pass table holds
   constexpr int WGN = 2;
@@ -620,6 +622,8 @@ hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t
   if (grid <= 0) return hipSuccess;
   if (mode == kContiguous)
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguous, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+  else if (mode == kContiguousUe8m0)
+    hipLaunchKernelGGL((fp8_gemm_wide_kernel<kContiguousUe8m0, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseUe8m0)
     hipLaunchKernelGGL((fp8_gemm_wide_kernel<kDenseUe8m0, false>), dim3((unsigned)grid), dim3(512), 0, stream, p);
   else if (mode == kDenseBf16)

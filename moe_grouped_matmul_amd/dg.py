@@ -43,6 +43,8 @@ EXPORTED = (
     "dg_quant_1x128_ue8m0",
     "dg_quant_128x128_ue8m0",
     "dg_fp8_gemm_nt_ue8m0",
+    "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+    "dg_m_grouped_fp8_gemm_nt_masked_ue8m0",
     "dg_get_workspace_size",
     "dg_describe_plan",
     "dg_get_m_alignment_for_contiguous_layout",
@@ -80,6 +82,8 @@ def load_library():
     lib.dg_fp8_gemm_nt_acc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, SZ, P]
+    lib.dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
+    lib.dg_m_grouped_fp8_gemm_nt_masked_ue8m0.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P, SZ, P]
     lib.dg_k_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
     lib.dg_quant_1x128.argtypes = [P, P, P, I64, I64, I64, P]
     lib.dg_quant_128x128.argtypes = [P, P, P, I64, I64, I64, P]
@@ -97,7 +101,8 @@ def load_library():
     lib.dg_version.restype = ctypes.c_char_p
     for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
                  "dg_k_grouped_fp8_gemm_nt_contiguous", "dg_quant_1x128", "dg_quant_1x128_ue8m0",
-                 "dg_quant_128x128_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
+                 "dg_quant_128x128_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
+                 "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
                  "dg_get_m_alignment_for_contiguous_layout"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -412,3 +417,48 @@ def dg_fp8_gemm_nt_ue8m0(A, sfa, B, sfb, D, workspace=None, stream=None):
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().dg_fp8_gemm_nt_ue8m0(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), M, N, K,
                                                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(A, sfa, B, sfb, D, m_indices, stream=None):
+    """M-grouped contiguous with packed UE8M0 scales: A [M_total,K], sfa [ceil(K/512),M_total] int32,
+    B [G,N,K], sfb [G,ceil(N/128),ceil(K/512)] int32, D [M_total,N] bf16, m_indices [M_total] int32."""
+    A = _bytes_view(A, "A")
+    B = _bytes_view(B, "B")
+    D = _bf16_out(D)
+    _need(A, "A", torch.uint8, 2)
+    _need(B, "B", torch.uint8, 3)
+    _need(sfa, "sfa", torch.int32, 2)
+    _need(sfb, "sfb", torch.int32, 3)
+    _need(D, "D", D.dtype, 2)
+    _need(m_indices, "m_indices", torch.int32, 1)
+    M_total, K = A.shape
+    G, N, _ = B.shape
+    if B.shape[2] != K or tuple(sfa.shape) != (_kw(K), M_total) or tuple(sfb.shape) != (G, (N + 127) // 128, _kw(K)) \
+            or tuple(D.shape) != (M_total, N) or m_indices.shape[0] != M_total:
+        raise ValueError("shape mismatch between A, sfa, B, sfb, D, m_indices")
+    _check(load_library().dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(
+        _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), _ptr(m_indices), M_total, N, K, G,
+        ctypes.c_void_p(0), 0, _stream(stream)))
+
+
+def dg_m_grouped_fp8_gemm_nt_masked_ue8m0(A, sfa, B, sfb, D, masked_m, expected_m=0, stream=None):
+    """M-grouped masked with packed UE8M0 scales: A [G,max_m,K], sfa [G,ceil(K/512),max_m] int32,
+    B [G,N,K], sfb [G,ceil(N/128),ceil(K/512)] int32, D [G,max_m,N] bf16, masked_m [G] int32."""
+    A = _bytes_view(A, "A")
+    B = _bytes_view(B, "B")
+    D = _bf16_out(D)
+    _need(A, "A", torch.uint8, 3)
+    _need(B, "B", torch.uint8, 3)
+    _need(sfa, "sfa", torch.int32, 3)
+    _need(sfb, "sfb", torch.int32, 3)
+    _need(D, "D", D.dtype, 3)
+    _need(masked_m, "masked_m", torch.int32, 1)
+    G, max_m, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != G or B.shape[2] != K or tuple(sfa.shape) != (G, _kw(K), max_m) \
+            or tuple(sfb.shape) != (G, (N + 127) // 128, _kw(K)) or tuple(D.shape) != (G, max_m, N) \
+            or masked_m.shape[0] != G:
+        raise ValueError("shape mismatch between A, sfa, B, sfb, D, masked_m")
+    _check(load_library().dg_m_grouped_fp8_gemm_nt_masked_ue8m0(
+        _ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), _ptr(masked_m), G, max_m, N, K, int(expected_m),
+        ctypes.c_void_p(0), 0, _stream(stream)))

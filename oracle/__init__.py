@@ -36,7 +36,13 @@ from .bf16 import bf16_rne_bits, bf16_bits_to_f64
 from .quant import quant_1x128, quant_128x128
 from .gemm_bf16 import gemm_bf16_nt
 from .gemm_kgrouped import k_grouped_contiguous
-from .ue8m0 import gemm_nt_ue8m0, quant_1x128_ue8m0, quant_128x128_ue8m0
+from .ue8m0 import (
+    gemm_nt_ue8m0,
+    grouped_contiguous_ue8m0,
+    grouped_masked_ue8m0,
+    quant_1x128_ue8m0,
+    quant_128x128_ue8m0,
+)
 from .gemm import (
     gemm_nt_acc,
     gemm_nt,
@@ -63,4 +69,6 @@ __all__ = [
     "quant_1x128_ue8m0",
     "quant_128x128_ue8m0",
     "gemm_nt_ue8m0",
+    "grouped_contiguous_ue8m0",
+    "grouped_masked_ue8m0",
 ]

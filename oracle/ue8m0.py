@@ -30,7 +30,7 @@ Readings where the pages are silent:
 import numpy as np
 
 from .e4m3 import E4M3_MAX, encode_e4m3
-from .gemm import gemm_nt
+from .gemm import gemm_nt, grouped_contiguous, grouped_masked
 
 
 def ue8m0_code(amax) -> np.ndarray:
@@ -125,3 +125,30 @@ def gemm_nt_ue8m0(a_codes, sfa_packed, b_codes, sfb_packed) -> np.ndarray:
     if sfa.shape != (kb, M) or sfb.shape != ((N + 127) // 128, kb):
         raise ValueError("scale tensor shape mismatch")
     return gemm_nt(a_codes, sfa, b_codes, sfb)
+
+
+def _decode_act(sfa_packed, kb):
+    """Packed activation codes [..., W, rows] -> fp32 powers of two [..., kb, rows]."""
+    w = np.asarray(sfa_packed)
+    return ue8m0_value(np.swapaxes(unpack_k(np.swapaxes(w, -1, -2), kb), -1, -2))
+
+
+def grouped_contiguous_ue8m0(a_codes, sfa_packed, b_codes, sfb_packed, m_indices, d_init) -> np.ndarray:
+    """M-grouped contiguous layout with UE8M0 scales (Lesson 13, Fig. 13-3;
+    deep-dive blog, section 3: the grouped GEMMs take the same scale formats):
+    sfa_packed int32 [ceil(KB/4), M_total], sfb_packed int32 [G, ceil(N/128),
+    ceil(KB/4)]; the codes decoded to their powers of two and the fp32-scale
+    grouped definition applied (rows with an index outside [0, G) untouched)."""
+    kb = np.asarray(a_codes).shape[1] // 128
+    return grouped_contiguous(a_codes, _decode_act(sfa_packed, kb), b_codes,
+                              ue8m0_value(unpack_k(np.asarray(sfb_packed), kb)), m_indices, d_init)
+
+
+def grouped_masked_ue8m0(a_codes, sfa_packed, b_codes, sfb_packed, masked_m, d_init) -> np.ndarray:
+    """M-grouped masked layout with UE8M0 scales: sfa_packed int32
+    [G, ceil(KB/4), max_m], sfb_packed int32 [G, ceil(N/128), ceil(KB/4)];
+    decoded, then the fp32-scale masked definition (rows at or past
+    clamp(masked_m[g], 0, max_m) untouched)."""
+    kb = np.asarray(a_codes).shape[2] // 128
+    return grouped_masked(a_codes, _decode_act(sfa_packed, kb), b_codes,
+                          ue8m0_value(unpack_k(np.asarray(sfb_packed), kb)), masked_m, d_init)

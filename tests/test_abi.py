@@ -149,11 +149,11 @@ def test_utilities(lib):
     # dense small-M shapes ask for split-K scratch; large ones only when the
     # 256 x 128 tiles they run leave a partial last round on the (default 256)
     # CUs, whose tail tiles are then split along K: 4096x2112 -> 16 x 17 = 272
-    # tiles, 16 tail tiles in 4 pieces of 256x128 fp32 partials + one counter
-    # each; 256 x 256 tiles (4096x7168, 4096x4096) need none
+    # tiles, 16 tail tiles in 4 pieces of 256x128 fp32 partials after the
+    # 4 KiB counter area; 256 x 256 tiles (4096x7168, 4096x4096) need none
     assert lib.dg_get_workspace_size(0, 64, 2112, 7168, 1) > 0
     assert lib.dg_set_num_cus(256) == 0  # the MI355X count, also when no device is visible
-    assert lib.dg_get_workspace_size(0, 4096, 2112, 7168, 1) == 16 * 4 * 256 * 128 * 4 + 16 * 4
+    assert lib.dg_get_workspace_size(0, 4096, 2112, 7168, 1) == 4096 + 16 * 4 * 256 * 128 * 4
     assert lib.dg_get_workspace_size(0, 4096, 7168, 16384, 1) == 0
     assert lib.dg_get_workspace_size(0, 4096, 4096, 7168, 1) == 0  # 256 x 256 tiles: whole rounds
     assert lib.dg_set_num_cus(0) == 0

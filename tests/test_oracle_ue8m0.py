@@ -111,3 +111,66 @@ def test_planted_mistakes_are_caught(mistake):
         rev = (c[:, 3].astype(np.uint32) | (c[:, 2].astype(np.uint32) << 8) | (c[:, 1].astype(np.uint32) << 16)
                | (c[:, 0].astype(np.uint32) << 24))
         assert rev[0] != pack_k(c).view(np.uint32)[0, 0]
+
+
+# ---- grouped forms with UE8M0 scales: every computed row equals the exact
+# rational GEMM of its expert (decoded powers of two), every other row keeps
+# its prior contents; a planted mistake (the first expert's weight codes used
+# for every expert) is caught
+
+def _grouped_case(rng, G, N, K):
+    from oracle.ue8m0 import quant_128x128_ue8m0 as qw
+
+    b = [qw((rng.standard_normal((N, K)) / 8 * 2.0 ** rng.integers(-3, 4)).astype(np.float32)) for _ in range(G)]
+    qb = np.stack([x[0] for x in b])
+    cb = np.stack([x[1] for x in b])
+    pb = np.stack([x[2] for x in b])
+    return qb, cb, pb
+
+
+def test_grouped_contiguous_ue8m0_equals_exact_rational_per_expert():
+    from oracle import grouped_contiguous_ue8m0
+
+    rng = np.random.default_rng(21)
+    G, N, K = 3, 16, 640
+    counts = [2, 0, 3]
+    idx = np.array([0, 0, -1, 2, 2, 2, 7], np.int32)  # -1 and 7: untouched
+    a32 = (rng.standard_normal((len(idx), K)) * 2.0 ** rng.integers(-4, 5, (len(idx), 1))).astype(np.float32)
+    qa, ca, pa = quant_1x128_ue8m0(a32)
+    qb, cb, pb = _grouped_case(rng, G, N, K)
+    init = rng.integers(0, 1 << 16, (len(idx), N)).astype(np.uint16)
+    got = grouped_contiguous_ue8m0(qa, pa, qb, pb, idx, init)
+    for r, e in enumerate(idx):
+        if 0 <= e < G:
+            _, ref = gemm_nt_exact(qa[r:r + 1], ue8m0_value(ca[:, r:r + 1]), qb[e], ue8m0_value(cb[e]))
+            assert np.array_equal(got[r:r + 1], ref), r
+        else:
+            assert np.array_equal(got[r], init[r])
+    assert sum(counts) == int(np.sum((idx >= 0) & (idx < G)))
+    # planted mistake: expert 0's weight codes for every expert
+    wrong = grouped_contiguous_ue8m0(qa, pa, qb, np.broadcast_to(pb[:1], pb.shape), idx, init)
+    assert not np.array_equal(wrong, got)
+
+
+def test_grouped_masked_ue8m0_equals_exact_rational_per_expert():
+    from oracle import grouped_masked_ue8m0
+
+    rng = np.random.default_rng(22)
+    G, max_m, N, K = 3, 4, 16, 512
+    mm = np.array([4, -2, 9], np.int32)  # clamped to 4, 0, 4
+    a32 = (rng.standard_normal((G * max_m, K)) * 2.0 ** rng.integers(-4, 5, (G * max_m, 1))).astype(np.float32)
+    qa, ca, pa = quant_1x128_ue8m0(a32)
+    qa = qa.reshape(G, max_m, K)
+    ca = np.ascontiguousarray(ca.reshape(K // 128, G, max_m).transpose(1, 0, 2))
+    pa = np.ascontiguousarray(pa.reshape(pa.shape[0], G, max_m).transpose(1, 0, 2))
+    qb, cb, pb = _grouped_case(rng, G, N, K)
+    init = rng.integers(0, 1 << 16, (G, max_m, N)).astype(np.uint16)
+    got = grouped_masked_ue8m0(qa, pa, qb, pb, mm, init)
+    for g in range(G):
+        m = min(max(int(mm[g]), 0), max_m)
+        if m:
+            _, ref = gemm_nt_exact(qa[g, :m], ue8m0_value(ca[g][:, :m]), qb[g], ue8m0_value(cb[g]))
+            assert np.array_equal(got[g, :m], ref)
+        assert np.array_equal(got[g, m:], init[g, m:])
+    wrong = grouped_masked_ue8m0(qa, pa, qb, np.broadcast_to(pb[:1], pb.shape), mm, init)
+    assert not np.array_equal(wrong, got)
