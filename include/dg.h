@@ -102,6 +102,23 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
                    size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free dense GEMM, for callers that cannot allocate (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * dg_fp8_gemm_nt with no workspace argument.  Same operands, result and plan
+ * as dg_fp8_gemm_nt given a workspace of dg_get_workspace_size(DG_OP_GEMM_NT,
+ * M, N, K, 1) bytes (so the outputs are bit-identical); the K-split partials
+ * and counters live in a static device array of 40 MiB that every GPU the
+ * library runs on holds until the process ends.  Shapes whose split-K scratch
+ * would exceed 40 MiB return DG_ERR_WORKSPACE (none does under the default
+ * plans on 256 CUs).  Nothing is allocated; the first call on a device
+ * resolves the array's address and clears its counter area with a small
+ * kernel on `stream`.  Calls that overlap on one GPU (other streams, other
+ * threads, concurrent graph replays) share the array and race: order them.
+ */
+int dg_fp8_gemm_nt_noalloc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
+                           uint16_t* D, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * M-grouped contiguous GEMM (MoE training forward / prefill).  Lesson 13,
  * Fig. 13-3 (contiguous layout); deep-dive blog section 3 (grouped API table,
  * per-expert segments aligned to the M block).

@@ -21,7 +21,7 @@ LIB_NAME = "libdg_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "gemm_skinny.hip", "gemm_persist.hip", "gemm_wide.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm_skinny.hip", "gemm_persist.hip", "gemm_wide.hip", "noalloc.hip", "api.cpp"]
 # per-source flags: the persistent kernels need the iterative ILP scheduler to
 # stay within 256 VGPRs (two waves per SIMD) without spilling
 SOURCE_FLAGS = {"gemm_persist.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],

@@ -641,6 +641,38 @@ int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const f
   return run_dense(kFp8, A, sfa, B, sfb, nullptr, D, M, N, K, workspace, workspace_bytes, stream);
 }
 
+int dg_fp8_gemm_nt_noalloc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, uint16_t* D,
+                           int64_t M, int64_t N, int64_t K, void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if ((rc = check_rows(M, "M"))) return rc;
+  if (M == 0) return ok();
+  if ((rc = check_operands(A, sfa, B, sfb, D))) return rc;
+  if ((rc = check_weights_and_scales(N, K, M, K / 128))) return rc;
+  const int64_t chunk = launch_rows(K, 2 * N);
+  if (chunk == 0) return fail(DG_ERR_SHAPE, "rows of %lld bytes do not fit 32-bit offsets", (long long)K);
+  int cus = 0;
+  if ((rc = check_device(&cus))) return rc;
+  // the plan dg_fp8_gemm_nt makes with a full workspace; every row chunk's
+  // split-K scratch must fit the static array
+  const int ecus = effective_cus(cus);
+  for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+    const DensePlan pl = plan_dense(kFp8, std::min(chunk, M - r0), N, K, ecus, (size_t)-1);
+    const size_t need = pl.skinny ? dg::skinny_workspace_bytes(pl.cfg, pl.m_tiles, pl.n_tiles, pl.wn, pl.splits)
+                        : (pl.persist && !pl.wide) ? dg::persistent_workspace_bytes(pl.sk_tiles, pl.sk_pieces)
+                                                   : 0;
+    if (need > dg::kScratchBytes)
+      return fail(DG_ERR_WORKSPACE,
+                  "this shape's split-K scratch (%zu bytes) exceeds the static maximum of %zu bytes; "
+                  "use dg_fp8_gemm_nt with a workspace",
+                  need, dg::kScratchBytes);
+  }
+  void* scratch = nullptr;
+  const hipError_t e = dg::scratch_for_current_device(&scratch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "static scratch unavailable: %s", hipGetErrorString(e));
+  return run_dense(kFp8, A, sfa, B, sfb, nullptr, D, M, N, K, scratch, dg::kScratchBytes, stream);
+}
+
 int dg_fp8_gemm_nt_acc(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb, const float* C,
                        float* D, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                        void* stream) {

@@ -110,6 +110,14 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
 constexpr int kWideMaxContigTiles = 64;
 hipError_t launch_gemm_wide(int mode, int grid, const GemmParams& p, hipStream_t stream);
 
+// Static split-K scratch of dg_fp8_gemm_nt_noalloc (noalloc.hip): one array
+// of kScratchBytes per device, laid out as a workspace (counters first).
+// scratch_for_current_device returns its device address for the current
+// device (resolved once per device; the first call also clears the counter
+// area with a fill kernel on `stream`).
+constexpr size_t kScratchBytes = (size_t)40 << 20;
+hipError_t scratch_for_current_device(void** out, hipStream_t stream);
+
 // ue8m0: scales as packed UE8M0 codes (int32 words of four K blocks) instead of fp32
 hipError_t launch_quant_1x128(const float* x, uint8_t* q, void* sfa, int64_t G, int64_t M, int64_t K, bool ue8m0,
                               hipStream_t stream);

@@ -33,6 +33,7 @@ DG_OP_K_GROUPED = 5
 
 EXPORTED = (
     "dg_fp8_gemm_nt",
+    "dg_fp8_gemm_nt_noalloc",
     "dg_fp8_gemm_nt_acc",
     "dg_bf16_gemm_nt",
     "dg_m_grouped_fp8_gemm_nt_contiguous",
@@ -78,6 +79,7 @@ def load_library():
     lib = ctypes.CDLL(p)
     P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     lib.dg_fp8_gemm_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
+    lib.dg_fp8_gemm_nt_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.dg_bf16_gemm_nt.argtypes = [P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_fp8_gemm_nt_acc.argtypes = [P, P, P, P, P, P, I64, I64, I64, P, SZ, P]
     lib.dg_m_grouped_fp8_gemm_nt_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
@@ -99,7 +101,7 @@ def load_library():
     lib.dg_get_num_cus.argtypes = []
     lib.dg_get_last_error.restype = ctypes.c_char_p
     lib.dg_version.restype = ctypes.c_char_p
-    for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_acc", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
+    for name in ("dg_fp8_gemm_nt", "dg_fp8_gemm_nt_noalloc", "dg_fp8_gemm_nt_acc", "dg_bf16_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
                  "dg_k_grouped_fp8_gemm_nt_contiguous", "dg_quant_1x128", "dg_quant_1x128_ue8m0",
                  "dg_quant_128x128_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0",
                  "dg_m_grouped_fp8_gemm_nt_masked_ue8m0", "dg_quant_128x128", "dg_set_num_cus", "dg_get_num_cus",
@@ -201,6 +203,26 @@ def dg_fp8_gemm_nt(A, sfa, B, sfb, D, workspace=None, stream=None):
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().dg_fp8_gemm_nt(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), M, N, K,
                                          _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dg_fp8_gemm_nt_noalloc(A, sfa, B, sfb, D, stream=None):
+    """dg_fp8_gemm_nt without a workspace argument: the split-K scratch is the
+    library's static per-device array (calls that overlap on one GPU race)."""
+    A = _bytes_view(A, "A")
+    B = _bytes_view(B, "B")
+    D = _bf16_out(D)
+    _need(A, "A", torch.uint8, 2)
+    _need(B, "B", torch.uint8, 2)
+    _need(sfa, "sfa", torch.float32, 2)
+    _need(sfb, "sfb", torch.float32, 2)
+    _need(D, "D", D.dtype, 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(sfa.shape) != (K // 128, M) or tuple(sfb.shape) != ((N + 127) // 128, K // 128) \
+            or tuple(D.shape) != (M, N):
+        raise ValueError("shape mismatch between A, sfa, B, sfb, D")
+    _check(load_library().dg_fp8_gemm_nt_noalloc(_ptr(A), _ptr(sfa), _ptr(B), _ptr(sfb), _ptr(D), M, N, K,
+                                                 _stream(stream)))
 
 
 def dg_fp8_gemm_nt_acc(A, sfa, B, sfb, C, D, workspace=None, stream=None):

@@ -56,6 +56,7 @@ int main(void) {
           (void)dg_fp8_gemm_nt_acc(P16, P16, P16, P16, NULL, P16, M, N, K, NULL, 0, s);
           (void)dg_fp8_gemm_nt_ue8m0(P16, P16, P16, P16, P16, M, N, K, NULL, 0, s);
           (void)dg_bf16_gemm_nt(P16, P16, P16, M, N, K, NULL, 0, s);
+          (void)dg_fp8_gemm_nt_noalloc(P16, P16, P16, P16, P16, M, N, K, s);
           (void)dg_m_grouped_fp8_gemm_nt_contiguous(P16, P16, P16, P16, P16, P16, M, N, K, 8, NULL, 0, s);
           (void)dg_m_grouped_fp8_gemm_nt_contiguous_ue8m0(P16, P16, P16, P16, P16, P16, M, N, K, 8, NULL, 0, s);
           (void)dg_m_grouped_fp8_gemm_nt_masked(P16, P16, P16, P16, P16, P16, 8, M, N, K, 0, NULL, 0, s);

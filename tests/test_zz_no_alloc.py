@@ -1,0 +1,107 @@
+"""The allocation-free dense entry point (dg_fp8_gemm_nt_noalloc) against the
+one that takes a workspace (dg_fp8_gemm_nt): same plan, so bit-identical
+outputs, on consecutive calls of decreasing size that share the static
+scratch (K splits of 128-row and 64-row skinny tiles, K-split tail pieces of
+the persistent kernel), each also within the per-element rule of the oracle
+(Lesson 13, Fig. 13-1); a captured graph of the call replayed with eager work
+between replays; and the rejection of a plan whose scratch exceeds the
+static maximum."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_grouped_matmul_amd import dg, workloads
+from tests.helpers import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _t(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _operands(M, N, K, seed):
+    a32, b32 = workloads.dense(M, N, K, seed)
+    qa, sa = oracle.quant_1x128(a32)
+    qb, sb = oracle.quant_128x128(b32)
+    return qa, sa, qb, sb
+
+
+# decreasing sizes; every plan splits K and so uses the scratch
+CALLS = [(128, 7168, 16384, "tile=128x128"), (64, 2112, 7168, "tile=64x64"), (4096, 2112, 7168, "tail=16x4")]
+
+
+def test_noalloc_equals_workspace_entry_point_on_consecutive_calls():
+    for M, N, K, plan in CALLS:
+        assert plan in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, M, N, K)
+        qa, sa, qb, sb = _operands(M, N, K, seed=M + N)
+        A, SA, B, SB = _t(qa), _t(sa), _t(qb), _t(sb)
+        wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, M, N, K)
+        assert wsz > 0
+        ws = torch.zeros(wsz // 4, dtype=torch.float32, device=DEV)
+        d_ws = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
+        d_na = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
+        dg.dg_fp8_gemm_nt(A, SA, B, SB, d_ws, ws)
+        dg.dg_fp8_gemm_nt_noalloc(A, SA, B, SB, d_na)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(d_na), _bits(d_ws)), f"{M}x{N}x{K}"
+        # the oracle on the first rows and two column blocks
+        rows = min(M, 192)
+        got = _bits(d_na)[:rows]
+        for c0 in (0, (N // 128 - 1) * 128):
+            ref = oracle.gemm_nt(qa[:rows], sa[:, :rows], qb[c0:c0 + 128], sb[c0 // 128:c0 // 128 + 1])
+            assert_close(got[:, c0:c0 + 128], ref, f"noalloc {M}x{N}x{K} columns {c0}")
+
+
+def test_noalloc_in_a_captured_graph():
+    M, N, K = 64, 2112, 7168
+    qa, sa, qb, sb = _operands(M, N, K, seed=3)
+    A, SA, B, SB = _t(qa), _t(sa), _t(qb), _t(sb)
+    D = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
+    dg.dg_fp8_gemm_nt_noalloc(A, SA, B, SB, D)
+    torch.cuda.synchronize()
+    eager = _bits(D)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dg.dg_fp8_gemm_nt_noalloc(A, SA, B, SB, D, stream=s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        D.fill_(-1)
+        # eager work on the same scratch between replays (another shape)
+        qa2, sa2, qb2, sb2 = _operands(128, 2112, 7168, seed=10 + i)
+        D2 = torch.empty((128, 2112), dtype=torch.int16, device=DEV)
+        dg.dg_fp8_gemm_nt_noalloc(_t(qa2), _t(sa2), _t(qb2), _t(sb2), D2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(D), eager), f"replay {i}"
+    assert_close(eager, oracle.gemm_nt(qa, sa, qb, sb), "noalloc graph")
+
+
+def test_noalloc_rejects_scratch_beyond_the_static_maximum():
+    # a forced 16-way split of 256 tiles of 128 x 128 would need 256 MiB
+    os.environ["DG_FORCE_CONFIG"] = "skinny=128x32x16x4"
+    try:
+        A = torch.zeros((128, 16384), dtype=torch.uint8, device=DEV)
+        SA = torch.ones((128, 128), dtype=torch.float32, device=DEV)
+        B = torch.zeros((32768, 16384), dtype=torch.uint8, device=DEV)
+        SB = torch.ones((256, 128), dtype=torch.float32, device=DEV)
+        D = torch.full((128, 32768), -1, dtype=torch.int16, device=DEV)
+        with pytest.raises(dg.DGError) as ei:
+            dg.dg_fp8_gemm_nt_noalloc(A, SA, B, SB, D)
+        assert ei.value.code == dg.DG_ERR_WORKSPACE and "static maximum" in str(ei.value)
+        torch.cuda.synchronize()
+        assert bool((D == -1).all())  # nothing was launched
+    finally:
+        del os.environ["DG_FORCE_CONFIG"]
