@@ -229,7 +229,9 @@ int dg_bf16_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* D, int64_t M
  * alpha = fl32(amax / 448) by IEEE division; q = e4m3_RNE(fl32(x / alpha)),
  * ties to even, sign of zero kept, saturating at +-448; a group with amax = 0
  * (or amax/448 underflowing to 0) gets alpha = 1.  Non-finite inputs give
- * unspecified codes.  Bit-exact and deterministic.
+ * unspecified codes.  Bit-exact and deterministic.  Limits: G <= 65535,
+ * M <= 2^31 - 16 and ceil(M / 16) * (K / 128) < 2^31 (else DG_ERR_SHAPE); x and q 16-byte
+ * aligned, sfa 4-byte aligned (else DG_ERR_ALIGN).
  */
 int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K,
                    void* stream);

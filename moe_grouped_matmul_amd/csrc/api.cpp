@@ -817,7 +817,8 @@ int dg_m_grouped_fp8_gemm_nt_masked_ue8m0(const uint8_t* A, const int32_t* sfa, 
 int dg_quant_1x128(const float* x, uint8_t* q, float* sfa, int64_t G, int64_t M, int64_t K, void* stream) {
   if (K <= 0 || K % 128) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
   if (G < 0 || M < 0) return fail(DG_ERR_SHAPE, "G and M must be >= 0");
-  if (G > ((int64_t)1 << 31) || M > ((int64_t)1 << 31) || G * M * (K / 128) > ((int64_t)1 << 35))
+  // grid (ceil(M / 16) * (K / 128), G)
+  if (G > 65535 || M > ((int64_t)1 << 31) - 16 || ceil_div(M, 16) * (K / 128) > ((int64_t)1 << 31) - 1)
     return fail(DG_ERR_SHAPE, "problem too large");
   if (G == 0 || M == 0) return ok();
   if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARG, "null pointer");
@@ -851,7 +852,8 @@ int dg_quant_128x128(const float* x, uint8_t* q, float* sfb, int64_t G, int64_t 
 int dg_quant_1x128_ue8m0(const float* x, uint8_t* q, int32_t* sfa, int64_t G, int64_t M, int64_t K, void* stream) {
   if (K <= 0 || K % 128) return fail(DG_ERR_SHAPE, "K must be a positive multiple of 128 (got %lld)", (long long)K);
   if (G < 0 || M < 0) return fail(DG_ERR_SHAPE, "G and M must be >= 0");
-  if (G > ((int64_t)1 << 31) || M > ((int64_t)1 << 31) || G * M * (K / 128) > ((int64_t)1 << 35))
+  // grid (ceil(M / 16) * (K / 128), G)
+  if (G > 65535 || M > ((int64_t)1 << 31) - 16 || ceil_div(M, 16) * (K / 128) > ((int64_t)1 << 31) - 1)
     return fail(DG_ERR_SHAPE, "problem too large");
   if (G == 0 || M == 0) return ok();
   if (!x || !q || !sfa) return fail(DG_ERR_INVALID_ARG, "null pointer");

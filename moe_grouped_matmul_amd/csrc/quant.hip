@@ -50,9 +50,6 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
   return s == 0.0f ? 1.0f : s;
 }
 
-__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d, float s) {
-  return e4m3_rne(a / s) | (e4m3_rne(b / s) << 8) | (e4m3_rne(c / s) << 16) | (e4m3_rne(d / s) << 24);
-}
 
 // UE8M0 code of a group: c = 127 + min{e : 448 * 2^e >= amax}, clamped to
 // [0, 254]; an all-zero group gets 127.  With amax = 1.f * 2^(E - 127) and
@@ -79,30 +76,55 @@ __device__ __forceinline__ void store_code(uint8_t* word, int kb, int KB, int c)
     for (int j = (kb & 3) + 1; j < 4; ++j) word[j] = 0;
 }
 
-// 1x128 groups: 16 lanes per group, 8 elements per lane (two 16-byte loads).
+// e4m3 byte of fl32(x / s), given r = fl32(1 / s) (IEEE division).  The
+// product fl32(x * r) carries two roundings of relative size 2^-24 each, so
+// it lies within a few fp32 steps of the correctly rounded quotient
+// fl32(x / s).  Rounding to the e4m3 grid keeps only the top 3 mantissa bits
+// (the low 20 are dropped, normal e4m3 range): both values give the same byte
+// unless a rounding midpoint of the e4m3 grid (low 20 bits 0x80000) lies
+// within kGuard steps of the product.  Those rare elements, and everything
+// outside the normal range (e4m3 subnormals, non-finite values), take the
+// exact IEEE division.
+constexpr uint32_t kGuard = 16;
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float x, float s, float r) {
+  const float y = x * r;
+  const uint32_t a = __float_as_uint(y) & 0x7fffffffu;
+  const uint32_t low = a & 0xfffffu;
+  const bool safe = a >= 0x3c800000u + kGuard && a < 0x7f000000u && (low + kGuard - 0x80000u) > 2u * kGuard;
+  return safe ? e4m3_rne(y) : e4m3_rne(x / s);
+}
+
+__device__ __forceinline__ uint32_t pack4_q(float a, float b, float c, float d, float s, float r) {
+  return e4m3_of_quotient(a, s, r) | (e4m3_of_quotient(b, s, r) << 8) | (e4m3_of_quotient(c, s, r) << 16) |
+         (e4m3_of_quotient(d, s, r) << 24);
+}
+
+// 1x128 groups.  Grid (ceil(M / 16) * (K / 128), G); a 256-thread workgroup
+// quantises K group kb of 16 consecutive rows of one group g: 16 lanes per
+// row, 8 elements per lane (two 16-byte loads), so the 16 rows' scales are
+// 64 contiguous bytes of the MN-major scale array.  kb runs fastest across
+// workgroups: neighbouring workgroups read neighbouring 512-byte pieces of
+// the same rows (measured faster than walking down the rows first).
 template <bool UE8M0>
 __global__ void __launch_bounds__(256) quant_1x128_kernel(const float* __restrict__ x, uint8_t* __restrict__ q,
-                                                          void* __restrict__ sfa, int64_t M, int K,
-                                                          int64_t total_groups) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t grp_raw = t >> 4;
-  const int sub = threadIdx.x & 15;
-  const bool active = grp_raw < total_groups;
-  const int64_t grp = active ? grp_raw : total_groups - 1;
+                                                          void* __restrict__ sfa, int M, int K) {
   const int KB = K >> 7;
-  const int64_t row = grp / KB;  // flattened (g, m)
-  const int kb = (int)(grp - row * KB);
-  const float* src = x + row * K + ((int64_t)kb << 7) + (sub << 3);
-  const float4 v0 = *reinterpret_cast<const float4*>(src);
-  const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+  const int rb = (int)blockIdx.x / KB;  // uniform: one scalar division per workgroup
+  const int kb = (int)blockIdx.x - rb * KB;
+  const int sub = threadIdx.x & 15;
+  const int m = rb * 16 + (threadIdx.x >> 4);
+  const int64_t g = blockIdx.y;
+  const bool active = m < M;
+  const int mm = active ? m : M - 1;  // inactive lanes repeat the last row (read only)
+  const int64_t off = (g * M + mm) * (int64_t)K + ((int64_t)kb << 7) + (sub << 3);
+  const float4 v0 = *reinterpret_cast<const float4*>(x + off);
+  const float4 v1 = *reinterpret_cast<const float4*>(x + off + 4);
   float amax = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
                      fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
   if (!active) return;
   uint2 out;
-  const int64_t g = row / M;
-  const int64_t m = row - g * M;
   if constexpr (UE8M0) {
     const int c = ue8m0_code(amax);
     const float inv = __builtin_ldexpf(1.0f, 127 - c);
@@ -114,11 +136,12 @@ __global__ void __launch_bounds__(256) quant_1x128_kernel(const float* __restric
     }
   } else {
     const float s = scale_from_amax(amax);
-    out.x = pack4(v0.x, v0.y, v0.z, v0.w, s);
-    out.y = pack4(v1.x, v1.y, v1.z, v1.w, s);
+    const float r = 1.0f / s;  // IEEE division, correctly rounded
+    out.x = pack4_q(v0.x, v0.y, v0.z, v0.w, s, r);
+    out.y = pack4_q(v1.x, v1.y, v1.z, v1.w, s, r);
     if (sub == 0) static_cast<float*>(sfa)[(g * KB + kb) * M + m] = s;
   }
-  *reinterpret_cast<uint2*>(q + row * K + ((int64_t)kb << 7) + (sub << 3)) = out;
+  *reinterpret_cast<uint2*>(q + off) = out;
 }
 
 // 128x128 blocks: one 256-thread workgroup per block; thread t covers rows
@@ -162,6 +185,7 @@ __global__ void __launch_bounds__(256) quant_128x128_kernel(const float* __restr
   __syncthreads();
   amax = fmaxf(fmaxf(s_wave_max[0], s_wave_max[1]), fmaxf(s_wave_max[2], s_wave_max[3]));
   const float s = scale_from_amax(amax);
+  const float rs = 1.0f / s;  // IEEE division, correctly rounded
   const int c = ue8m0_code(amax);
   const float inv = __builtin_ldexpf(1.0f, 127 - c);
   uint8_t* qbase = q + (g * N) * K + ((int64_t)kb << 7) + col;
@@ -174,8 +198,8 @@ __global__ void __launch_bounds__(256) quant_128x128_kernel(const float* __restr
         out.x = pack4_pow2(v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, inv);
         out.y = pack4_pow2(v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w, inv);
       } else {
-        out.x = pack4(v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, s);
-        out.y = pack4(v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w, s);
+        out.x = pack4_q(v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, s, rs);
+        out.y = pack4_q(v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w, s, rs);
       }
       *reinterpret_cast<uint2*>(qbase + r * K) = out;
     }
@@ -194,14 +218,12 @@ __global__ void __launch_bounds__(256) quant_128x128_kernel(const float* __restr
 
 hipError_t launch_quant_1x128(const float* x, uint8_t* q, void* sfa, int64_t G, int64_t M, int64_t K, bool ue8m0,
                               hipStream_t stream) {
-  const int64_t groups = G * M * (K / 128);
-  const int64_t blocks = (groups * 16 + 255) / 256;
+  // the host guarantees ceil(M / 16) * (K / 128) < 2^31 and G <= 65535
+  const dim3 grid((unsigned)((M + 15) / 16 * (K / 128)), (unsigned)G);
   if (ue8m0)
-    hipLaunchKernelGGL(quant_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, sfa, M, (int)K,
-                       groups);
+    hipLaunchKernelGGL(quant_1x128_kernel<true>, grid, dim3(256), 0, stream, x, q, sfa, (int)M, (int)K);
   else
-    hipLaunchKernelGGL(quant_1x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, sfa, M, (int)K,
-                       groups);
+    hipLaunchKernelGGL(quant_1x128_kernel<false>, grid, dim3(256), 0, stream, x, q, sfa, (int)M, (int)K);
   return hipGetLastError();
 }
 

@@ -124,6 +124,11 @@ def test_status_codes_from_host(lib):
     assert q1(None, P16, P16, 1, 4, 128, s) == dg.DG_ERR_INVALID_ARG
     assert q1(P16, P16 + 4, P16, 1, 4, 128, s) == dg.DG_ERR_ALIGN
     assert q1(P16, P16, P16, 1, 0, 128, s) == dg.DG_OK
+    # launch grid (ceil(M / 16) * (K / 128), G): each dimension's limit
+    assert q1(P16, P16, P16, 65536, 4, 128, s) == dg.DG_ERR_SHAPE
+    assert q1(P16, P16, P16, 1, 1 << 28, 1 << 14, s) == dg.DG_ERR_SHAPE
+    assert q1(P16, P16, P16, 1, (1 << 31) - 15, 128, s) == dg.DG_ERR_SHAPE
+    assert lib.dg_quant_1x128_ue8m0(P16, P16, P16, 65536, 4, 128, s) == dg.DG_ERR_SHAPE
     q2 = lib.dg_quant_128x128
     assert q2(P16, P16, P16, 1, 4, 130, s) == dg.DG_ERR_SHAPE
     assert q2(P16, P16, P16 + 1, 1, 4, 128, s) == dg.DG_ERR_ALIGN

@@ -120,6 +120,52 @@ def test_quant_1x128_near_rounding_midpoints():
     assert np.array_equal(_np(q), qr)
 
 
+def _extreme_groups(rows, seed):
+    # one 128-element group per row, amax spread from fp32 subnormals (where
+    # alpha is subnormal and 1 / alpha overflows) to the top of the range
+    rng = np.random.default_rng(seed)
+    amax = np.array([2.0 ** -149, 2.0 ** -140, 2.0 ** -133, 2.0 ** -126, 1e-38, 3e-36, 1.0, 3e30, 1e38, 3.4e38],
+                    np.float32)
+    x = rng.uniform(-1, 1, (rows, 128)).astype(np.float32) * amax[np.arange(rows) % amax.size, None]
+    x[np.arange(rows), rng.integers(0, 128, rows)] = amax[np.arange(rows) % amax.size]
+    return x
+
+
+def test_quant_1x128_extreme_scales():
+    x = _extreme_groups(40, 5)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    s = torch.empty((1, x.shape[0]), dtype=torch.float32, device=DEV)
+    dg.dg_quant_1x128(_t(x), q, s)
+    qr, sr = oracle.quant_1x128(x)
+    assert np.array_equal(_np(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(_np(q), qr)
+
+
+def test_quant_128x128_extreme_scales_and_midpoints():
+    # top block row: one block per amax from fp32 subnormals to the top of the
+    # range; bottom: alpha = 1/3 and values within a few ulps of e4m3
+    # rounding midpoints times alpha
+    rng = np.random.default_rng(13)
+    amax = np.array([2.0 ** -149, 2.0 ** -140, 2.0 ** -133, 2.0 ** -126, 1e-38, 3e-36, 1.0, 3e30, 1e38, 3.4e38],
+                    np.float32)
+    top = rng.uniform(-1, 1, (128, 128 * amax.size)).astype(np.float32) * np.repeat(amax, 128)[None]
+    top[rng.integers(0, 128, amax.size), np.arange(amax.size) * 128 + 5] = amax
+    amid = np.float32(448.0 / 3.0)
+    alpha = np.float32(amid / np.float32(448.0))
+    mids = ((1.0 + (2 * rng.integers(0, 8, top.shape) + 1) / 16.0) * np.exp2(rng.integers(-5, 7, top.shape)))
+    near = (mids.astype(np.float32) * alpha).view(np.int32) + rng.integers(-3, 4, top.shape).astype(np.int32)
+    bot = near.view(np.float32) * np.where(rng.random(top.shape) < 0.5, -1, 1).astype(np.float32)
+    bot = np.clip(bot, -amid, amid)
+    bot[0, ::128] = amid
+    x = np.concatenate([top, bot], 0)[None]
+    q = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    s = torch.empty((1, 2, x.shape[2] // 128), dtype=torch.float32, device=DEV)
+    dg.dg_quant_128x128(_t(x), q, s)
+    qr, sr = oracle.quant_128x128(x)
+    assert np.array_equal(_np(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(_np(q), qr)
+
+
 @pytest.mark.parametrize("G,N,K", [(1, 16, 128), (1, 200, 384), (2, 136, 256), (1, 2112, 1024)])
 def test_quant_128x128_bit_exact(G, N, K):
     rng = np.random.default_rng(N + K)
