@@ -356,18 +356,18 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
   pl.splits = (int)ceil_div(KB, pl.kb_per_split);
 }
 
-// The dense forms.  kFp8 / kAcc: skinny for M <= 128, else 256 x 256 tiles
-// where they fill whole rounds, else 256 x 128 tiles with a K-split tail.
-// kUe8m0 / kBf16: 256 x 256 tiles where they fill whole rounds, else
-// 256 x 128 tiles.  DG_FORCE_CONFIG=kernel=... overrides the wide / 256 x 128
-// choice for M > 128 (and for the UE8M0 / BF16 forms at any M >= 1).
+// The dense forms.  kFp8 / kAcc / kUe8m0: skinny for M <= 128, else 256 x 256
+// tiles where they fill whole rounds, else 256 x 128 tiles with a K-split
+// tail.  kBf16: 256 x 256 tiles where they fill whole rounds, else 256 x 128
+// tiles.  DG_FORCE_CONFIG=kernel=... overrides the wide / 256 x 128 choice
+// for M > 128 (and for the BF16 form at any M >= 1).
 enum DenseKind { kFp8 = 0, kAcc = 1, kUe8m0 = 2, kBf16 = 3 };
 
 DensePlan plan_dense(DenseKind kind, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   DensePlan pl;
   const int64_t kbytes = kind == kBf16 ? 2 * K : K;  // bytes per operand row
   const Force f = forced();
-  if ((kind == kFp8 || kind == kAcc) && M <= 128) {
+  if (kind != kBf16 && M <= 128) {
     plan_skinny(pl, M, N, K, cus, ws_bytes);
     return pl;
   }
@@ -443,7 +443,7 @@ int run_dense(DenseKind kind, const uint8_t* A, const void* sfa, const uint8_t* 
     const int mode = kind == kFp8 ? dg::kDense : kind == kAcc ? dg::kDenseAcc : kind == kUe8m0 ? dg::kDenseUe8m0
                                                                                                  : dg::kDenseBf16;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = pl.skinny ? dg::launch_gemm_skinny(pl.cfg, pl.wn, pl.depth, p, st)
+    const hipError_t e = pl.skinny ? dg::launch_gemm_skinny(pl.cfg, pl.wn, pl.depth, kind == kUe8m0, p, st)
                          : pl.wide ? dg::launch_gemm_wide(mode, pl.grid, p, st)
                                    : dg::launch_gemm_persistent(mode, pl.grid, p, st);
     if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));

@@ -75,8 +75,11 @@ constexpr size_t kWsCounterBytes = 4 * kWsMaxCounters;
 // p.m_tiles = ceil(M / bm), p.n_tiles = ceil(N / (4 wn)), p.splits K splits of
 // p.kb_per_split blocks.  With p.splits > 1 (then at most kWsMaxCounters
 // tiles), p.ws must hold skinny_workspace_bytes(...) bytes laid out as above.
+// ue: UE8M0 scales packed four per int32 along K (sfa [ceil(KB/4)][rows],
+// sfb [ceil(N/128)][ceil(KB/4)]); p.Dacc selects the fp32 accumulating
+// epilogue (fp32 scales only).
 size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int splits);
-hipError_t launch_gemm_skinny(int bm, int wn, int depth, const GemmParams& p, hipStream_t stream);
+hipError_t launch_gemm_skinny(int bm, int wn, int depth, bool ue, const GemmParams& p, hipStream_t stream);
 // K blocks in flight per wave (ring depth; LDS per slot is (bm + 4 wn) * 128 B
 // plus 1 KB); a split's block count is padded to a multiple of it (padding
 // blocks read as zeros), so splits should be multiples.  Four slots for 64-row

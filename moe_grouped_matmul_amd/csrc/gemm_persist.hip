@@ -63,9 +63,9 @@
 // j % 3 with iteration j + 3 -- which may belong to the next tile -- then runs
 // the MFMAs and promotions of iteration j.  A finished tile is written with
 // buffer stores (lanes outside the tile address past the buffer end) while
-// the next tile's blocks are already loading.  Operand layout, fragment order
-// and promotion are those of the non-persistent LDS-ring kernel
-// (gemm_lds.hip).
+// the next tile's blocks are already loading.  Operand layout (128-byte LDS
+// rows, 16-byte chunk c of row r at c ^ (r % 8)), fragment order and
+// promotion are shared with the wide-tile kernel (gemm_wide.hip).
 
 #include "dg_internal.hpp"
 #include "gemm_common.hpp"

@@ -24,7 +24,10 @@
 //     the prefetch; LDS-targeted loads are tracked exactly);
 //   * promotion: each 16x16x128 MFMA (B as row operand, A as column operand)
 //     writes a fresh fp32 partial that one FMA per element adds into the
-//     accumulator with scale alpha * beta;
+//     accumulator with scale alpha * beta.  With UE8M0 scales (four codes
+//     per 32-bit word along K, as in the other kernels) the matrix cores
+//     apply beta's code to B and each row's alpha code to A, which is exact
+//     for powers of two, and the promotion is one fp32 add;
 //   * K is split over several workgroups when the tiles alone cannot occupy
 //     the GPU.  Each split stores its fp32 partial tile in the workspace in
 //     MFMA fragment order (16-byte stores, coherent across XCDs); the last
@@ -51,7 +54,7 @@ constexpr int kCoherent = 16;  // sc1
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM, int WN, int P, bool ACC>
+template <int BM, int WN, int P, bool ACC, bool UE>
 __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4;
@@ -66,6 +69,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
   static_assert(WN == 16 || WN == 32, "WN");
   static_assert(P == 4 || P == 6 || P == 8, "ring depth");
   static_assert((P - 1) * L_STEP < 64, "vmcnt range");
+  static_assert(!(ACC && UE), "the accumulating form has fp32 scales");
 
   // ring slots are separate arrays so the compiler can tell DMA targets from
   // the slots being read; slots 4..7 exist only for deeper rings
@@ -109,6 +113,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
   const int N = p.N;
   const int M = (int)p.rows;
   const int KB = K >> 7;
+  const int KW = (KB + 3) >> 2;  // UE8M0: packed words (four K blocks) per scale row
   const int NB = (N + 127) >> 7;
   const int kb_lo = split * p.kb_per_split;
   const int kb_hi = kb_lo + p.kb_per_split < KB ? kb_lo + p.kb_per_split : KB;
@@ -126,7 +131,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
   // alpha rows are sfa_ld apart (the row stride of the caller's [K/128][rows]
   // array); the range ends after this launch's last row of the last K block
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.sfa + m0, ((uint32_t)p.sfa_ld * (uint32_t)(KB - 1) + (uint32_t)(M - m0)) * 4u);
+      make_rsrc(p.sfa + m0, ((uint32_t)p.sfa_ld * (uint32_t)((UE ? KW : KB) - 1) + (uint32_t)(M - m0)) * 4u);
   // zero-length ranges: loads for the padding steps past the split's last
   // block read zeros and touch no memory
   const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(p.A, 0);
@@ -168,7 +173,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
   nblk = nblk < NB ? nblk : NB - 1;
   const DG_CONST float* sfb_w;
   {
-    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + nblk * KB);
+    const uint64_t a = reinterpret_cast<uint64_t>(p.sfb + nblk * (UE ? KW : KB));
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
     sfb_w = (const DG_CONST float*)(((uint64_t)hi << 32) | lo);
@@ -199,7 +204,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_, (DG_LDS void*)(SK_SLOT(sA, st_) + (i_ * NW + wave) * 1024), \
                                                  16, a_src + i_ * a_stride, (kb_) << 7, 0, 0);             \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (DG_LDS void*)(SK_SLOT(sS, st_) + wave * 64), 4, s_src,  \
-                                             (kb_) * p.sfa_ld * 4, 0, 0);                                  \
+                                             (UE ? (kb_) >> 2 : (kb_)) * p.sfa_ld * 4, 0, 0);              \
     _Pragma("unroll") for (int j_ = 0; j_ < TN; ++j_)                                                      \
       _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                                     \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                          \
@@ -228,7 +233,13 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
   }())
 #define SK_STEP(st_, j_)                                                                                   \
   do {                                                                                                     \
-    const float beta_ = sfb_w[(j_) < nsteps ? SK_KB(j_) : kb_lo];                                          \
+    const int kbj_ = (j_) < nsteps ? SK_KB(j_) : kb_lo;                                                    \
+    /* fp32 scales: beta of the block; UE8M0: the block's codes are byte kbj_ % 4 of the packed words */   \
+    const float beta_ = UE ? 1.f : sfb_w[kbj_];                                                            \
+    const int ash_ = 8 * (kbj_ & 3);                                                                       \
+    const int bcode_ = UE ? __builtin_bit_cast(int, sfb_w[kbj_ >> 2]) >> ash_ : 0;                        \
+    (void)ash_;                                                                                            \
+    (void)bcode_;                                                                                          \
     wait_vmcnt<(P - 2) * L_STEP>();                                                                        \
     wait_lgkmcnt0();                                                                                       \
     __builtin_amdgcn_s_barrier();                                                                          \
@@ -240,20 +251,32 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
     _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_) bf_[j2_] = SK_FRAG(bs_ + j2_ * 2048);             \
     _Pragma("unroll") for (int g_ = 0; g_ < TM; g_ += TG) {                                                \
       i32x8 af_[TG];                                                                                       \
-      float sc_[TG];                                                                                       \
+      float sc_[TG]; /* fp32 scales: alpha * beta of the row tile's rows */                                \
+      int acode_[TG]; /* UE8M0: the rows' alpha codes in byte 0 */                                         \
       f32x4 t_[TG][TN];                                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TG; ++i_) {                                                  \
         af_[i_] = SK_FRAG(as_ + (g_ + i_) * 2048);                                                         \
-        sc_[i_] = ss_[(g_ + i_) * 16 + (lane & 15)] * beta_;                                               \
+        const float al_ = ss_[(g_ + i_) * 16 + (lane & 15)];                                               \
+        if constexpr (UE) acode_[i_] = __builtin_bit_cast(int, al_) >> ash_;                               \
+        else sc_[i_] = al_ * beta_;                                                                        \
       }                                                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TG; ++i_)                                                    \
-        _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_)                                               \
-          t_[i_][j2_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                                  \
-              bf_[j2_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);                             \
+        _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_) {                                             \
+          if constexpr (UE) /* alpha and beta applied by the matrix cores (exact powers of two) */         \
+            t_[i_][j2_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                                \
+                bf_[j2_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, bcode_, 0, acode_[i_]);             \
+          else                                                                                             \
+            t_[i_][j2_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                                \
+                bf_[j2_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);                           \
+        }                                                                                                  \
       _Pragma("unroll") for (int i_ = 0; i_ < TG; ++i_)                                                    \
         _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_)                                               \
-          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                                 \
-            acc[g_ + i_][j2_][v_] = __builtin_fmaf(t_[i_][j2_][v_], sc_[i_], acc[g_ + i_][j2_][v_]);       \
+          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) {                                               \
+            if constexpr (UE) /* the promotion: one fp32 add of the scaled block product */                \
+              acc[g_ + i_][j2_][v_] += t_[i_][j2_][v_];                                                    \
+            else                                                                                           \
+              acc[g_ + i_][j2_][v_] = __builtin_fmaf(t_[i_][j2_][v_], sc_[i_], acc[g_ + i_][j2_][v_]);     \
+          }                                                                                                \
     }                                                                                                      \
   } while (0)
 
@@ -397,14 +420,16 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 }
 
 template <int BM, int WN, int P>
-hipError_t launch_skinny_cfg(const GemmParams& p, hipStream_t stream) {
+hipError_t launch_skinny_cfg(bool ue, const GemmParams& p, hipStream_t stream) {
   const int64_t units = (int64_t)p.n_tiles * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.m_tiles;
   if (grid <= 0) return hipSuccess;
-  if (p.Dacc)
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  if (ue)
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else if (p.Dacc)
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, true, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -416,10 +441,12 @@ size_t skinny_workspace_bytes(int bm, int m_tiles, int n_tiles, int wn, int spli
   return kWsCounterBytes + (size_t)splits * m_tiles * n_tiles * bm * 4 * wn * 4;
 }
 
-hipError_t launch_gemm_skinny(int bm, int wn, int depth, const GemmParams& p, hipStream_t stream) {
-  if (bm == 64 && wn == 16) return depth == 8 ? launch_skinny_cfg<64, 16, 8>(p, stream) : launch_skinny_cfg<64, 16, 4>(p, stream);
-  if (bm == 64) return depth == 6 ? launch_skinny_cfg<64, 32, 6>(p, stream) : launch_skinny_cfg<64, 32, 4>(p, stream);
-  return wn == 16 ? launch_skinny_cfg<128, 16, 6>(p, stream) : launch_skinny_cfg<128, 32, 4>(p, stream);
+hipError_t launch_gemm_skinny(int bm, int wn, int depth, bool ue, const GemmParams& p, hipStream_t stream) {
+  if (bm == 64 && wn == 16)
+    return depth == 8 ? launch_skinny_cfg<64, 16, 8>(ue, p, stream) : launch_skinny_cfg<64, 16, 4>(ue, p, stream);
+  if (bm == 64)
+    return depth == 6 ? launch_skinny_cfg<64, 32, 6>(ue, p, stream) : launch_skinny_cfg<64, 32, 4>(ue, p, stream);
+  return wn == 16 ? launch_skinny_cfg<128, 16, 6>(ue, p, stream) : launch_skinny_cfg<128, 32, 4>(ue, p, stream);
 }
 
 }  // namespace dg

@@ -2,8 +2,9 @@
 (oracle/ue8m0.py): both quantisers bit-exact (bytes and packed code words,
 ragged N, K blocks not a multiple of four, several groups, zero groups,
 amax exactly at and just past the power-of-two boundaries, tiny values), the
-GEMM within the bf16 tolerance over small, ragged and split shapes and on
-256 x 256 tiles, bit identity with the fp32-scale kernel fed the same powers
+GEMM within the bf16 tolerance over small, ragged and split shapes, on
+256 x 256 tiles and on the skinny (rows <= 128) kernel's every compiled
+configuration, bit identity with the fp32-scale kernels fed the same powers
 of two, and the
 4096x7168x16384 shape at full size on sampled rows and column blocks."""
 
@@ -152,6 +153,37 @@ def test_gemm_ue8m0_bit_identical_to_fp32_scale_kernel(M, N, K):
     dg.dg_fp8_gemm_nt(_t(qa), _t(sa), _t(qb), _t(sb), D2, _ws(M, N, K))
     torch.cuda.synchronize()
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+
+
+# (M, N, K, forced plan): rows <= 128 run the skinny kernel; the forced plans
+# reach every compiled (tile rows, columns per wave, ring depth) instance with
+# a K split, ragged M and N, and K blocks not a multiple of four
+SKINNY = [(1, 16, 128, None), (37, 400, 640, None), (100, 528, 1152, None), (64, 2112, 7168, None),
+          (128, 7168, 2048, None), (50, 272, 640, "skinny=64x16x2x4"), (64, 400, 1024, "skinny=64x16x3x8"),
+          (64, 528, 1152, "skinny=64x32x3x4"), (61, 528, 1024, "skinny=64x32x2x6"),
+          (128, 272, 896, "skinny=128x16x2x6"), (120, 528, 1152, "skinny=128x32x3x4")]
+
+
+@pytest.mark.parametrize("M,N,K,force", SKINNY)
+def test_gemm_ue8m0_skinny(M, N, K, force, monkeypatch):
+    if force:
+        monkeypatch.setenv("DG_FORCE_CONFIG", force)
+    plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
+    assert "kernel=skinny" in plan
+    if force:
+        assert f"splits={force.split('x')[2]}" in plan
+    qa, pa, qb, pb = _case(M, N, K, seed=11 * M + N + K)
+    kb = K // 128
+    ws = torch.zeros(16 << 20, dtype=torch.float32, device=DEV)  # the same plan for both forms
+    D1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    D2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.dg_fp8_gemm_nt_ue8m0(_t(qa), _t(pa), _t(qb), _t(pb), D1, ws)
+    # the fp32-scale skinny kernel fed the same powers of two: bit for bit
+    dg.dg_fp8_gemm_nt(_t(qa), _t(ue8m0_value(unpack_k(pa.T, kb).T)), _t(qb), _t(ue8m0_value(unpack_k(pb, kb))), D2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+    assert_close(D1.view(torch.int16).cpu().numpy().view(np.uint16), oracle.gemm_nt_ue8m0(qa, pa, qb, pb),
+                 f"ue8m0 skinny {M}x{N}x{K} {force or 'default plan'}")
 
 
 @pytest.mark.timeout(600)
