@@ -52,7 +52,8 @@ CPU_SAMPLE_ROWS = 2048  # rows per shape in the CPU-oracle baseline sample
 COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE /
 # WRITE_SIZE counters (calibrated against a plain copy) and recorded together with
-# a hash of the kernel's sources: reported only while those sources are unchanged.
+# a hash of the kernel's sources (code only, comments stripped): reported only
+# while that code is unchanged.
 TRAFFIC_RECORDS = {
     "sweep": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_dense_sweep.md"),
     "masked": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_masked_4096x7168.md"),
@@ -63,13 +64,43 @@ KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_m
                   "moe_grouped_matmul_amd/build.py")
 
 
+def _code_only(text, python):
+    """Source text with comments and blank space removed, so a record stays
+    tied to the code that was measured and not to its comments.  C-family
+    files: // and /* */ comments outside string and character literals;
+    Python: lines that are only a comment."""
+    if python:
+        lines = [l.rstrip() for l in text.splitlines() if l.strip() and not l.lstrip().startswith("#")]
+        return "\n".join(lines)
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            k = text.find("*/", i + 2)
+            i = n if k < 0 else k + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(" ".join(l.split()) for l in "".join(out).splitlines() if l.strip())
+
+
 def kernel_source_hash():
     import hashlib
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(_code_only(f.read(), rel.endswith(".py")).encode())
     return h.hexdigest()
 
 
@@ -542,53 +573,78 @@ def run_acc(args, torch, dg, workloads):
                 config=config)
 
 
+UE8M0_DECODE = [(64, 2112, 7168), (128, 7168, 2048)]  # timed per call beside the step
+
+
 def run_ue8m0(args, torch, dg, workloads):
     """Dense FP8 GEMM with UE8M0 (power-of-two) scales packed four per int32
-    at 4096 x 7168 x 16384: one step = one GEMM call over one rotating set."""
+    at 4096 x 7168 x 16384: one step = one GEMM call over one rotating set.
+    Two decode shapes (rows <= 128, the skinny kernel) are timed per call
+    beside the step and reported in per_shape only."""
     dev = torch.device("cuda:0")
-    M, N, K = 4096, 7168, 16384
-    KW = (K // 128 + 3) // 4
-    a32, b32 = workloads.dense(M, N, K, 200)
-    A32 = torch.from_numpy(a32).to(dev)
-    B32 = torch.from_numpy(b32).to(dev)
-    A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    SA = torch.empty((KW, M), dtype=torch.int32, device=dev)
-    B8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
-    SB = torch.empty(((N + 127) // 128, KW), dtype=torch.int32, device=dev)
-    dg.dg_quant_1x128_ue8m0(A32, A8, SA)
-    dg.dg_quant_128x128_ue8m0(B32, B8, SB)
-    del A32, B32
-    per_set = M * K + N * K + 2 * M * N
-    nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
-    sets = [dict(a=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(), b=B8 if i == 0 else B8.clone(),
-                 sb=SB if i == 0 else SB.clone(), d=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
-            for i in range(nsets)]
-    wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
-    ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
     timer = Timer(torch)
 
-    def step(i):
-        st = sets[i % nsets]
-        dg.dg_fp8_gemm_nt_ue8m0(st["a"], st["sa"], st["b"], st["sb"], st["d"], ws)
+    def prepare(M, N, K, seed):
+        KW = (K // 128 + 3) // 4
+        a32, b32 = workloads.dense(M, N, K, seed)
+        A32 = torch.from_numpy(a32).to(dev)
+        B32 = torch.from_numpy(b32).to(dev)
+        A8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        SA = torch.empty((KW, M), dtype=torch.int32, device=dev)
+        B8 = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        SB = torch.empty(((N + 127) // 128, KW), dtype=torch.int32, device=dev)
+        dg.dg_quant_1x128_ue8m0(A32, A8, SA)
+        dg.dg_quant_128x128_ue8m0(B32, B8, SB)
+        del A32, B32
+        per_set = M * K + N * K + 2 * M * N
+        nsets = max(2, math.ceil(ROTATE_BYTES / per_set))
+        sets = [dict(a=A8 if i == 0 else A8.clone(), sa=SA if i == 0 else SA.clone(), b=B8 if i == 0 else B8.clone(),
+                     sb=SB if i == 0 else SB.clone(), d=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                for i in range(nsets)]
+        wsz = dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
+        ws = torch.zeros(max(wsz // 4, 1), dtype=torch.float32, device=dev) if wsz else None
 
+        def call(i):
+            st = sets[i % nsets]
+            dg.dg_fp8_gemm_nt_ue8m0(st["a"], st["sa"], st["b"], st["sb"], st["d"], ws)
+
+        flops = 2.0 * M * N * K
+        nbytes = float(M * K + N * K + 4 * M * KW + 4 * ((N + 127) // 128) * KW + 2 * M * N)
+        return call, nsets, flops, nbytes
+
+    def row(M, N, K, us, flops, nbytes):
+        plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
+        kname = ("fp8_gemm_wide_kernel<ue8m0>" if "kernel=wide" in plan else
+                 "fp8_gemm_skinny_kernel<ue8m0>" if "kernel=skinny" in plan else "fp8_gemm_persistent_kernel<ue8m0>")
+        bound = "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_FP8_TFLOPS * 1e12) else "mfma"
+        return dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(flops / us / 1e6, 1),
+                    gbs=round(nbytes / us / 1e3, 1), bound=bound, roof_frac=round(roof_time_us(flops, nbytes) / us, 4),
+                    kernel=kname)
+
+    M, N, K = 4096, 7168, 16384
+    step, _, flops, nbytes = prepare(M, N, K, 200)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ms_per_step, _ = timed_steps(torch, timer, step, args)
-    flops = 2.0 * M * N * K
-    nbytes = float(M * K + N * K + 4 * M * KW + 4 * ((N + 127) // 128) * KW + 2 * M * N)
     us = ms_per_step * 1e3
     achieved = flops / us / 1e6
-    plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, M, N, K, 1)
-    kname = "fp8_gemm_wide_kernel<ue8m0>" if "kernel=wide" in plan else "fp8_gemm_persistent_kernel<ue8m0>"
+    per_shape = [row(M, N, K, us, flops, nbytes)]
     roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
-                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel=kname,
+                frac=round(achieved / PEAK_FP8_TFLOPS, 4), traffic=None, kernel=per_shape[0]["kernel"],
                 launches_per_step=1, avg_launch_us=round(us, 2), algorithmic_bytes_per_launch=round(nbytes),
                 algorithmic_flops_per_launch=round(flops))
-    per_shape = [dict(M=M, N=N, K=K, gemm_us=round(us, 2), tflops=round(achieved, 1), gbs=round(nbytes / us / 1e3, 1),
-                      bound="mfma", roof_frac=round(roof_time_us(flops, nbytes) / us, 4),
-                      kernel=kname)]
+    del step
+    torch.cuda.empty_cache()
+    for (m, n, k) in ([] if args.shapes else UE8M0_DECODE):
+        call, nsets, f, b = prepare(m, n, k, 201)
+        launches = max(16, nsets)
+        g = capture(torch, lambda: [call(i) for i in range(launches)])
+        per_shape.append(row(m, n, k, time_graph(torch, timer, g, 5) * 1e3 / launches, f, b))
+        del g, call
+        torch.cuda.empty_cache()
     config = dict(workload="dense_fp8_nt_ue8m0_4096x7168x16384", shapes=[f"{M}x{N}x{K}"],
+                  per_call_only=[f"{m}x{n}x{k}" for (m, n, k) in UE8M0_DECODE] if not args.shapes else [],
                   scales="UE8M0 1x128 activations, 128x128 weights, four codes per int32", out="bf16",
                   step="dg_fp8_gemm_nt_ue8m0", cold_hbm=True)
     return dict(ms_per_step=ms_per_step, step_flops=flops, per_shape=per_shape, roofline=roof, name=config["workload"],
