@@ -58,6 +58,9 @@ TRAFFIC_RECORDS = {
     "sweep": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_dense_sweep.md"),
     "masked": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_masked_4096x7168.md"),
 }
+CLOCK_RECORDS = {
+    "fp8_gemm_wide_kernel": os.path.join(ROOT, "profiles", "counters_fp8_gemm_wide_kernel_4096x7168x16384.md"),
+}
 KERNEL_SOURCES = ("moe_grouped_matmul_amd/csrc/gemm_persist.hip", "moe_grouped_matmul_amd/csrc/gemm_wide.hip",
                   "moe_grouped_matmul_amd/csrc/gemm_common.hpp",
                   "moe_grouped_matmul_amd/csrc/dg_internal.hpp", "moe_grouped_matmul_amd/csrc/api.cpp",
@@ -104,22 +107,42 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter record, or None when the
-    record is missing, is for another kernel/workload, or predates the sources."""
-    if workload not in TRAFFIC_RECORDS:
-        return None
+def _record_fields(path, kernel):
+    """The "- key: value" fields of a committed counter record, or None when the
+    record is missing, is for another kernel, or predates the sources."""
     try:
-        with open(TRAFFIC_RECORDS[workload]) as f:
+        with open(path) as f:
             fields = dict(l.strip()[2:].split(": ", 1) for l in f if l.startswith("- ") and ": " in l)
     except OSError:
         return None
-    if fields.get("kernel") != kernel or fields.get("workload") != workload:
+    if fields.get("kernel") != kernel or fields.get("source_sha256") != kernel_source_hash():
         return None
-    if fields.get("source_sha256") != kernel_source_hash():
+    return fields
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter record, or None when the
+    record is missing, is for another kernel/workload, or predates the sources."""
+    fields = _record_fields(TRAFFIC_RECORDS[workload], kernel) if workload in TRAFFIC_RECORDS else None
+    if fields is None or fields.get("workload") != workload:
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def recorded_clock(kernel):
+    """Achieved shader clock and MFMA-busy fraction of a kernel from its committed
+    rocprofv3 counter record (SQ_BUSY_CYCLES over the 32 shader engines against
+    the dispatch time; SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs), or None.
+    The clock's published peak, 2.4 GHz, underlies the 5.0 PF FP8 peak."""
+    fields = _record_fields(CLOCK_RECORDS[kernel], kernel) if kernel in CLOCK_RECORDS else None
+    if fields is None:
+        return None
+    try:
+        return dict(clock_ghz=float(fields["clock_ghz"]), clock_peak_ghz=2.4, mfma_busy=float(fields["mfma_busy"]),
+                    clock_record=os.path.relpath(CLOCK_RECORDS[kernel], ROOT) + " (" + fields["workload"] + ")")
     except (KeyError, ValueError):
         return None
 
@@ -317,6 +340,9 @@ def run_dense(args, torch, dg, workloads):
     roof.update(traffic=traffic, kernel=dom_name, launches_per_step=dom["n"], avg_launch_us=round(avg_us, 2),
                 algorithmic_bytes_per_launch=round(dom["bytes"] / dom["n"]),
                 algorithmic_flops_per_launch=round(dom["flops"] / dom["n"]))
+    clock = recorded_clock(dom_name)
+    if clock:
+        roof.update(clock)
     return dict(ms_per_step=ms_per_step, wall_s=wall, step_flops=step_flops, per_shape=per_shape, roofline=roof,
                 shapes=[(p["M"], p["N"], p["K"]) for p in prepared])
 
