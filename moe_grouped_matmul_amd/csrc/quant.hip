@@ -4,10 +4,14 @@
 // breakdown" (hpc.payai.win), Fig. 13-1: activations get one fp32 scale per
 // token per 128 K elements, weights one per 128x128 block; the scale is the
 // group's largest magnitude divided by 448, the e4m3 maximum.  The pages leave
-// the rounding open; these kernels use IEEE fp32 division for the scale and
-// for x / scale, and round-to-nearest-even onto the e4m3 grid (subnormals
-// included, ties to even mantissa, sign of zero kept, saturation at 448), so
-// the output bytes are unique.  An all-zero group gets scale 1.
+// the rounding open; these kernels take the correctly rounded fp32 quotients
+// amax / 448 and x / scale, and round to nearest even onto the e4m3 grid
+// (subnormals included, ties to even mantissa, sign of zero kept, saturation
+// at 448), so the output bytes are unique.  An all-zero group gets scale 1.
+// The rounding onto e4m3 is the hardware conversion (v_cvt_pk_fp8_f32) of
+// the value clamped to +-448, which gives that byte for every finite fp32
+// input (compared against an integer implementation of the rule over all
+// 2^32 bit patterns on gfx950).
 //
 // UE8M0 variants (newer library versions accept power-of-two scales: Lesson
 // 13, the notes after Fig. 13-1; the deep-dive blog, section 3, packs four of
@@ -27,22 +31,12 @@ namespace {
 
 constexpr float kE4M3Max = 448.0f;
 
-// fp32 -> OCP e4m3 (E4M3FN) byte, round to nearest even, saturating.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return s | 0x7fu;  // NaN
-  if (a >= 0x43e00000u) return s | 0x7eu;  // |y| >= 448 (and inf): saturate
-  if (a >= 0x3c800000u) {
-    // |y| >= 2^-6: normal e4m3.  Drop 20 of the 23 fp32 mantissa bits with
-    // round-to-nearest-even (a carry moves into the exponent by itself), then
-    // rebias the exponent from 127 to 7.
-    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
-    return s | (r - (120u << 3));
-  }
-  // Subnormal e4m3: multiples of 2^-9.  |y| * 512 is exact; rint is RNE.
-  return s | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+// four fp32 values -> four e4m3 bytes (a in byte 0): clamp to +-448, then the
+// hardware's round-to-nearest-even conversion, two values per instruction
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -kE4M3Max), kE4M3Max); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);
 }
 
 __device__ __forceinline__ float scale_from_amax(float amax) {
@@ -65,7 +59,7 @@ __device__ __forceinline__ int ue8m0_code(float amax) {
 // x * 2^(127 - c): an exact power-of-two scaling (one rounding only when the
 // product is an fp32 subnormal, far below the e4m3 grid)
 __device__ __forceinline__ uint32_t pack4_pow2(float a, float b, float c, float d, float inv) {
-  return e4m3_rne(a * inv) | (e4m3_rne(b * inv) << 8) | (e4m3_rne(c * inv) << 16) | (e4m3_rne(d * inv) << 24);
+  return e4m3x4(a * inv, b * inv, c * inv, d * inv);
 }
 
 // stores code c of K block kb into its packed word (byte kb % 4); the last
@@ -76,27 +70,36 @@ __device__ __forceinline__ void store_code(uint8_t* word, int kb, int KB, int c)
     for (int j = (kb & 3) + 1; j < 4; ++j) word[j] = 0;
 }
 
-// e4m3 byte of fl32(x / s), given r = fl32(1 / s) (IEEE division).  The
-// product fl32(x * r) carries two roundings of relative size 2^-24 each, so
-// it lies within a few fp32 steps of the correctly rounded quotient
-// fl32(x / s).  Rounding to the e4m3 grid keeps only the top 3 mantissa bits
-// (the low 20 are dropped, normal e4m3 range): both values give the same byte
-// unless a rounding midpoint of the e4m3 grid (low 20 bits 0x80000) lies
-// within kGuard steps of the product.  Those rare elements, and everything
-// outside the normal range (e4m3 subnormals, non-finite values), take the
-// exact IEEE division.
+// fl32(x / s) for e4m3 rounding, given r = fl32(1 / s) (IEEE division).  The
+// product y = fl32(x * r) carries two roundings of relative size 2^-24 each,
+// so it lies within a few fp32 steps of the correctly rounded quotient
+// fl32(x / s).  Rounding to the normal e4m3 grid keeps the top 3 mantissa
+// bits (the low 20 are dropped): both values give the same byte unless a
+// rounding midpoint of the grid (low 20 bits 0x80000) lies within kGuard
+// steps of y.  Those rare elements, and everything outside the normal range
+// (e4m3 subnormals, non-finite values), take the IEEE division instead.
 constexpr uint32_t kGuard = 16;
-__device__ __forceinline__ uint32_t e4m3_of_quotient(float x, float s, float r) {
-  const float y = x * r;
+__device__ __forceinline__ bool product_safe(float y) {
   const uint32_t a = __float_as_uint(y) & 0x7fffffffu;
   const uint32_t low = a & 0xfffffu;
-  const bool safe = a >= 0x3c800000u + kGuard && a < 0x7f000000u && (low + kGuard - 0x80000u) > 2u * kGuard;
-  return safe ? e4m3_rne(y) : e4m3_rne(x / s);
+  return a >= 0x3c800000u + kGuard && a < 0x7f000000u && (low + kGuard - 0x80000u) > 2u * kGuard;
 }
 
-__device__ __forceinline__ uint32_t pack4_q(float a, float b, float c, float d, float s, float r) {
-  return e4m3_of_quotient(a, s, r) | (e4m3_of_quotient(b, s, r) << 8) | (e4m3_of_quotient(c, s, r) << 16) |
-         (e4m3_of_quotient(d, s, r) << 24);
+// q[0..N) = bytes of fl32(x[e] / s): the products, with the division redone
+// (rarely) for the elements whose product is not safe
+template <int N>
+__device__ __forceinline__ void quotients(const float* x, float* y, float s, float r) {
+  bool all_safe = true;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    y[e] = x[e] * r;
+    all_safe &= product_safe(y[e]);
+  }
+  if (!all_safe) {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (!product_safe(y[e])) y[e] = x[e] / s;
+  }
 }
 
 // 1x128 groups.  Grid (ceil(M / 16) * (K / 128), G); a 256-thread workgroup
@@ -137,8 +140,11 @@ __global__ void __launch_bounds__(256) quant_1x128_kernel(const float* __restric
   } else {
     const float s = scale_from_amax(amax);
     const float r = 1.0f / s;  // IEEE division, correctly rounded
-    out.x = pack4_q(v0.x, v0.y, v0.z, v0.w, s, r);
-    out.y = pack4_q(v1.x, v1.y, v1.z, v1.w, s, r);
+    const float xv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float y[8];
+    quotients<8>(xv, y, s, r);
+    out.x = e4m3x4(y[0], y[1], y[2], y[3]);
+    out.y = e4m3x4(y[4], y[5], y[6], y[7]);
     if (sub == 0) static_cast<float*>(sfa)[(g * KB + kb) * M + m] = s;
   }
   *reinterpret_cast<uint2*>(q + off) = out;
@@ -198,8 +204,11 @@ __global__ void __launch_bounds__(256) quant_128x128_kernel(const float* __restr
         out.x = pack4_pow2(v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, inv);
         out.y = pack4_pow2(v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w, inv);
       } else {
-        out.x = pack4_q(v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, s, rs);
-        out.y = pack4_q(v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w, s, rs);
+        const float xv[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w, v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+        float y[8];
+        quotients<8>(xv, y, s, rs);
+        out.x = e4m3x4(y[0], y[1], y[2], y[3]);
+        out.y = e4m3x4(y[4], y[5], y[6], y[7]);
       }
       *reinterpret_cast<uint2*>(qbase + r * K) = out;
     }
