@@ -53,6 +53,16 @@ __device__ __forceinline__ int xcd_tile(int bid, int tiles) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// Tile id of round s of a walk over `tiles` tiles by `g` persistent
+// workgroups in lockstep rounds: round s covers ids [s g, s g + g), and inside
+// a round each XCD takes a contiguous run, so at any time all XCDs work on
+// neighbouring tiles (the grouped forms: the same few experts' weights, shared
+// through the Infinity Cache).
+__device__ __forceinline__ int round_tile(int bid, int s, int g, int tiles) {
+  const int left = tiles - s * g;
+  return s * g + xcd_tile(bid, left < g ? left : g);
+}
+
 // Linear tile id -> (m, n) with groups of gm m-tiles walked column by column,
 // so concurrently running tiles share operand rows in L2.
 __device__ __forceinline__ void grouped_mn(int t, int m_tiles, int n_tiles, int gm, int* m, int* n) {

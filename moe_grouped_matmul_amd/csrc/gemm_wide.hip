@@ -24,8 +24,8 @@
 //   * the promotion FMAs of each MFMA run three MFMAs later, as in the
 //     256 x 128 kernel (gemm_persist.hip), whose operand layout, swizzle, B
 //     row permutation and deferred bf16 store this kernel shares.
-// Tile walk: ids b, b + G, ... per workgroup, mapped so each XCD runs a
-// contiguous, m-grouped range of tiles.  No K split: used where the tiles
+// Tile walk: lockstep rounds of one tile per workgroup (m-grouped ids),
+// each XCD a contiguous run of the round.  No K split: used where the tiles
 // fill the CUs in whole or nearly whole rounds.
 //
 // UE8M0 scales (dense and contiguous): alpha and beta are powers of two given
@@ -170,7 +170,13 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
     }
     __syncthreads();
   }
-  auto dense_tile = [&](int s, int* mt, int* nt) { grouped_mn(xcd_tile(b + s * G, T), p.m_tiles, p.n_tiles, GM, mt, nt); };
+  // tile s of this workgroup: lockstep rounds of G consecutive tiles, each XCD
+  // a contiguous run inside the round, so all XCDs work on neighbouring tiles
+  // at any time (the contiguous form: the same few experts' weights).  Against
+  // each XCD walking its own eighth of the tiles this measured 1035 -> 972 us
+  // on the 8-expert 4096x7168 contiguous call and 114 -> 94 us on
+  // 4096x32768x512 (its bf16 output is then written in one region at a time).
+  auto dense_tile = [&](int s, int* mt, int* nt) { grouped_mn(round_tile(b, s, G, T), p.m_tiles, p.n_tiles, GM, mt, nt); };
 
   int nseg = n_dp;  // passes (dense: one per tile)
   if constexpr (CONTIG) {
@@ -280,8 +286,7 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
       *hm = __builtin_amdgcn_readfirstlane(pass_half[s]);
     } else if constexpr (KG) {
       // round s of one tile per workgroup, XCD-contiguous inside the round
-      const int left = T - s * G;
-      const int t = s * G + xcd_tile(b, left < G ? left : G);
+      const int t = round_tile(b, s, G, T);
       const int g = t / tpg;
       grouped_mn(t - g * tpg, p.m_tiles, p.n_tiles, GM, mt, nt);
       *e = g;  // the group (of C and D; A and B are shared)
