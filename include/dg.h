@@ -92,10 +92,12 @@ enum {
  *   deterministic).  Required size for the full split is
  *   dg_get_workspace_size(DG_OP_GEMM_NT, M, N, K, 1); a smaller buffer limits
  *   the split.  The workspace MUST be zero-filled before its first use (e.g.
- *   hipMemset once after allocation): for M <= 128 it holds per-tile
- *   completion counters besides the fp32 partials, and every call leaves
- *   those counters at zero again, so a workspace stays reusable without
- *   clearing.  Calls that share one workspace must be ordered on one stream.
+ *   hipMemset once after allocation): whenever the plan splits K (M <= 128,
+ *   or a partial last round of 256 x 128 tiles) its first 4 KiB hold per-tile
+ *   completion counters and the fp32 partials follow; every call leaves the
+ *   counters at zero again, so a workspace stays reusable across calls and
+ *   shapes without clearing.  Calls that share one workspace must be ordered
+ *   on one stream.
  */
 int dg_fp8_gemm_nt(const uint8_t* A, const float* sfa, const uint8_t* B, const float* sfb,
                    uint16_t* D, int64_t M, int64_t N, int64_t K, void* workspace,
