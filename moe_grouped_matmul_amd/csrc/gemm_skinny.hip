@@ -22,6 +22,11 @@
 //     could go straight to registers, but the compiler's wait-count tracking
 //     of register loads across the ring loop adds waits that drain most of
 //     the prefetch; LDS-targeted loads are tracked exactly);
+//   * with M <= 64 (one row tile) each weight line is read by exactly one
+//     workgroup, and the weight loads carry the non-temporal cache policy
+//     (NT = true: 2-13% faster on the decode shapes); where two 64-row tiles
+//     share the weights through one L2, or one 128-row tile reads them, the
+//     default policy was as fast or faster;
 //   * promotion: each 16x16x128 MFMA (B as row operand, A as column operand)
 //     writes a fresh fp32 partial that one FMA per element adds into the
 //     accumulator with scale alpha * beta.  With UE8M0 scales (four codes
@@ -51,10 +56,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // cache policy of the split-K partial stores and loads: coherent at agent
 // scope (the XCDs' L2 caches are not kept coherent with each other)
 constexpr int kCoherent = 16;  // sc1
+// cache policy of the weight loads when one row tile covers M, so every
+// weight line is read by exactly one workgroup: non-temporal (nt)
+constexpr int kStream = 2;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM, int WN, int P, bool ACC, bool UE>
+template <int BM, int WN, int P, bool ACC, bool UE, bool NT>
 __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = 4;
@@ -209,7 +217,7 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
       _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                                     \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                          \
             rb_, (DG_LDS void*)(SK_SLOT(sB, st_) + (wave * TN + j_) * 2048 + h_ * 1024), 16,               \
-            b_src[h_] + j_ * b_tile, (kb_) << 7, 0, 0);                                                    \
+            b_src[h_] + j_ * b_tile, (kb_) << 7, 0, NT ? kStream : 0);                                     \
   } while (0)
 
   // Step j (the j-th K block in rotated order, ring slot st_ = j % P):
@@ -419,17 +427,31 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+template <int BM, int WN, int P, bool NT>
+void launch_skinny_form(bool ue, const GemmParams& p, int64_t grid, hipStream_t stream) {
+  if (ue)
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false, true, NT>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else if (p.Dacc)
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, true, false, NT>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false, false, NT>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+}
+
 template <int BM, int WN, int P>
 hipError_t launch_skinny_cfg(bool ue, const GemmParams& p, hipStream_t stream) {
   const int64_t units = (int64_t)p.n_tiles * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.m_tiles;
   if (grid <= 0) return hipSuccess;
-  if (ue)
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false, true>), dim3((unsigned)grid), dim3(256), 0, stream, p);
-  else if (p.Dacc)
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, true, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fp8_gemm_skinny_kernel<BM, WN, P, false, false>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  // M <= 64 (one 64-row tile): the weights stream past once with the
+  // non-temporal policy.  Where two row tiles share the weights, or one
+  // 128-row tile reads them, the default policy measured faster.
+  if constexpr (BM == 64) {
+    if (p.m_tiles == 1) {
+      launch_skinny_form<BM, WN, P, true>(ue, p, grid, stream);
+      return hipGetLastError();
+    }
+  }
+  launch_skinny_form<BM, WN, P, false>(ue, p, grid, stream);
   return hipGetLastError();
 }
 
