@@ -313,8 +313,18 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
  *                     kernel wherever the planner chooses between them, and
  *                     "chunk_rows=<n>" splits calls into row chunks of at
  *                     most n rows (rounded down to a multiple of 256, at
- *                     least 256); results stay within the same bounds
- *   DG_PRINT_CONFIGS  print every launch's plan on stderr */
+ *                     least 256), and "skinny=<bm>x<wn>x<s>x<p>" makes calls
+ *                     with at most 128 rows use bm-row tiles (64 or 128) of
+ *                     4 wn columns (wn 16 or 32), a K split of s (bounded by
+ *                     the K blocks and the workspace) and ring depth p (one
+ *                     of the compiled depths; other values are ignored);
+ *                     results stay within the same bounds
+ *   DG_PRINT_CONFIGS  print every launch's plan on stderr
+ *   DG_CHECK_LAYOUT   the contiguous forms copy m_indices to the host
+ *                     (synchronising the stream; skipped while the stream is
+ *                     being captured) and reject, with DG_ERR_INVALID_ARG, a
+ *                     layout whose aligned 128-row block holds rows of two
+ *                     experts */
 const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t G);
 
 /* Row alignment of expert segments in the contiguous layout (deep-dive blog,

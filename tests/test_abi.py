@@ -228,3 +228,26 @@ def test_dense_planner_choice(lib):
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 1024, 4096, 7168, 8)  # 64 tiles
     finally:
         dg.dg_set_num_cus(0)
+
+
+def test_forced_config_parsing(lib, monkeypatch):
+    # host logic only: DG_FORCE_CONFIG items the planner honours, and items it
+    # ignores (a ring depth that is not compiled, a malformed item)
+    from moe_grouped_matmul_amd import dg
+
+    try:
+        dg.dg_set_num_cus(256)
+        default = dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048)
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x32x3x4")
+        assert "kernel=skinny tile=64x128 tiles=56 splits=3" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048)
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x32x3x5")  # depth 5 is not compiled
+        assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x32")  # malformed
+        assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
+        monkeypatch.setenv("DG_FORCE_CONFIG", "kernel=persistent")
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)
+        monkeypatch.setenv("DG_FORCE_CONFIG", "kernel=wide,chunk_rows=1000")
+        plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)
+        assert "kernel=wide tile=256x256 grid=27 tiles=27" in plan and plan.endswith("chunks=6")  # 5 x 768 + 256 rows
+    finally:
+        dg.dg_set_num_cus(0)
