@@ -32,7 +32,8 @@
 //     accumulator with scale alpha * beta.  With UE8M0 scales (four codes
 //     per 32-bit word along K, as in the other kernels) the matrix cores
 //     apply beta's code to B and each row's alpha code to A, which is exact
-//     for powers of two, and the promotion is one fp32 add;
+//     for powers of two, and accumulate into the fp32 accumulator (the
+//     promotion, bit for bit the separate add of the scaled product);
 //   * K is split over several workgroups when the tiles alone cannot occupy
 //     the GPU.  Each split stores its fp32 partial tile in the workspace in
 //     MFMA fragment order (16-byte stores, coherent across XCDs); the last
@@ -270,21 +271,19 @@ __global__ void __launch_bounds__(256) fp8_gemm_skinny_kernel(GemmParams p) {
       }                                                                                                    \
       _Pragma("unroll") for (int i_ = 0; i_ < TG; ++i_)                                                    \
         _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_) {                                             \
-          if constexpr (UE) /* alpha and beta applied by the matrix cores (exact powers of two) */         \
-            t_[i_][j2_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                                \
-                bf_[j2_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, bcode_, 0, acode_[i_]);             \
+          if constexpr (UE) /* alpha and beta applied, and the scaled block product added to the */        \
+            /* accumulator, by the matrix cores (exact powers of two): the promotion in one instruction */  \
+            acc[g_ + i_][j2_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                          \
+                bf_[j2_], af_[i_], acc[g_ + i_][j2_], 0, 0, 0, bcode_, 0, acode_[i_]);                      \
           else                                                                                             \
             t_[i_][j2_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                                \
                 bf_[j2_], af_[i_], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);                           \
         }                                                                                                  \
-      _Pragma("unroll") for (int i_ = 0; i_ < TG; ++i_)                                                    \
-        _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_)                                               \
-          _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) {                                               \
-            if constexpr (UE) /* the promotion: one fp32 add of the scaled block product */                \
-              acc[g_ + i_][j2_][v_] += t_[i_][j2_][v_];                                                    \
-            else                                                                                           \
+      if constexpr (!UE)                                                                                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < TG; ++i_)                                                  \
+          _Pragma("unroll") for (int j2_ = 0; j2_ < TN; ++j2_)                                             \
+            _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
               acc[g_ + i_][j2_][v_] = __builtin_fmaf(t_[i_][j2_][v_], sc_[i_], acc[g_ + i_][j2_][v_]);     \
-          }                                                                                                \
     }                                                                                                      \
   } while (0)
 

@@ -33,7 +33,9 @@
 // gemm_persist.hip).
 // The matrix cores apply them (v_mfma_scale_f32_16x16x128_f8f6f4: beta's byte
 // for the B operand, each row's alpha byte for the A operand), which is exact,
-// and the promotion is one fp32 add of the scaled block product.
+// and accumulate the scaled block product into the tile's fp32 accumulator:
+// the promotion is the MFMA itself (bit for bit the separate fp32 add, as the
+// accumulator input is added with one rounding after the products).
 //
 // BF16 operands (plain GEMM, no scales): a K block is 64 bf16 = 128 bytes
 // per row, so LDS rows, swizzle, DMA and fragment reads are those of the fp8
@@ -588,10 +590,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
           if (KG && k_ % TM == 0) /* beta of the 4 columns of fragment j_ this lane holds */               \
             bt_[j_ & 1] = *reinterpret_cast<const f32x4*>(                                                 \
                 WD_SS(st_) + 256 + wn * 128 + (j_ >> 2) * 64 + q * 16 + (j_ & 3) * 4);                     \
-          if constexpr (UE) /* alpha and beta applied by the matrix cores (exact powers of two) */          \
-            t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],        \
-                                                                         f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, \
-                                                                         bcode_, 0, acode_[k_ % TM]);      \
+          if constexpr (UE) /* alpha and beta applied, and the scaled block product added to the */        \
+            /* accumulator, by the matrix cores (exact powers of two): the promotion in one instruction */  \
+            u[k_ % TM][j_] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],   \
+                                                                             u[k_ % TM][j_], 0, 0, 0,      \
+                                                                             bcode_, 0, acode_[k_ % TM]);  \
           else                                                                                             \
             t_[k_ & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf_[j_ & 1], af_[k_ % TM],        \
                                                                          f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0); \
@@ -600,13 +603,12 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
         if (k_ >= 3) {                                                                                     \
           const int kk_ = k_ - 3;                                                                          \
           f32x4& uk_ = u[kk_ % TM][kk_ / TM];                                                              \
-          if constexpr (UE) {                                                                              \
-            uk_ += t_[kk_ & 3]; /* the promotion: one fp32 add of the scaled block product */             \
-          } else {                                                                                         \
+          if constexpr (!UE) {                                                                             \
             if constexpr (KG) t_[kk_ & 3] *= bt_[(kk_ / TM) & 1];                                          \
             _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_)                                               \
               uk_[v_] = __builtin_fmaf(t_[kk_ & 3][v_], sc_[kk_ % TM], uk_[v_]);                           \
           }                                                                                                \
+          /* (UE8M0: pins the accumulator of the MFMA three steps back, which keeps the schedule) */       \
           asm volatile("" : "+v"(uk_));                                                                    \
         }                                                                                                  \
         __builtin_amdgcn_sched_barrier(0);                                                                 \
