@@ -79,6 +79,7 @@ namespace {
 
 constexpr int kRsrcWord3 = 0x00020000;     // raw (untyped) buffer, gfx9 family
 constexpr int kCoherent = 16;              // sc1: coherent across the XCDs' L2 caches
+constexpr int kStream = 2;                 // nt: weight lines that no other task reads
 constexpr uint32_t kOOB = 0xFFFFFF00u;     // an offset past every buffer range used here
 constexpr int kMaxMaskedGroups = 1024;     // groups the masked task list supports
 constexpr int kMaxContigSegs = kPersistentMaxContigTiles;  // tiles per workgroup the contiguous table holds
@@ -103,7 +104,11 @@ struct Seg {
 };
 
 // HASC (fp32-output modes): C is given and read; without it nothing is loaded.
-template <int MODE, bool HASC>
+// NT (masked forms with max_m <= 128, one row tile per expert): every weight
+// line is read by exactly one task, and the weight loads carry the
+// non-temporal cache policy (where two row tiles of an expert share the
+// weights through one L2, the default policy keeps the second read a hit).
+template <int MODE, bool HASC, bool NT>
 __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr bool BF16 = MODE == kDenseBf16;  // bf16 operands, no scales, no promotion
@@ -426,7 +431,8 @@ __global__ void __launch_bounds__(512) fp8_gemm_persistent_kernel(GemmParams p) 
     else if ((n_) < A_INS + B_INS)                                                                         \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_,                                                        \
                                                (DG_LDS void*)(PS_SB(st_) + ((n_) - A_INS) * NWAVES * 1024 + wave * 1024), \
-                                               16, is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, 0); \
+                                               16, is_boff[(n_) < A_INS + B_INS && (n_) >= A_INS ? (n_) - A_INS : 0], ks_, 0, \
+                                               NT ? kStream : 0);                                          \
     else                                                                                                   \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                            \
           rs_, (DG_LDS void*)(bwave ? &bring[KG ? (bs_) : 0][(wave - 4) * 64] : PS_SS(st_) + wave * 64), 4,     \
@@ -837,28 +843,33 @@ hipError_t launch_gemm_persistent(int mode, int grid, const GemmParams& p, hipSt
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), t(512);
   const bool c = p.Cacc != nullptr;
-  if (mode == kMasked)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked, false>), g, t, 0, stream, p);
+  const bool nt = p.m_tiles == 1;  // masked: one 128-row tile per expert
+  if (mode == kMasked && nt)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked, false, true>), g, t, 0, stream, p);
+  else if (mode == kMasked)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMasked, false, false>), g, t, 0, stream, p);
   else if (mode == kDenseBf16)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseBf16, false, false>), g, t, 0, stream, p);
   else if (mode == kDenseAcc && c)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc, true>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc, true, false>), g, t, 0, stream, p);
   else if (mode == kDenseAcc)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseAcc, false, false>), g, t, 0, stream, p);
   else if (mode == kKGrouped && c)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, true>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, true, false>), g, t, 0, stream, p);
   else if (mode == kKGrouped)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kKGrouped, false, false>), g, t, 0, stream, p);
   else if (mode == kContiguous)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguous, false, false>), g, t, 0, stream, p);
   else if (mode == kDenseUe8m0)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseUe8m0, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDenseUe8m0, false, false>), g, t, 0, stream, p);
   else if (mode == kContiguousUe8m0)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguousUe8m0, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kContiguousUe8m0, false, false>), g, t, 0, stream, p);
+  else if (mode == kMaskedUe8m0 && nt)
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMaskedUe8m0, false, true>), g, t, 0, stream, p);
   else if (mode == kMaskedUe8m0)
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMaskedUe8m0, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kMaskedUe8m0, false, false>), g, t, 0, stream, p);
   else
-    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense, false>), g, t, 0, stream, p);
+    hipLaunchKernelGGL((fp8_gemm_persistent_kernel<kDense, false, false>), g, t, 0, stream, p);
   return hipGetLastError();
 }
 
