@@ -27,8 +27,9 @@ over rotating buffer sets; their rows join `per_shape` and `roofline_by_form`
 holds one roofline per form (--no-grouped skips them).
 
 Other workloads: --workload large | small (one dense shape), contiguous | masked
-(the M-grouped forms as the timed step), bf16 | acc | kgrouped | ue8m0 (the
-BF16, accumulating, K-grouped and UE8M0-scale variants).
+(the M-grouped forms as the timed step), masked_decode (the masked form with
+32 experts x 128 rows, masked_m uniform in [0, 128]), bf16 | acc | kgrouped |
+ue8m0 (the BF16, accumulating, K-grouped and UE8M0-scale variants).
 """
 
 import argparse
@@ -174,8 +175,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked", "bf16", "acc",
-                                                              "kgrouped", "ue8m0"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "large", "small", "contiguous", "masked",
+                                                              "masked_decode", "bf16", "acc", "kgrouped", "ue8m0"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-grouped", action="store_true",
                     help="sweep only: skip the per-call timing of the contiguous and masked calls")
@@ -352,7 +353,8 @@ def run_grouped(args, torch, dg, workloads, form=None, timed=True):
     segments padded to 128) or masked (32 experts x 256 capacity, masked_m
     uniform in [0, 256]) GEMMs for both (N, K) pairs.  Activations arrive
     already in e4m3 (as from an expert-parallel dispatch), so a step is the two
-    grouped GEMM calls.  form: "contiguous" | "masked" (default: the workload);
+    grouped GEMM calls.  form: "contiguous" | "masked" | "masked_decode" (32
+    experts x 128 capacity, masked_m uniform in [0, 128]) (default: the workload);
     timed=False measures only the per-call kernel times (graphs of
     back-to-back launches over the rotating sets), as the default sweep run
     does for the grouped forms."""
@@ -463,7 +465,8 @@ def run_grouped(args, torch, dg, workloads, form=None, timed=True):
                 algorithmic_bytes_per_launch=round(big_p["bytes"]),
                 algorithmic_flops_per_launch=round(big_p["flops"]),
                 avg_launch_us=big["gemm_us"])
-    name = "m_grouped_contiguous_8x_tokens_1to8192" if form == "contiguous" else "m_grouped_masked_32x256"
+    name = {"contiguous": "m_grouped_contiguous_8x_tokens_1to8192", "masked": "m_grouped_masked_32x256",
+            "masked_decode": "m_grouped_masked_32x128"}[form]
     config = dict(workload=name, shapes=[f"G={p['G']} N={p['N']} K={p['K']}" for p in prepared],
                   step="grouped GEMM per (N,K) pair", cold_hbm=True)
     return dict(ms_per_step=ms_per_step, wall_s=wall, step_flops=sum(p["flops"] for p in prepared),

@@ -53,6 +53,8 @@ CONFIGS = {
     "dense_large": [dict(M=4096, N=7168, K=16384, seed=200)],
     "contiguous": [dict(G=8, N=4096, K=7168, seed=300), dict(G=8, N=7168, K=2048, seed=301)],
     "masked": [dict(G=32, max_m=256, N=4096, K=7168, seed=400), dict(G=32, max_m=256, N=7168, K=2048, seed=401)],
+    # decode-sized masked calls: at most 128 tokens per expert
+    "masked_decode": [dict(G=32, max_m=128, N=4096, K=7168, seed=402), dict(G=32, max_m=128, N=7168, K=2048, seed=403)],
     # weight gradients of 8 local experts' up (4096 x 7168) and down (7168 x 2048) projections
     "k_grouped": [dict(G=8, M=4096, N=7168, seed=500), dict(G=8, M=7168, N=2048, seed=501)],
 }

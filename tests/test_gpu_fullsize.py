@@ -130,7 +130,8 @@ def test_contiguous_full_size(cfg):
         start += c
 
 
-@pytest.mark.parametrize("cfg", workloads.CONFIGS["masked"], ids=lambda c: f"G{c['G']}x{c['max_m']}-{c['N']}x{c['K']}")
+@pytest.mark.parametrize("cfg", workloads.CONFIGS["masked"] + workloads.CONFIGS["masked_decode"],
+                         ids=lambda c: f"G{c['G']}x{c['max_m']}-{c['N']}x{c['K']}")
 def test_masked_full_size(cfg):
     G, max_m, N, K, seed = cfg["G"], cfg["max_m"], cfg["N"], cfg["K"], cfg["seed"]
     print(f"masked G={G} max_m={max_m} {N}x{K} seed {seed}", flush=True)
