@@ -14,9 +14,10 @@
 //     split get ids 8 apart (the same XCD under round-robin dispatch);
 //   * A and the row scales alpha (shared by the four waves) and each wave's
 //     own B columns go HBM/L2 -> LDS with gfx950 buffer-to-LDS loads into a
-//     P-slot ring, P - 1 K blocks ahead (P = 8 for 16 columns per wave: the
-//     weight stream needs many bytes in flight per CU to cover HBM latency
-//     under load).  Fragments are read from LDS while the MFMAs run; the slot
+//     P-slot ring, P - 1 K blocks ahead (P = 4 for 64-row tiles, so two
+//     workgroups fit one CU and one's barrier wait hides behind the other's
+//     loads; 6 or 4 for 128-row tiles; deeper rings are compiled for
+//     measurement).  Fragments are read from LDS while the MFMAs run; the slot
 //     of block k - 1 is refilled only after the barrier of block k, which
 //     every wave reaches after its reads of block k - 1 have returned.  (B
 //     could go straight to registers, but the compiler's wait-count tracking
