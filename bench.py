@@ -21,10 +21,11 @@ the CPU oracle timed on a bounded sample of the same workload.
 
 The default run also times the M-grouped calls beside the step (not part of
 `value`): the contiguous form (8 experts, tokens per expert uniform in
-[1, 8192], (N, K) in {(4096, 7168), (7168, 2048)}) and the masked form
-(32 experts x 256 rows, masked_m uniform in [0, 256], same (N, K)), each call
-over rotating buffer sets; their rows join `per_shape` and `roofline_by_form`
-holds one roofline per form (--no-grouped skips them).
+[1, 8192], (N, K) in {(4096, 7168), (7168, 2048)}), the masked form
+(32 experts x 256 rows, masked_m uniform in [0, 256], same (N, K)) and its
+decode-sized configuration (32 experts x 128 rows, masked_m uniform in
+[0, 128]), each call over rotating buffer sets; their rows join `per_shape`
+and `roofline_by_form` holds one roofline per form (--no-grouped skips them).
 
 Other workloads: --workload large | small (one dense shape), contiguous | masked
 (the M-grouped forms as the timed step), masked_decode (the masked form with
@@ -797,7 +798,7 @@ def main():
             # (not part of `value`): per-call rows and one roofline per form
             r["roofline_by_form"] = {"dense": r["roofline"]}
             grouped_names = []
-            for form in ("contiguous", "masked"):
+            for form in ("contiguous", "masked", "masked_decode"):
                 torch.cuda.empty_cache()
                 g = run_grouped(args, torch, dg, workloads, form=form, timed=False)
                 r["per_shape"] = r["per_shape"] + g["per_shape"]
