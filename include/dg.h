@@ -303,9 +303,13 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
  * shape on the current device with a full workspace, e.g. "kernel=wide
  * tile=256x256 grid=256 tiles=448 whole=448 tail=0x1" (DG_OP_GEMM_NT,
  * DG_OP_GEMM_NT_UE8M0, DG_OP_BF16_GEMM_NT, DG_OP_CONTIGUOUS with rows = M_total
- * and G the expert count, and DG_OP_K_GROUPED with rows = M, G the group
- * count and K the total K; "" for other ops or invalid shapes); for a call
- * split into row chunks it describes the first chunk and ends in "chunks=n".
+ * and G the expert count, DG_OP_K_GROUPED with rows = M, G the group count
+ * and K the total K, and DG_OP_MASKED with rows = max_m and G the expert
+ * count, whose task count depends on masked_m and is given as its maximum;
+ * "" for invalid shapes); for a call split into row chunks it describes the
+ * first chunk and ends in "chunks=n".  "weights=nt" marks plans whose weight
+ * loads carry the non-temporal cache policy (each weight line read by one
+ * workgroup: dense calls with M <= 64, masked calls with max_m <= 128).
  * The pointer stays valid until the next call on the same thread.
  * Debugging aids, read from the environment on every call:
  *   DG_FORCE_CONFIG   comma-separated; "kernel=wide" / "kernel=persistent"

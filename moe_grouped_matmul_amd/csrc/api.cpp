@@ -430,9 +430,10 @@ int run_dense(DenseKind kind, const uint8_t* A, const void* sfa, const uint8_t* 
       if (pl.skinny)
         std::fprintf(stderr,
                      "[dg] %s M=%lld N=%lld K=%lld rows=%lld+%lld kernel=skinny tile=%dx%d m_tiles=%d n_tiles=%d splits=%d "
-                     "depth=%d\n",
+                     "depth=%d weights=%s\n",
                      kind_name(kind), (long long)M, (long long)N, (long long)K, (long long)r0, (long long)rows, pl.cfg,
-                     4 * pl.wn, pl.m_tiles, pl.n_tiles, pl.splits, pl.depth);
+                     4 * pl.wn, pl.m_tiles, pl.n_tiles, pl.splits, pl.depth,
+                     pl.cfg == 64 && pl.m_tiles == 1 ? "nt" : "default");
       else
         std::fprintf(stderr,
                      "[dg] %s M=%lld N=%lld K=%lld rows=%lld+%lld kernel=%s grid=%d tiles=%d whole=%d tail=%d x %d pieces of %d\n",
@@ -618,8 +619,9 @@ int run_masked(bool ue, const uint8_t* A, const void* sfa, const uint8_t* B, con
   const int ecus = effective_cus(cus);
   const int grid = (int)(tiles < ecus ? tiles : ecus);
   if (print_configs())
-    std::fprintf(stderr, "[dg] masked%s G=%lld max_m=%lld N=%lld K=%lld tile=128x256 kernel=persistent grid=%d\n",
-                 ue ? "_ue8m0" : "", (long long)G, (long long)max_m, (long long)N, (long long)K, grid);
+    std::fprintf(stderr, "[dg] masked%s G=%lld max_m=%lld N=%lld K=%lld tile=128x256 kernel=persistent grid=%d weights=%s\n",
+                 ue ? "_ue8m0" : "", (long long)G, (long long)max_m, (long long)N, (long long)K, grid,
+                 p.m_tiles == 1 ? "nt" : "default");
   const hipError_t e = dg::launch_gemm_persistent(ue ? dg::kMaskedUe8m0 : dg::kMasked, grid, p,
                                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
@@ -913,7 +915,7 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   thread_local std::string text;
   text.clear();
   if ((op != DG_OP_GEMM_NT && op != DG_OP_CONTIGUOUS && op != DG_OP_GEMM_NT_UE8M0 && op != DG_OP_BF16_GEMM_NT &&
-       op != DG_OP_K_GROUPED) ||
+       op != DG_OP_K_GROUPED && op != DG_OP_MASKED) ||
       rows <= 0 || N <= 0 || K <= 0 || K % (op == DG_OP_BF16_GEMM_NT ? 64 : 128) || N % 16)
     return text.c_str();
   const int ecus = effective_cus(query_cus());
@@ -925,6 +927,15 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
     const ContigPlan cp = plan_contiguous(r, N, K, ecus);
     std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx256 grid=%d tiles=%lld chunks=%lld", cp.wide ? "wide" : "persistent",
                   cp.wide ? 256 : 128, cp.grid, (long long)cp.tiles, (long long)ceil_div(rows, chunk));
+    text = buf;
+    return text.c_str();
+  }
+  if (op == DG_OP_MASKED) {  // rows = max_m, G experts; the weights stream non-temporally with one row tile
+    const int64_t g = G < 1 ? 1 : G;
+    const int64_t mt = ceil_div(rows, 128);
+    const int64_t tiles = g * mt * ceil_div(N, 256);
+    std::snprintf(buf, sizeof(buf), "kernel=persistent tile=128x256 grid=%lld max_tiles=%lld weights=%s",
+                  (long long)(tiles < ecus ? tiles : ecus), (long long)tiles, mt == 1 ? "nt" : "default");
     text = buf;
     return text.c_str();
   }
@@ -947,8 +958,9 @@ const char* dg_describe_plan(int op, int64_t rows, int64_t N, int64_t K, int64_t
   const int64_t r = std::min(rows, chunk);
   const DensePlan pl = plan_dense(kind, r, N, K, ecus, (size_t)-1);
   if (pl.skinny)
-    std::snprintf(buf, sizeof(buf), "kernel=skinny tile=%dx%d tiles=%d splits=%d chunks=%lld", pl.cfg, 4 * pl.wn,
-                  pl.m_tiles * pl.n_tiles, pl.splits, (long long)ceil_div(rows, chunk));
+    std::snprintf(buf, sizeof(buf), "kernel=skinny tile=%dx%d tiles=%d splits=%d weights=%s chunks=%lld", pl.cfg,
+                  4 * pl.wn, pl.m_tiles * pl.n_tiles, pl.splits, pl.cfg == 64 && pl.m_tiles == 1 ? "nt" : "default",
+                  (long long)ceil_div(rows, chunk));
   else
     std::snprintf(buf, sizeof(buf), "kernel=%s tile=%dx%d grid=%d tiles=%d whole=%d tail=%dx%d chunks=%lld",
                   pl.wide ? "wide" : "persistent", 256, pl.wide ? 256 : 128, pl.grid, pl.m_tiles * pl.n_tiles,

@@ -217,10 +217,17 @@ def test_dense_planner_choice(lib):
         assert "tile=64x64" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 4096, 7168)
         assert "tile=64x64" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 16384)
         assert "tail=16x4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)
+        # weight loads streamed non-temporally where one workgroup reads each weight line
+        assert "splits=5 weights=nt" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 2112, 7168)
+        assert "weights=default" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 2112, 7168)   # two 64-row tiles
+        assert "weights=default" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 128, 7168, 16384)  # one 128-row tile
+        assert dg.dg_describe_plan(dg.DG_OP_MASKED, 128, 4096, 7168, 32) == \
+            "kernel=persistent tile=128x256 grid=256 max_tiles=512 weights=nt"
+        assert dg.dg_describe_plan(dg.DG_OP_MASKED, 256, 4096, 7168, 32).endswith("max_tiles=1024 weights=default")
         dg.dg_set_num_cus(4)
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 384)          # 4 tiles on 4 CUs
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 100) == ""                      # invalid K
-        assert dg.dg_describe_plan(dg.DG_OP_MASKED, 500, 496, 384) == ""
+        assert dg.dg_describe_plan(dg.DG_OP_MASKED, 500, 496, 100) == ""                      # invalid K
         dg.dg_set_num_cus(256)
         # contiguous: 256 x 256 tiles when K >= 4096 and they fill whole rounds
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 36000, 4096, 7168, 8)
