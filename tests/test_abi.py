@@ -258,3 +258,41 @@ def test_forced_config_parsing(lib, monkeypatch):
         assert "kernel=wide tile=256x256 grid=27 tiles=27" in plan and plan.endswith("chunks=6")  # 5 x 768 + 256 rows
     finally:
         dg.dg_set_num_cus(0)
+
+
+def test_errors_are_thread_local(lib):
+    # host logic only: concurrent calls failing for different reasons each read
+    # back their own message (dg_get_last_error is per thread), and the
+    # validation and plan description are safe to call from several threads
+    import threading
+
+    from moe_grouped_matmul_amd import dg
+
+    s = ctypes.c_void_p(0)
+    cases = [
+        (lambda: lib.dg_fp8_gemm_nt(P16, P16, P16, P16, P16, 64, 2112, 7000, None, 0, s), dg.DG_ERR_SHAPE, "K"),
+        (lambda: lib.dg_fp8_gemm_nt(P16, P16, P16, P16, P16, 64, 2110, 7168, None, 0, s), dg.DG_ERR_SHAPE, "N"),
+        (lambda: lib.dg_m_grouped_fp8_gemm_nt_contiguous(P16, P16, P16, P16, P16, P16, 256, 128, 256, 1025, None, 0, s),
+         dg.DG_ERR_SHAPE, "G"),
+        (lambda: lib.dg_fp8_gemm_nt(P16 + 8, P16, P16, P16, P16, 64, 2112, 7168, None, 0, s), dg.DG_ERR_ALIGN,
+         "align"),
+    ]
+    failures = []
+    barrier = threading.Barrier(len(cases))
+
+    def worker(call, code, word):
+        barrier.wait()
+        for _ in range(200):
+            rc = call()
+            msg = lib.dg_get_last_error().decode()
+            plan = lib.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384, 1)
+            if rc != code or word not in msg or not plan:
+                failures.append((rc, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not failures, failures[:3]
