@@ -13,10 +13,11 @@
 // DG_FORCE_CONFIG (debug, read on every call): a comma-separated list of
 //   kernel=wide|persistent  force the 256x256 or the 256x128 / 128x256 tile
 //                           kernel where the planner chooses between them
-//                           (rows > 128, or the contiguous form)
+//                           (rows > 128 outside the skinny domain, or the
+//                           contiguous form)
 //   chunk_rows=<n>          at most n rows per launch (rounded down to a
 //                           multiple of 256, at least 256)
-//   skinny=<bm>x<wn>x<s>x<p>  rows <= 128: bm-row tiles (64 | 128) of 4 wn
+//   skinny=<bm>x<wn>x<s>x<p>  rows <= 256: bm-row tiles (64 | 128) of 4 wn
 //                           columns (wn 16 | 32), K split s ways (bounded by
 //                           the K blocks and the workspace), ring depth p
 //                           among the compiled ones (dg::skinny_depth_ok)
@@ -217,7 +218,7 @@ bool kgrouped_wide(int64_t G, int64_t M, int64_t N, int cus) {
 struct DensePlan {
   bool wide = false;    // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
   bool persist = false; // persistent kernel (gemm_persist.hip): 256 x 128 tiles, K-split tail
-  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 128
+  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 256
   int grid = 0;         // wide / persistent: workgroups
   int dp_tiles = 0, sk_tiles = 0, sk_pieces = 1, sk_kb = 0;
   int cfg = 0;          // skinny rows per tile (64 | 128)
@@ -297,18 +298,19 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
   pl.skinny = true;
   // 64 < M <= 128: one 128-row tile (weights read once) when the columns
   // alone nearly fill the CUs; otherwise two 64-row tiles, whose split-K
-  // partials are half as large per tile
-  pl.cfg = (M <= 64 || ceil_div(N, 64) < cus / 2) ? 64 : 128;
+  // partials are half as large per tile.  128 < M <= 256: 64-row tiles of 64
+  // columns (measured fastest there against 128 x 128 tiles)
+  pl.cfg = (M <= 64 || M > 128 || ceil_div(N, 64) < cus / 2) ? 64 : 128;
   pl.m_tiles = (int)ceil_div(M, pl.cfg);
   const int64_t t16 = pl.m_tiles * ceil_div(N, 64);
   const int64_t t32 = pl.m_tiles * ceil_div(N, 128);
   auto fill = [&](int64_t t) { return (double)t / (double)(ceil_div(t, cus) * cus); };
-  pl.wn = (t16 >= cus && fill(t32) >= fill(t16)) ? 32 : 16;
+  pl.wn = (M <= 128 && t16 >= cus && fill(t32) >= fill(t16)) ? 32 : 16;
   int cap_rows = pl.cfg;  // K split capped at K / (20 * cap_rows): partials (splits * bm * 4 B per column) <= K / 5
   // 64 < M <= 128 with two 64-row tiles: each streams all of A beside its
   // columns of B; one 128 x 128 tile halves those A reads, and wins where it
   // still fills the CUs through a K split (partials then up to K / 2.5 per column)
-  if (M > 64 && pl.cfg == 64) {
+  if (M > 64 && M <= 128 && pl.cfg == 64) {
     const int64_t t128 = ceil_div(N, 128);
     int64_t s128 = t128 < cus ? cus / t128 : 1;
     if (s128 > K / 1280) s128 = K / 1280;
@@ -356,9 +358,10 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
   pl.splits = (int)ceil_div(KB, pl.kb_per_split);
 }
 
-// The dense forms.  kFp8 / kAcc / kUe8m0: skinny for M <= 128, else 256 x 256
-// tiles where they fill whole rounds, else 256 x 128 tiles with a K-split
-// tail.  kBf16: 256 x 256 tiles where they fill whole rounds, else 256 x 128
+// The dense forms.  kFp8 / kAcc / kUe8m0: skinny for M <= 128 (and for
+// M <= 256 where the 256 x 128 tiles would leave half the CUs idle and
+// K <= 8192), else 256 x 256 tiles where they fill whole rounds, else
+// 256 x 128 tiles with a K-split tail.  kBf16: 256 x 256 tiles where they fill whole rounds, else 256 x 128
 // tiles.  DG_FORCE_CONFIG=kernel=... overrides the wide / 256 x 128 choice
 // for M > 128 (and for the BF16 form at any M >= 1).
 enum DenseKind { kFp8 = 0, kAcc = 1, kUe8m0 = 2, kBf16 = 3 };
@@ -367,7 +370,13 @@ DensePlan plan_dense(DenseKind kind, int64_t M, int64_t N, int64_t K, int cus, s
   DensePlan pl;
   const int64_t kbytes = kind == kBf16 ? 2 * K : K;  // bytes per operand row
   const Force f = forced();
-  if (kind != kBf16 && M <= 128) {
+  // 128 < M <= 256: the decode kernel where the 256 x 128 tiles would all be
+  // split along K (at most half the CUs' worth of tiles) and K is moderate;
+  // measured 30-58% faster there, and slower at K = 16384 or with a whole
+  // round of tiles
+  const bool mid = M > 128 && M <= 256 && f.kernel == kForceNone &&
+                   (f.sk_bm || (2 * ceil_div(N, 128) <= cus && K <= 8192));
+  if (kind != kBf16 && (M <= 128 || mid)) {
     plan_skinny(pl, M, N, K, cus, ws_bytes);
     return pl;
   }

@@ -1,5 +1,6 @@
-// Block-scaled FP8 GEMM for gfx950 when M is small (decode, M <= 128): the
-// weights B dominate the traffic and are streamed from HBM exactly once.
+// Block-scaled FP8 GEMM for gfx950 when M is small (decode, M <= 128, and
+// M <= 256 where the output has few columns): the weights B dominate the
+// traffic and are streamed from HBM once per row tile, through L2.
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: every 128-wide K block's fp8 partial product is
@@ -8,7 +9,8 @@
 //
 // Organisation:
 //   * a workgroup is 4 wave64s (one per SIMD) and owns a BM-row tile of A
-//     (BM = 64, or 128 when 64 < M <= 128, so the weights are read once)
+//     (BM = 64, or 128 when 64 < M <= 128, so the weights are read once;
+//     three or four 64-row tiles when 128 < M <= 256)
 //     times BN = 4 * WN columns of B; each wave owns WN columns.  Should
 //     there be several row tiles, the workgroups of one column tile and K
 //     split get ids 8 apart (the same XCD under round-robin dispatch);

@@ -224,6 +224,17 @@ def test_dense_planner_choice(lib):
         assert dg.dg_describe_plan(dg.DG_OP_MASKED, 128, 4096, 7168, 32) == \
             "kernel=persistent tile=128x256 grid=256 max_tiles=512 weights=nt"
         assert dg.dg_describe_plan(dg.DG_OP_MASKED, 256, 4096, 7168, 32).endswith("max_tiles=1024 weights=default")
+        # 128 < M <= 256: 64 x 64 skinny tiles where the 256 x 128 tiles would
+        # fill at most half the CUs and K <= 8192; otherwise the tile kernels
+        assert "kernel=skinny tile=64x64 tiles=99 splits=2 weights=default" in \
+            dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 160, 2112, 7168)
+        assert "kernel=skinny tile=64x64 tiles=448 splits=1" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 256, 7168, 2048)
+        assert "kernel=skinny tile=64x64 tiles=132" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 256, 2112, 7168)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 192, 7168, 16384)   # K > 8192
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 256, 24576, 1536)   # 192 tiles
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 257, 2112, 7168)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 160, 2112, 7168)
+        assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, 160, 2112, 7168) > 0
         dg.dg_set_num_cus(4)
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 384)          # 4 tiles on 4 CUs
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 100) == ""                      # invalid K
@@ -251,8 +262,12 @@ def test_forced_config_parsing(lib, monkeypatch):
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
         monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x32")  # malformed
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x16x4x8")  # honoured up to 256 rows
+        assert "kernel=skinny tile=64x64 tiles=176 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 200, 2816, 1024)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 300, 2816, 1024)
         monkeypatch.setenv("DG_FORCE_CONFIG", "kernel=persistent")
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 160, 2112, 7168)
         monkeypatch.setenv("DG_FORCE_CONFIG", "kernel=wide,chunk_rows=1000")
         plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)
         assert "kernel=wide tile=256x256 grid=27 tiles=27" in plan and plan.endswith("chunks=6")  # 5 x 768 + 256 rows

@@ -241,16 +241,22 @@ SKINNY = [(1, 2112, 7168), (17, 144, 1024), (64, 2112, 7168), (100, 272, 4096), 
           (64, 4096, 640), (128, 32768, 512), (33, 24576, 1536), (64, 7168, 2048),
           (100, 7168, 5120)]  # the last: one 128-row tile of 128 columns, K split in 4
 
+# skinny kernel with three or four 64-row tiles (128 < M <= 256, few columns,
+# K <= 8192), with and without a K split, ragged last row tile
+SKINNY_MID = [(129, 144, 640), (160, 2112, 7168), (193, 400, 1024), (256, 7168, 2048), (250, 1008, 3072)]
+
 
 # persistent kernel (M > 128): tile counts that leave a partial last round, so
 # tail tiles are split along K into pieces (2 to 4, including a short last
 # piece), again with one workspace reused across calls
-PERSISTENT_TAIL = [(130, 144, 640), (257, 400, 384), (300, 272, 1024), (1000, 528, 512), (777, 2112, 640),
+PERSISTENT_TAIL = [(200, 144, 9216), (257, 400, 384), (300, 272, 1024), (1000, 528, 512), (777, 2112, 640),
                    (2048, 4096, 1536)]
 
 
-@pytest.mark.parametrize("M,N,K", SKINNY + PERSISTENT_TAIL)
+@pytest.mark.parametrize("M,N,K", SKINNY + SKINNY_MID + PERSISTENT_TAIL)
 def test_dense_skinny_matches_oracle_with_reused_workspace(M, N, K):
+    plan = dg.dg_describe_plan(dg.DG_OP_GEMM_NT, M, N, K)
+    assert ("kernel=skinny" in plan) == ((M, N, K) in SKINNY + SKINNY_MID), plan
     a32, b32 = workloads.dense(M, N, K, seed=M + 3 * N + K)
     qa, sa = oracle.quant_1x128(a32)
     qb, sb = oracle.quant_128x128(b32)

@@ -155,13 +155,17 @@ def test_gemm_ue8m0_bit_identical_to_fp32_scale_kernel(M, N, K):
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
 
 
-# (M, N, K, forced plan): rows <= 128 run the skinny kernel; the forced plans
-# reach every compiled (tile rows, columns per wave, ring depth) instance with
-# a K split, ragged M and N, and K blocks not a multiple of four
+# (M, N, K, forced plan): rows <= 128 (and rows <= 256 with few columns) run
+# the skinny kernel; the forced plans reach every compiled (tile rows, columns
+# per wave, ring depth) instance with a K split, ragged M and N, and K blocks
+# not a multiple of four, also with several row tiles
 SKINNY = [(1, 16, 128, None), (37, 400, 640, None), (100, 528, 1152, None), (64, 2112, 7168, None),
-          (128, 7168, 2048, None), (50, 272, 640, "skinny=64x16x2x4"), (64, 400, 1024, "skinny=64x16x3x8"),
+          (128, 7168, 2048, None), (160, 2112, 7168, None), (230, 528, 1152, None),
+          (50, 272, 640, "skinny=64x16x2x4"), (64, 400, 1024, "skinny=64x16x3x8"),
           (64, 528, 1152, "skinny=64x32x3x4"), (61, 528, 1024, "skinny=64x32x2x6"),
-          (128, 272, 896, "skinny=128x16x2x6"), (120, 528, 1152, "skinny=128x32x3x4")]
+          (128, 272, 896, "skinny=128x16x2x6"), (120, 528, 1152, "skinny=128x32x3x4"),
+          (200, 528, 1152, "skinny=64x32x3x4"), (256, 272, 896, "skinny=128x16x2x6"),
+          (170, 528, 1152, "skinny=128x32x3x4")]
 
 
 @pytest.mark.parametrize("M,N,K,force", SKINNY)
