@@ -17,7 +17,7 @@
 //                           contiguous form)
 //   chunk_rows=<n>          at most n rows per launch (rounded down to a
 //                           multiple of 256, at least 256)
-//   skinny=<bm>x<wn>x<s>x<p>  rows <= 256: bm-row tiles (64 | 128) of 4 wn
+//   skinny=<bm>x<wn>x<s>x<p>  rows <= 512: bm-row tiles (64 | 128) of 4 wn
 //                           columns (wn 16 | 32), K split s ways (bounded by
 //                           the K blocks and the workspace), ring depth p
 //                           among the compiled ones (dg::skinny_depth_ok)
@@ -218,7 +218,7 @@ bool kgrouped_wide(int64_t G, int64_t M, int64_t N, int cus) {
 struct DensePlan {
   bool wide = false;    // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
   bool persist = false; // persistent kernel (gemm_persist.hip): 256 x 128 tiles, K-split tail
-  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 256
+  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 512
   int grid = 0;         // wide / persistent: workgroups
   int dp_tiles = 0, sk_tiles = 0, sk_pieces = 1, sk_kb = 0;
   int cfg = 0;          // skinny rows per tile (64 | 128)
@@ -293,6 +293,31 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
 // of tile shape, split and ring depth on the decode shapes of the dense sweep,
 // each configuration with a freshly zeroed workspace: no configuration beat
 // this rule by more than the run-to-run spread.)
+// Estimated time (us) of a skinny plan with bm x 4wn tiles and a K split of
+// s, for 256 < M <= 512, from the bytes each CU pulls: a workgroup streams
+// (bm + 4 wn) rows of its K range; 64 x 64 tiles run two workgroups per CU
+// (sharing the CU's rate), the larger ones one; the grid is padded to whole
+// groups of 8 units per row tile and runs in rounds of cus (x2) workgroups;
+// a split adds its partial store and the last split's read-back.  The
+// constants (per-CU rate 60 GB/s with two workgroups, 50 GB/s with one,
+// 3.5 us launch, 3 us fix-up latency) were tuned on forced-plan timings of
+// 40 shapes at 288-512 rows: the plan they pick was on average 1% and at
+// most 16% slower than the fastest plan timed for the shape.
+double skinny_cost_us(int64_t M, int64_t N, int64_t K, int bm, int wn, int s, int cus) {
+  const int64_t KB = K / 128;
+  const int64_t kbs = ceil_div(KB, s);
+  s = (int)ceil_div(KB, kbs);
+  const int64_t bn = 4 * wn;
+  const int64_t mt = ceil_div(M, bm), nt = ceil_div(N, bn);
+  const int occ = (bm == 64 && wn == 16) ? 2 : 1;
+  const int64_t grid = ceil_div(nt * s, 8) * 8 * mt;
+  const double bytes = (double)((bm + bn) * kbs * 128);
+  const double rounds = (double)ceil_div(grid, (int64_t)cus * occ);
+  double t = (occ == 2 && grid > cus) ? rounds * 2.0 * bytes / 60e3 : rounds * bytes / 50e3;
+  if (s > 1) t += 3.0 + (double)s * (double)(bm * bn * 4) / 50e3;
+  return 3.5 + t;
+}
+
 void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   const int KB = (int)(K / 128);
   pl.skinny = true;
@@ -337,6 +362,28 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
       --splits;
     if (splits < 2) splits = 1;
   }
+  if (M > 256) {  // 256 < M <= 512: the tile shape and split of least estimated time
+    const int shapes[3][2] = {{64, 16}, {64, 32}, {128, 32}};
+    double best = -1.0;
+    for (const auto& sh : shapes) {
+      const int mt = (int)ceil_div(M, sh[0]), nt = (int)ceil_div(N, 4 * sh[1]);
+      const int cap = (int)(K / (20 * sh[0]));
+      for (int s = 1; s <= 4; ++s) {
+        if (s > 1 && (s > cap || (int64_t)mt * nt > dg::kWsMaxCounters ||
+                      dg::skinny_workspace_bytes(sh[0], mt, nt, sh[1], s) > ws_bytes))
+          break;
+        const double t = skinny_cost_us(M, N, K, sh[0], sh[1], s, cus);
+        if (best < 0.0 || t < best) {
+          best = t;
+          pl.cfg = sh[0];
+          pl.wn = sh[1];
+          pl.m_tiles = mt;
+          pl.n_tiles = nt;
+          splits = s;
+        }
+      }
+    }
+  }
   int depth = dg::skinny_depth(pl.cfg, pl.wn);
   const Force f = forced();
   if (f.sk_bm) {  // DG_FORCE_CONFIG=skinny=...
@@ -359,8 +406,7 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
 }
 
 // The dense forms.  kFp8 / kAcc / kUe8m0: skinny for M <= 128 (and for
-// M <= 256 where the 256 x 128 tiles would leave half the CUs idle and
-// K <= 8192), else 256 x 256 tiles where they fill whole rounds, else
+// M <= 512 where 2 ceil(N / 128) <= CUs and K <= 8192), else 256 x 256 tiles where they fill whole rounds, else
 // 256 x 128 tiles with a K-split tail.  kBf16: 256 x 256 tiles where they fill whole rounds, else 256 x 128
 // tiles.  DG_FORCE_CONFIG=kernel=... overrides the wide / 256 x 128 choice
 // for M > 128 (and for the BF16 form at any M >= 1).
@@ -370,11 +416,12 @@ DensePlan plan_dense(DenseKind kind, int64_t M, int64_t N, int64_t K, int cus, s
   DensePlan pl;
   const int64_t kbytes = kind == kBf16 ? 2 * K : K;  // bytes per operand row
   const Force f = forced();
-  // 128 < M <= 256: the decode kernel where the 256 x 128 tiles would all be
-  // split along K (at most half the CUs' worth of tiles) and K is moderate;
-  // measured 30-58% faster there, and slower at K = 16384 or with a whole
-  // round of tiles
-  const bool mid = M > 128 && M <= 256 && f.kernel == kForceNone &&
+  // 128 < M <= 512: the decode kernel where the output has few columns
+  // (2 ceil(N / 128) <= CUs: at most half the CUs' worth of 256 x 128 tiles
+  // per row tile, all of them split along K below 257 rows) and K is
+  // moderate; measured 1.1-3.4x faster there, and slower at K = 16384 or
+  // with more columns
+  const bool mid = M > 128 && M <= 512 && f.kernel == kForceNone &&
                    (f.sk_bm || (2 * ceil_div(N, 128) <= cus && K <= 8192));
   if (kind != kBf16 && (M <= 128 || mid)) {
     plan_skinny(pl, M, N, K, cus, ws_bytes);

@@ -1,5 +1,5 @@
 // Block-scaled FP8 GEMM for gfx950 when M is small (decode, M <= 128, and
-// M <= 256 where the output has few columns): the weights B dominate the
+// M <= 512 where the output has few columns): the weights B dominate the
 // traffic and are streamed from HBM once per row tile, through L2.
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
@@ -10,7 +10,7 @@
 // Organisation:
 //   * a workgroup is 4 wave64s (one per SIMD) and owns a BM-row tile of A
 //     (BM = 64, or 128 when 64 < M <= 128, so the weights are read once;
-//     three or four 64-row tiles when 128 < M <= 256)
+//     several row tiles of 64 or 128 rows when 128 < M <= 512)
 //     times BN = 4 * WN columns of B; each wave owns WN columns.  Should
 //     there be several row tiles, the workgroups of one column tile and K
 //     split get ids 8 apart (the same XCD under round-robin dispatch);

@@ -232,7 +232,17 @@ def test_dense_planner_choice(lib):
         assert "kernel=skinny tile=64x64 tiles=132" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 256, 2112, 7168)
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 192, 7168, 16384)   # K > 8192
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 256, 24576, 1536)   # 192 tiles
-        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 257, 2112, 7168)
+        # 256 < M <= 512: 64x64, 64x128 or 128x128 tiles and a K split of at most
+        # 4, the least estimated time from the bytes each CU pulls
+        assert "kernel=skinny tile=64x64 tiles=231 splits=2" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 448, 2112, 7168)
+        assert "kernel=skinny tile=64x128 tiles=119 splits=1" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 400, 2112, 1024)
+        assert "kernel=skinny tile=128x128 tiles=224 splits=1" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 512, 7168, 2048)
+        assert "kernel=skinny tile=128x128 tiles=128 splits=2" in \
+            dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 512, 4096, 7168)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 512, 24576, 1536)   # 384 tiles
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 320, 7168, 16384)   # K > 8192
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 513, 2112, 7168)
+        assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, 448, 2112, 7168) > 0
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 160, 2112, 7168)
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, 160, 2112, 7168) > 0
         dg.dg_set_num_cus(4)
@@ -262,9 +272,10 @@ def test_forced_config_parsing(lib, monkeypatch):
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
         monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x32")  # malformed
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
-        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x16x4x8")  # honoured up to 256 rows
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x16x4x8")  # honoured up to 512 rows
         assert "kernel=skinny tile=64x64 tiles=176 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 200, 2816, 1024)
-        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 300, 2816, 1024)
+        assert "kernel=skinny tile=64x64 tiles=352 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 2816, 1024)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 513, 2816, 1024)
         monkeypatch.setenv("DG_FORCE_CONFIG", "kernel=persistent")
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 160, 2112, 7168)

@@ -1,7 +1,8 @@
 """The allocation-free dense entry point (dg_fp8_gemm_nt_noalloc) against the
 one that takes a workspace (dg_fp8_gemm_nt): same plan, so bit-identical
 outputs, on consecutive calls of decreasing size that share the static
-scratch (K splits of 128-row and 64-row skinny tiles, K-split tail pieces of
+scratch (K splits of 128-row and 64-row skinny tiles, the latter also three
+row tiles deep, K-split tail pieces of
 the persistent kernel), each also within the per-element rule of the oracle
 (Lesson 13, Fig. 13-1); a captured graph of the call replayed with eager work
 between replays; and the rejection of a plan whose scratch exceeds the
@@ -37,7 +38,8 @@ def _operands(M, N, K, seed):
 
 
 # decreasing sizes; every plan splits K and so uses the scratch
-CALLS = [(128, 7168, 16384, "tile=128x128"), (64, 2112, 7168, "tile=64x64"), (4096, 2112, 7168, "tail=16x4")]
+CALLS = [(128, 7168, 16384, "tile=128x128"), (160, 2112, 7168, "tile=64x64 tiles=99 splits=2"),
+         (64, 2112, 7168, "tile=64x64"), (4096, 2112, 7168, "tail=16x4")]
 
 
 def test_noalloc_equals_workspace_entry_point_on_consecutive_calls():
