@@ -69,7 +69,8 @@
 // rows tagged with that expert; a tile without a valid index is none.  A
 // pass whose rows lie in one 128-row half runs the MFMAs of that half's four
 // waves only (each SIMD holds one wave of each half) and loads no A rows of
-// the other half, so a straddling tile costs about one full pass.
+// the other half, so a straddling tile costs about one full pass.  A pass
+// loads the A rows tagged with its expert only.
 
 #include "dg_internal.hpp"
 #include "gemm_common.hpp"
@@ -343,7 +344,11 @@ __global__ void __launch_bounds__(512) fp8_gemm_wide_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int r = 64 * i + a_loc;
-      is_aoff[i] = r < row_limit && ((hm >> (r >> 7)) & 1) ? (uint32_t)(mt * BM + r) * (uint32_t)K + dma_chunk : kWideOOB;
+      bool ld = r < row_limit && ((hm >> (r >> 7)) & 1);
+      // contiguous: only the rows tagged with the pass's expert (padding rows
+      // and another expert's rows are never stored, so their A is not read)
+      if constexpr (CONTIG) ld = ld && ((pass_mask[is_seg][r >> 5] >> (r & 31)) & 1u);
+      is_aoff[i] = ld ? (uint32_t)(mt * BM + r) * (uint32_t)K + dma_chunk : kWideOOB;
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
