@@ -92,10 +92,10 @@ enum {
  *   deterministic).  Required size for the full split is
  *   dg_get_workspace_size(DG_OP_GEMM_NT, M, N, K, 1); a smaller buffer limits
  *   the split.  The workspace MUST be zero-filled before its first use (e.g.
- *   hipMemset once after allocation): whenever the plan splits K (M <= 512
- *   on the skinny kernel, or a partial last round of 256 x 128 tiles) its first 4 KiB hold per-tile
- *   completion counters and the fp32 partials follow; every call leaves the
- *   counters at zero again, so a workspace stays reusable across calls and
+ *   hipMemset once after allocation): whenever the plan splits K (the
+ *   skinny kernel, at up to 2048 rows, or a partial last round of 256 x 128
+ *   tiles) its first 4 KiB hold per-tile completion counters and the fp32
+ *   partials follow; every call leaves the counters at zero again, so a workspace stays reusable across calls and
  *   shapes without clearing.  Calls that share one workspace must be ordered
  *   on one stream.
  */
@@ -318,7 +318,7 @@ size_t dg_get_workspace_size(int op, int64_t rows, int64_t N, int64_t K, int64_t
  *                     "chunk_rows=<n>" splits calls into row chunks of at
  *                     most n rows (rounded down to a multiple of 256, at
  *                     least 256), and "skinny=<bm>x<wn>x<s>x<p>" makes calls
- *                     with at most 512 rows use bm-row tiles (64 or 128) of
+ *                     with at most 2048 rows use bm-row tiles (64 or 128) of
  *                     4 wn columns (wn 16 or 32), a K split of s (bounded by
  *                     the K blocks and the workspace) and ring depth p (one
  *                     of the compiled depths; other values are ignored);

@@ -17,7 +17,7 @@
 //                           contiguous form)
 //   chunk_rows=<n>          at most n rows per launch (rounded down to a
 //                           multiple of 256, at least 256)
-//   skinny=<bm>x<wn>x<s>x<p>  rows <= 512: bm-row tiles (64 | 128) of 4 wn
+//   skinny=<bm>x<wn>x<s>x<p>  rows <= 2048: bm-row tiles (64 | 128) of 4 wn
 //                           columns (wn 16 | 32), K split s ways (bounded by
 //                           the K blocks and the workspace), ring depth p
 //                           among the compiled ones (dg::skinny_depth_ok)
@@ -218,7 +218,7 @@ bool kgrouped_wide(int64_t G, int64_t M, int64_t N, int cus) {
 struct DensePlan {
   bool wide = false;    // wide-tile persistent kernel (gemm_wide.hip): 256 x 256 tiles, no K split
   bool persist = false; // persistent kernel (gemm_persist.hip): 256 x 128 tiles, K-split tail
-  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 512
+  bool skinny = false;  // skinny kernel (gemm_skinny.hip), M <= 2048
   int grid = 0;         // wide / persistent: workgroups
   int dp_tiles = 0, sk_tiles = 0, sk_pieces = 1, sk_kb = 0;
   int cfg = 0;          // skinny rows per tile (64 | 128)
@@ -284,17 +284,8 @@ void plan_persistent(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, si
   pl.grid = (int)g;
 }
 
-// Skinny kernel (one workgroup per CU): column width and K split chosen so
-// the workgroups fill the CUs in whole rounds.  Without a split the wider
-// tile wins ties; with one, 16-column waves give the most tiles, and the split
-// is at most K / (20 bm) (the fp32 partials then stay below a fifth of the
-// weight bytes; more splits lose more in the fix-up than they gain), at most
-// 16, and only as large as the workspace holds.  (Re-measured against a sweep
-// of tile shape, split and ring depth on the decode shapes of the dense sweep,
-// each configuration with a freshly zeroed workspace: no configuration beat
-// this rule by more than the run-to-run spread.)
 // Estimated time (us) of a skinny plan with bm x 4wn tiles and a K split of
-// s, for 256 < M <= 512, from the bytes each CU pulls: a workgroup streams
+// s, for 256 < M <= 2048, from the bytes each CU pulls: a workgroup streams
 // (bm + 4 wn) rows of its K range; 64 x 64 tiles run two workgroups per CU
 // (sharing the CU's rate), the larger ones one; the grid is padded to whole
 // groups of 8 units per row tile and runs in rounds of cus (x2) workgroups;
@@ -318,6 +309,57 @@ double skinny_cost_us(int64_t M, int64_t N, int64_t K, int bm, int wn, int s, in
   return 3.5 + t;
 }
 
+// The skinny plan of least estimated time over 64 x 64, 64 x 128 and
+// 128 x 128 tiles and K splits of 1-4; a split only where its workgroups
+// still run in one round (so its partials stay within 16 MiB) and fit the
+// workspace.  Returns the estimate.
+double best_skinny(int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes, int* bm, int* wn, int* splits) {
+  const int shapes[3][2] = {{64, 16}, {64, 32}, {128, 32}};
+  double best = -1.0;
+  for (const auto& sh : shapes) {
+    const int64_t mt = ceil_div(M, sh[0]), nt = ceil_div(N, 4 * sh[1]);
+    const int occ = sh[0] == 64 && sh[1] == 16 ? 2 : 1;
+    const int cap = (int)(K / (20 * sh[0]));
+    for (int s = 1; s <= 4; ++s) {
+      if (s > 1 && (s > cap || mt * nt * s > (int64_t)cus * occ || mt * nt > dg::kWsMaxCounters ||
+                    dg::skinny_workspace_bytes(sh[0], (int)mt, (int)nt, sh[1], s) > ws_bytes))
+        break;
+      const double t = skinny_cost_us(M, N, K, sh[0], sh[1], s, cus);
+      if (best < 0.0 || t < best) {
+        best = t;
+        *bm = sh[0];
+        *wn = sh[1];
+        *splits = s;
+      }
+    }
+  }
+  return best;
+}
+
+// Estimated time (us) of a 256 x 128 tile plan: its whole rounds of tiles,
+// then the tail's K pieces and their fix-up (the last piece of a tile reads
+// the others' 128 KB partials).  Constants fitted to default-plan timings of
+// 126 shapes at 129-2048 rows (per-CU rate 61 GB/s, 9.5 us fixed, 5.5 us
+// fix-up latency; mean error 10%).
+double persistent_cost_us(const DensePlan& pl, int64_t K) {
+  const double tb = 384.0 * 128.0;  // A and B bytes of one K block of a tile
+  double t = pl.dp_tiles ? (double)ceil_div(pl.dp_tiles, pl.grid) * (double)(K / 128) * tb / 61e3 : 0.0;
+  if (pl.sk_tiles) {
+    t += (double)pl.sk_kb * tb / 61e3;
+    if (pl.sk_pieces > 1) t += 5.5 + (double)pl.sk_pieces * 256.0 * 128.0 * 4.0 / 61e3;
+  }
+  return 9.5 + t;
+}
+
+// Skinny kernel (one workgroup per CU): column width and K split chosen so
+// the workgroups fill the CUs in whole rounds.  Without a split the wider
+// tile wins ties; with one, 16-column waves give the most tiles, and the split
+// is at most K / (20 bm) (the fp32 partials then stay below a fifth of the
+// weight bytes; more splits lose more in the fix-up than they gain), at most
+// 16, and only as large as the workspace holds.  (Re-measured against a sweep
+// of tile shape, split and ring depth on the decode shapes of the dense sweep,
+// each configuration with a freshly zeroed workspace: no configuration beat
+// this rule by more than the run-to-run spread.)
 void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t ws_bytes) {
   const int KB = (int)(K / 128);
   pl.skinny = true;
@@ -362,27 +404,10 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
       --splits;
     if (splits < 2) splits = 1;
   }
-  if (M > 256) {  // 256 < M <= 512: the tile shape and split of least estimated time
-    const int shapes[3][2] = {{64, 16}, {64, 32}, {128, 32}};
-    double best = -1.0;
-    for (const auto& sh : shapes) {
-      const int mt = (int)ceil_div(M, sh[0]), nt = (int)ceil_div(N, 4 * sh[1]);
-      const int cap = (int)(K / (20 * sh[0]));
-      for (int s = 1; s <= 4; ++s) {
-        if (s > 1 && (s > cap || (int64_t)mt * nt > dg::kWsMaxCounters ||
-                      dg::skinny_workspace_bytes(sh[0], mt, nt, sh[1], s) > ws_bytes))
-          break;
-        const double t = skinny_cost_us(M, N, K, sh[0], sh[1], s, cus);
-        if (best < 0.0 || t < best) {
-          best = t;
-          pl.cfg = sh[0];
-          pl.wn = sh[1];
-          pl.m_tiles = mt;
-          pl.n_tiles = nt;
-          splits = s;
-        }
-      }
-    }
+  if (M > 256) {  // 256 < M <= 2048: the tile shape and split of least estimated time
+    best_skinny(M, N, K, cus, ws_bytes, &pl.cfg, &pl.wn, &splits);
+    pl.m_tiles = (int)ceil_div(M, pl.cfg);
+    pl.n_tiles = (int)ceil_div(N, 4 * pl.wn);
   }
   int depth = dg::skinny_depth(pl.cfg, pl.wn);
   const Force f = forced();
@@ -405,8 +430,9 @@ void plan_skinny(DensePlan& pl, int64_t M, int64_t N, int64_t K, int cus, size_t
   pl.splits = (int)ceil_div(KB, pl.kb_per_split);
 }
 
-// The dense forms.  kFp8 / kAcc / kUe8m0: skinny for M <= 128 (and for
-// M <= 512 where 2 ceil(N / 128) <= CUs and K <= 8192), else 256 x 256 tiles where they fill whole rounds, else
+// The dense forms.  kFp8 / kAcc / kUe8m0: skinny for M <= 128 (for M <= 512
+// where 2 ceil(N / 128) <= CUs and K <= 8192, and for M <= 2048 where its
+// estimated time beats the 256 x 128 plan's), else 256 x 256 tiles where they fill whole rounds, else
 // 256 x 128 tiles with a K-split tail.  kBf16: 256 x 256 tiles where they fill whole rounds, else 256 x 128
 // tiles.  DG_FORCE_CONFIG=kernel=... overrides the wide / 256 x 128 choice
 // for M > 128 (and for the BF16 form at any M >= 1).
@@ -421,8 +447,8 @@ DensePlan plan_dense(DenseKind kind, int64_t M, int64_t N, int64_t K, int cus, s
   // per row tile, all of them split along K below 257 rows) and K is
   // moderate; measured 1.1-3.4x faster there, and slower at K = 16384 or
   // with more columns
-  const bool mid = M > 128 && M <= 512 && f.kernel == kForceNone &&
-                   (f.sk_bm || (2 * ceil_div(N, 128) <= cus && K <= 8192));
+  const bool mid = M > 128 && f.kernel == kForceNone &&
+                   ((f.sk_bm && M <= 2048) || (M <= 512 && 2 * ceil_div(N, 128) <= cus && K <= 8192));
   if (kind != kBf16 && (M <= 128 || mid)) {
     plan_skinny(pl, M, N, K, cus, ws_bytes);
     return pl;
@@ -432,6 +458,18 @@ DensePlan plan_dense(DenseKind kind, int64_t M, int64_t N, int64_t K, int cus, s
     plan_wide(pl, M, N, kbytes, cus);
   else
     plan_persistent(pl, M, N, kbytes, cus, ws_bytes);
+  // 512 < M <= 2048, K <= 8192, on at least 128 CUs (the estimates were
+  // fitted on the whole chip): the skinny kernel where its estimate beats the
+  // 256 x 128 plan's by 15% (few tiles and short K, where that plan's K-split
+  // fix-up dominates: measured up to 3.3x faster; with more tiles or longer K
+  // the tile kernel stays)
+  if (kind != kBf16 && !wide && f.kernel == kForceNone && M > 512 && M <= 2048 && K <= 8192 && cus >= 128) {
+    int bm = 0, wn = 0, s = 0;
+    if (1.15 * best_skinny(M, N, K, cus, ws_bytes, &bm, &wn, &s) < persistent_cost_us(pl, K)) {
+      pl = DensePlan();
+      plan_skinny(pl, M, N, K, cus, ws_bytes);
+    }
+  }
   return pl;
 }
 

@@ -1,6 +1,7 @@
-// Block-scaled FP8 GEMM for gfx950 when M is small (decode, M <= 128, and
-// M <= 512 where the output has few columns): the weights B dominate the
-// traffic and are streamed from HBM once per row tile, through L2.
+// Block-scaled FP8 GEMM for gfx950 when M is small (decode, M <= 128, and up
+// to 2048 rows where the output has few columns or K is short): the weights
+// B dominate the traffic and are streamed from HBM once per row tile,
+// through L2.
 //
 // The computation is the one of Lesson 13 (hpc.payai.win), Fig. 13-1 and its
 // closed-form equation: every 128-wide K block's fp8 partial product is
@@ -10,7 +11,7 @@
 // Organisation:
 //   * a workgroup is 4 wave64s (one per SIMD) and owns a BM-row tile of A
 //     (BM = 64, or 128 when 64 < M <= 128, so the weights are read once;
-//     several row tiles of 64 or 128 rows when 128 < M <= 512)
+//     several row tiles of 64 or 128 rows when 128 < M <= 2048)
 //     times BN = 4 * WN columns of B; each wave owns WN columns.  Should
 //     there be several row tiles, the workgroups of one column tile and K
 //     split get ids 8 apart (the same XCD under round-robin dispatch);

@@ -241,8 +241,25 @@ def test_dense_planner_choice(lib):
             dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 512, 4096, 7168)
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 512, 24576, 1536)   # 384 tiles
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 320, 7168, 16384)   # K > 8192
-        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 513, 2112, 7168)
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, 448, 2112, 7168) > 0
+        # 512 < M <= 2048, K <= 8192: the skinny plan where its estimate beats
+        # the 256 x 128 plan's by 15%
+        assert "kernel=skinny tile=64x64 tiles=256 splits=1" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 1024, 1024, 4096)
+        assert "kernel=skinny tile=128x128 tiles=72 splits=2" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 700, 1536, 5120)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 1536, 4096, 7168)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 1024, 2112, 7168)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 2100, 1024, 4096)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 700, 1536, 9216)   # K > 8192
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 2048, 7168, 2048)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 1024, 1024, 4096)
+        dg.dg_set_num_cus(100)  # the estimates hold for the whole chip only
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 1024, 1024, 4096)
+        dg.dg_set_num_cus(256)
+        # no default plan needs more split-K scratch than the allocation-free entry holds (40 MiB)
+        worst = max(dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, m, n, k)
+                    for m in (1, 64, 100, 128, 129, 200, 256, 300, 384, 512, 520, 700, 1024, 1500, 2048, 2100, 4096)
+                    for n in (16, 144, 1024, 2112, 4096, 7168, 24576, 32768) for k in (512, 1536, 2048, 4096, 7168, 16384))
+        assert 0 < worst <= 40 << 20
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 160, 2112, 7168)
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, 160, 2112, 7168) > 0
         dg.dg_set_num_cus(4)
@@ -272,10 +289,11 @@ def test_forced_config_parsing(lib, monkeypatch):
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
         monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x32")  # malformed
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 64, 7168, 2048) == default
-        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x16x4x8")  # honoured up to 512 rows
+        monkeypatch.setenv("DG_FORCE_CONFIG", "skinny=64x16x4x8")  # honoured up to 2048 rows
         assert "kernel=skinny tile=64x64 tiles=176 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 200, 2816, 1024)
         assert "kernel=skinny tile=64x64 tiles=352 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 2816, 1024)
-        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 513, 2816, 1024)
+        assert "kernel=skinny tile=64x64 tiles=704 splits=4" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 1000, 2816, 1024)
+        assert "kernel=skinny" not in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 2049, 2816, 1024)
         monkeypatch.setenv("DG_FORCE_CONFIG", "kernel=persistent")
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 160, 2112, 7168)

@@ -1,6 +1,7 @@
 """Accumulating FP8 GEMM (dg_fp8_gemm_nt_acc, D = C + A.B^T in fp32) against
-the oracle (oracle.gemm_nt_c): skinny (M <= 128, and M <= 512 with few
-columns), persistent (other M > 128) and wide (256 x 256 tiles) kernels, with C given, absent and aliased to D, with
+the oracle (oracle.gemm_nt_c): skinny (M <= 128, and up to 2048 rows with
+few columns or short K), persistent (other M > 128) and wide (256 x 256
+tiles) kernels, with C given, absent and aliased to D, with
 and without K splits, many tiles per workgroup; integer inputs bit-exact; the
 4096 x 7168 x 16384 shape in place at full size on sampled rows and columns."""
 
@@ -48,7 +49,7 @@ def _check(got, qa, sa, qb, sb, c, what):
 
 SHAPES = [(1, 16, 128), (64, 2112, 1024), (100, 272, 4096), (128, 528, 512), (130, 144, 640), (250, 1008, 3072),
           (257, 400, 384), (400, 2112, 1024), (333, 1536, 7168), (257, 7168, 1024), (200, 144, 9216),
-          (600, 400, 384), (1000, 528, 512), (2048, 256, 1024)]
+          (700, 1536, 1024), (777, 2112, 1024), (2100, 400, 384), (1000, 528, 512), (2048, 256, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

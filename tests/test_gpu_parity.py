@@ -198,7 +198,7 @@ def test_dense_matches_oracle(M, N, K, workspace):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 272, 512), (128, 256, 384), (200, 144, 1024), (1, 16, 256), (512, 400, 640),
-                                   (333, 1536, 2048), (600, 400, 640)])
+                                   (333, 1536, 2048), (2100, 400, 640)])
 def test_dense_integer_inputs_bit_exact(M, N, K):
     # integers in [-10, 9] with unit scales: every partial and every fp32 sum is
     # an exact integer below 2^24, so the bf16 result must equal the oracle's bits
@@ -242,17 +242,20 @@ SKINNY = [(1, 2112, 7168), (17, 144, 1024), (64, 2112, 7168), (100, 272, 4096), 
           (64, 4096, 640), (128, 32768, 512), (33, 24576, 1536), (64, 7168, 2048),
           (100, 7168, 5120)]  # the last: one 128-row tile of 128 columns, K split in 4
 
-# skinny kernel with several row tiles (128 < M <= 512, few columns, K <=
-# 8192): 64x64 tiles up to 256 rows, then 64x64, 64x128 or 128x128 tiles,
+# skinny kernel with several row tiles (128 < M <= 2048, few columns or
+# short K): 64x64 tiles up to 256 rows, then 64x64, 64x128 or 128x128 tiles,
 # with and without a K split, ragged last row tile
 SKINNY_MID = [(129, 144, 640), (160, 2112, 7168), (193, 400, 1024), (256, 7168, 2048), (250, 1008, 3072),
-              (257, 144, 3072), (400, 2112, 1024), (333, 1536, 7168), (257, 7168, 1024), (333, 4096, 5120)]
+              (257, 144, 3072), (400, 2112, 1024), (333, 1536, 7168), (257, 7168, 1024), (333, 4096, 5120),
+              (520, 144, 3072), (700, 1536, 1024), (520, 1008, 7168), (777, 2112, 1024), (700, 1536, 5120),
+              (2048, 1024, 2048)]
 
 
-# persistent kernel (M > 512, or K > 8192): tile counts that leave a partial
+# persistent kernel (M > 2048, or K > 8192): tile counts that leave a partial
 # last round, so tail tiles are split along K into pieces (2 to 4, including a
-# short last piece), again with one workspace reused across calls
-PERSISTENT_TAIL = [(200, 144, 9216), (257, 400, 9216), (600, 272, 1024), (1000, 528, 512), (777, 2112, 640),
+# short last piece), and one whole round, again with one workspace reused
+# across calls
+PERSISTENT_TAIL = [(200, 144, 9216), (257, 400, 9216), (2100, 272, 1024), (2300, 528, 512), (2300, 384, 640),
                    (2048, 4096, 1536)]
 
 
@@ -280,10 +283,10 @@ def test_dense_skinny_matches_oracle_with_reused_workspace(M, N, K):
 
 # zero scales (an all-zero group quantised as amax / 448 gives alpha = 0, a
 # zero weight block gives beta = 0): such blocks contribute exactly nothing,
-# on the skinny (M <= 512 here) and the LDS-ring (M > 512) paths, including a
-# zero scale in the first and in the last K block of a row
+# on the skinny (M <= 512 here) and the LDS-ring (M > 2048 here) paths,
+# including a zero scale in the first and in the last K block of a row
 @pytest.mark.parametrize("M,N,K", [(64, 272, 1024), (300, 272, 1024), (128, 2112, 7168), (512, 384, 640),
-                                   (600, 272, 1024), (700, 384, 640)])
+                                   (2100, 272, 1024), (2300, 384, 640)])
 def test_dense_zero_scales_add_nothing(M, N, K):
     a32, b32 = workloads.dense(M, N, K, seed=M + N)
     qa, sa = oracle.quant_1x128(a32)

@@ -41,9 +41,9 @@ def _case(i):
     c["K"] = 64 * int(rng.integers(1, 21)) if form == "bf16" else 128 * int(rng.integers(1, 11))
     if form in ("dense", "acc", "ue8m0", "bf16"):
         c["M"] = int(rng.integers(1, 129)) if rng.random() < 0.5 else int(rng.integers(129, 700))
-        # the skinny kernel takes up to 512 rows: half the cases between 129
-        # and 512 rows go there, the other half to the tile kernels
-        if form != "bf16" and (c["M"] <= 128 or (c["M"] <= 512 and rng.random() < 0.5)):
+        # the skinny kernel takes up to 2048 rows: half the cases past 128
+        # rows go there, the other half to the tile kernels
+        if form != "bf16" and (c["M"] <= 128 or (c["M"] <= 2048 and rng.random() < 0.5)):
             if rng.random() < 0.8:
                 c["force"] = "skinny=" + str(rng.choice(SKINNY)).format(int(rng.integers(1, 5)))
         else:

@@ -57,7 +57,7 @@ def _ws(op, M, N, K):
 # (cus, M, N, K, kernel the planner is expected to take)
 DENSE = [(0, 64, 272, 512, "skinny"), (0, 100, 2112, 4096, "skinny"), (0, 300, 400, 512, "skinny"),
          (0, 333, 1536, 4096, "skinny"), (0, 320, 7168, 1024, "skinny"), (0, 384, 4096, 2048, "skinny"),
-         (0, 600, 400, 512, "persistent"), (5, 1000, 528, 640, "persistent"), (4, 512, 496, 512, "wide"),
+         (0, 700, 1536, 1024, "skinny"), (0, 2100, 400, 512, "persistent"), (5, 1000, 528, 640, "persistent"), (4, 512, 496, 512, "wide"),
          (2, 300, 608, 384, "wide")]
 
 

@@ -3,7 +3,7 @@
 ragged N, K blocks not a multiple of four, several groups, zero groups,
 amax exactly at and just past the power-of-two boundaries, tiny values), the
 GEMM within the bf16 tolerance over small, ragged and split shapes, on
-256 x 256 tiles and on the skinny (rows <= 512) kernel's every compiled
+256 x 256 tiles and on the skinny (rows <= 2048) kernel's every compiled
 configuration, bit identity with the fp32-scale kernels fed the same powers
 of two, and the
 4096x7168x16384 shape at full size on sampled rows and column blocks."""
@@ -84,7 +84,7 @@ def _ws(M, N, K):
     return torch.zeros(max(n // 4, 1), dtype=torch.float32, device=DEV) if n else None
 
 
-SHAPES = [(1, 16, 128), (64, 2112, 1024), (128, 272, 640), (257, 400, 384), (600, 400, 384), (1000, 528, 512),
+SHAPES = [(1, 16, 128), (64, 2112, 1024), (128, 272, 640), (257, 400, 384), (2100, 400, 384), (1000, 528, 512),
           (2048, 256, 1152),
           (4096, 256, 256)]
 
@@ -156,7 +156,7 @@ def test_gemm_ue8m0_bit_identical_to_fp32_scale_kernel(M, N, K):
     assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
 
 
-# (M, N, K, forced plan): rows <= 128 (and rows <= 512 with few columns) run
+# (M, N, K, forced plan): rows <= 128 (and up to 2048 rows with few columns) run
 # the skinny kernel; the forced plans reach every compiled (tile rows, columns
 # per wave, ring depth) instance with a K split, ragged M and N, and K blocks
 # not a multiple of four, also with several row tiles
@@ -167,7 +167,8 @@ SKINNY = [(1, 16, 128, None), (37, 400, 640, None), (100, 528, 1152, None), (64,
           (128, 272, 896, "skinny=128x16x2x6"), (120, 528, 1152, "skinny=128x32x3x4"),
           (200, 528, 1152, "skinny=64x32x3x4"), (256, 272, 896, "skinny=128x16x2x6"),
           (170, 528, 1152, "skinny=128x32x3x4"), (400, 2112, 1024, None), (257, 7168, 1024, None),
-          (333, 1536, 3072, None), (450, 528, 1152, "skinny=64x16x3x8"), (500, 400, 1024, "skinny=128x16x2x6")]
+          (333, 1536, 3072, None), (450, 528, 1152, "skinny=64x16x3x8"), (500, 400, 1024, "skinny=128x16x2x6"),
+          (520, 1008, 7168, None), (700, 1536, 5120, None), (1500, 272, 896, "skinny=128x32x2x4")]
 
 
 @pytest.mark.parametrize("M,N,K,force", SKINNY)
