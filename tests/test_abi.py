@@ -267,9 +267,10 @@ def test_dense_planner_choice(lib):
         assert dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 500, 496, 100) == ""                      # invalid K
         assert dg.dg_describe_plan(dg.DG_OP_MASKED, 500, 496, 100) == ""                      # invalid K
         dg.dg_set_num_cus(256)
-        # contiguous: 256 x 256 tiles when K >= 4096 and they fill whole rounds
+        # contiguous: 256 x 256 tiles when they fill whole rounds, at any K
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 36000, 4096, 7168, 8)
-        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 25472, 7168, 2048, 8)
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 25472, 7168, 2048, 8)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 1152, 400, 2048, 3)  # 10 tiles on 3 CUs
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_CONTIGUOUS, 1024, 4096, 7168, 8)  # 64 tiles
     finally:
         dg.dg_set_num_cus(0)

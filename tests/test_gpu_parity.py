@@ -501,10 +501,10 @@ def test_contiguous_many_tiles_per_workgroup(few_cus, cus, counts, N, K):
 
 
 # (cus, counts, N, K, kernel): 256 x 256 tiles (two half passes where a tile
-# straddles two experts) when K >= 4096 and they fill whole rounds to >= 85%
+# straddles two experts) when they fill whole rounds to >= 85%, at any K
 CONTIG_WIDE = [(1, [130, 5, 300, 1, 256], 400, 4096, "wide"), (2, [256, 256, 100], 272, 4224, "wide"),
                (4, [300, 256, 256], 528, 4096, "wide"), (3, [130, 5, 300, 1, 256], 400, 4096, "persistent"),
-               (1, [130, 5, 300, 1, 256], 400, 2048, "persistent")]
+               (1, [130, 5, 300, 1, 256], 400, 2048, "wide"), (3, [130, 5, 300, 1, 256], 400, 1024, "persistent")]
 
 
 @pytest.mark.parametrize("cus,counts,N,K,kernel", CONTIG_WIDE)

@@ -112,8 +112,8 @@ def test_k_grouped_varying_power_of_two_scales_bit_exact(cus, G, M, N, ks):
 
 
 # (cus, counts, N, K): contiguous on 128 x 256 tiles, and on 256 x 256 tiles
-# (K >= 4096, tiles straddling two experts) on capped CUs
-CONTIG = [(0, [130, 5, 256], 272, 512), (2, [200, 300, 40], 512, 4096)]
+# (tiles straddling two experts) on capped CUs, at a long and a short K
+CONTIG = [(0, [130, 5, 256], 272, 512), (2, [200, 300, 40], 512, 4096), (2, [200, 300, 40], 512, 1024)]
 
 
 @pytest.mark.parametrize("cus,counts,N,K", CONTIG)
