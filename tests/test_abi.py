@@ -196,6 +196,11 @@ def test_dense_planner_choice(lib):
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 7168, 16384)      # 448 tiles: 0.875
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 4096, 7168)       # 256 tiles: 1.0
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 4096, 2112, 7168)  # 144 tiles: 0.56
+        # one round of 256 x 256 tiles on >= 60% of the CUs: the fp8 forms take it, BF16 does not
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 2560, 4096, 2048)       # 160 tiles: 0.625
+        assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 2560, 4096, 2048)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_BF16_GEMM_NT, 2560, 4096, 2048)
+        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 8192, 2112, 7168)  # 288 tiles: 2 rounds
         # UE8M0 scales: the same 256 x 256 rule (no workspace needed there), else 256 x 128 tiles
         assert "kernel=wide" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 4096, 7168, 16384)
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT_UE8M0, 4096, 7168, 16384) == 0
@@ -239,7 +244,7 @@ def test_dense_planner_choice(lib):
         assert "kernel=skinny tile=128x128 tiles=224 splits=1" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 512, 7168, 2048)
         assert "kernel=skinny tile=128x128 tiles=128 splits=2" in \
             dg.dg_describe_plan(dg.DG_OP_GEMM_NT_UE8M0, 512, 4096, 7168)
-        assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 512, 24576, 1536)   # 384 tiles
+        assert "kernel=skinny" not in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 512, 24576, 1536)   # 384 tiles
         assert "kernel=persistent" in dg.dg_describe_plan(dg.DG_OP_GEMM_NT, 320, 7168, 16384)   # K > 8192
         assert dg.dg_get_workspace_size(dg.DG_OP_GEMM_NT, 448, 2112, 7168) > 0
         # 512 < M <= 2048, K <= 8192: the skinny plan where its estimate beats

@@ -442,9 +442,11 @@ def _planned_kernel(capfd, fn):
 
 
 # (cus, M, N, K, kernel): 256 x 256 tiles are planned when they fill whole
-# rounds of the CUs to >= 85%, else 256 x 128 tiles with a K-split tail
+# rounds of the CUs to >= 85% or make one round on >= 60% of them, else
+# 256 x 128 tiles with a K-split tail
 WIDE_CASES = [(1, 256, 256, 128, "wide"), (4, 512, 512, 640, "wide"), (4, 500, 496, 384, "wide"),
               (3, 300, 608, 1024, "wide"), (7, 1000, 1792, 512, "wide"), (2, 1024, 272, 256, "wide"),
+              (10, 768, 512, 512, "wide"), (10, 1280, 256, 512, "persistent"),
               (7, 2048, 256, 1024, "persistent"), (5, 777, 400, 384, "persistent")]
 
 
