@@ -59,6 +59,8 @@ COPY_CAL_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte cou
 TRAFFIC_RECORDS = {
     "sweep": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_dense_sweep.md"),
     "masked": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_masked_4096x7168.md"),
+    "masked_decode": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_persistent_kernel_masked_decode_4096x7168.md"),
+    "contiguous": os.path.join(ROOT, "profiles", "traffic_fp8_gemm_wide_kernel_contiguous_4096x7168.md"),
 }
 CLOCK_RECORDS = {
     "fp8_gemm_wide_kernel": os.path.join(ROOT, "profiles", "counters_fp8_gemm_wide_kernel_4096x7168x16384.md"),
